@@ -1,0 +1,375 @@
+"""Pins for the fp64 oracle: closed forms, invariants, hand-derived fixtures, brute force.
+
+Each check is chosen so that a plausible slip in the oracle (a dropped term, a wrong sign
+or index, a transposed operand, an off-by-one in the mask) fails at least one of them.
+The plant tests at the end mutate the oracle on the CPU and assert the pins notice.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as A
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, make_prefill, default_scale
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_prefix_mean(causal):
+    B, H, N, d = 2, 3, 37, 8
+    q = np.zeros((B, H, N, d))
+    k, v = rnd(1, B, H, N, d), rnd(2, B, H, N, d)
+    o, lse = oracle.forward(q, k, v, 0.3, causal)
+    for i in range(N):
+        upto = i + 1 if causal else N
+        np.testing.assert_allclose(o[:, :, i], v[:, :, :upto].mean(axis=2), rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[:, :, i], math.log(upto), rtol=1e-14)
+
+
+def test_causal_row0_is_v0():
+    B, H, N, d = 1, 2, 19, 16
+    q, k, v = rnd(3, B, H, N, d), rnd(4, B, H, N, d), rnd(5, B, H, N, d)
+    o, lse = oracle.forward(q, k, v, 0.25, True)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.25 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]), rtol=1e-14)
+
+
+def test_single_key_returns_v():
+    q, k, v = rnd(6, 1, 1, 1, 4), rnd(7, 1, 1, 1, 4), rnd(8, 1, 1, 1, 4)
+    for causal in (False, True):
+        o, _ = oracle.forward(q, k, v, 1.0, causal)
+        np.testing.assert_array_equal(o, v)
+
+
+def test_constant_v_gives_constant_o():
+    q, k = rnd(9, 1, 2, 23, 8), rnd(10, 1, 2, 23, 8)
+    v = np.ones((1, 2, 23, 8))
+    for causal in (False, True):
+        o, _ = oracle.forward(q, k, v, 0.7, causal)
+        np.testing.assert_allclose(o, 1.0, rtol=1e-14)
+
+
+@pytest.mark.parametrize("alpha,beta", [(1.0, 2.0), (4.0, 0.5), (2.0, 8.0)])
+def test_one_hot_queries_and_keys(alpha, beta):
+    """Q_i = alpha e_{a_i}, K_j = beta e_{b_j}: S_ij = scale alpha beta [a_i == b_j]."""
+    N, d, scale = 29, 6, 0.125
+    rng = np.random.default_rng(11)
+    a, b = rng.integers(0, d, N), rng.integers(0, d, N)
+    q = np.zeros((1, 1, N, d)); q[0, 0, np.arange(N), a] = alpha
+    k = np.zeros((1, 1, N, d)); k[0, 0, np.arange(N), b] = beta
+    v = rnd(12, 1, 1, N, 5)
+    o, lse = oracle.forward(q, k, v, scale, False)
+    w = math.exp(scale * alpha * beta)
+    for i in range(N):
+        match = b == a[i]
+        z = match.sum() * w + (N - match.sum())
+        p = np.where(match, w / z, 1.0 / z)
+        np.testing.assert_allclose(o[0, 0, i], p @ v[0, 0], rtol=1e-13)
+        np.testing.assert_allclose(lse[0, 0, i], math.log(z), rtol=1e-14)
+
+
+def _golden_rows(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            parts = line.split()
+            rows.setdefault(parts[0], {})[int(parts[1])] = np.array([float(x) for x in parts[2:]])
+    return rows
+
+
+def test_hand_derived_2x2_fixture():
+    g = _golden_rows("hand_2x2.txt")
+    q = np.array([[[[math.log(2), 0.0], [0.0, 0.0]]]])
+    k = np.eye(2)[None, None]
+    v = np.array([[[[2.0, 0.0], [1.0, 3.0]]]])
+    for causal, tag in ((False, "full"), (True, "causal")):
+        o, lse = oracle.forward(q, k, v, 1.0, causal)
+        for i in range(2):
+            np.testing.assert_allclose(o[0, 0, i], g["O_" + tag][i], rtol=1e-15, atol=1e-16)
+            np.testing.assert_allclose(lse[0, 0, i], g["LSE_" + tag][i][0], rtol=1e-15)
+    dout = np.array([[[[1.0, 0.0], [0.0, 0.0]]]])
+    dq, dk, dv = oracle.backward(q, k, v, dout, 1.0, False)
+    for name, arr in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        for i in range(2):
+            np.testing.assert_allclose(arr[0, 0, i], g[name][i], rtol=1e-14, atol=1e-16)
+
+
+def test_flop_formula_matches_printed_table():
+    with open(os.path.join(GOLDEN, "flops_table.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            n, d, gf = line.split()
+            val = oracle.attention_flops(1, 1, int(n), int(d), causal=False) / 1e9
+            digits = len(gf.split(".")[1])
+            assert round(val, digits) == pytest.approx(float(gf)), (n, d, val, gf)
+    assert oracle.attention_flops(2, 16, 4096, 128, True) == 0.5 * 4 * 32 * 4096**2 * 128
+    assert oracle.attention_flops(1, 1, 8, 4, True, backward=True) == 2.5 * 0.5 * 4 * 64 * 4
+
+
+# ----------------------------------------------------------------------------- invariants
+def test_probability_rows_sum_to_one_and_mask_is_exact_zero():
+    q, k = rnd(13, 40, 16), rnd(14, 40, 16)
+    for causal in (False, True):
+        p = oracle.probabilities(q, k, 0.5, causal)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+        if causal:
+            assert np.all(p[np.triu_indices(40, 1)] == 0.0)
+            assert np.all(p[np.tril_indices(40)] > 0.0)
+
+
+def test_key_shift_leaves_output_and_shifts_lse():
+    B, H, N, d, scale = 1, 2, 31, 8, 0.4
+    q, k, v = rnd(15, B, H, N, d), rnd(16, B, H, N, d), rnd(17, B, H, N, d)
+    u = rnd(18, d)
+    for causal in (False, True):
+        o1, l1 = oracle.forward(q, k, v, scale, causal)
+        o2, l2 = oracle.forward(q, k + u, v, scale, causal)
+        np.testing.assert_allclose(o2, o1, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(l2 - l1, scale * (q @ u), rtol=1e-9, atol=1e-11)
+
+
+def test_output_inside_convex_hull_of_values():
+    q, k, v = rnd(19, 1, 1, 50, 8) * 3, rnd(20, 1, 1, 50, 8) * 3, rnd(21, 1, 1, 50, 8)
+    for causal in (False, True):
+        o, _ = oracle.forward(q, k, v, 1.0, causal)
+        for i in range(50):
+            upto = i + 1 if causal else 50
+            assert np.all(o[0, 0, i] >= v[0, 0, :upto].min(axis=0) - 1e-12)
+            assert np.all(o[0, 0, i] <= v[0, 0, :upto].max(axis=0) + 1e-12)
+
+
+def test_joint_key_value_permutation_invariance():
+    q, k, v = rnd(22, 1, 2, 33, 8), rnd(23, 1, 2, 33, 8), rnd(24, 1, 2, 33, 8)
+    perm = np.random.default_rng(25).permutation(33)
+    o1, l1 = oracle.forward(q, k, v, 0.3, False)
+    o2, l2 = oracle.forward(q, k[:, :, perm], v[:, :, perm], 0.3, False)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=1e-13)
+
+
+def test_gqa_equals_repeated_kv():
+    B, Hq, Hkv, N, d = 2, 6, 2, 17, 8
+    q, k, v = rnd(26, B, Hq, N, d), rnd(27, B, Hkv, N, d), rnd(28, B, Hkv, N, d)
+    g = Hq // Hkv
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    for causal in (False, True):
+        o1, l1 = oracle.forward(q, k, v, 0.35, causal)
+        o2, l2 = oracle.forward(q, kr, vr, 0.35, causal)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+    dout = rnd(29, B, Hq, N, d)
+    dq1, dk1, dv1 = oracle.backward(q, k, v, dout, 0.35, True)
+    dq2, dk2, dv2 = oracle.backward(q, kr, vr, dout, 0.35, True)
+    np.testing.assert_allclose(dq1, dq2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dk1, dk2.reshape(B, Hkv, g, N, d).sum(axis=2), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv1, dv2.reshape(B, Hkv, g, N, d).sum(axis=2), rtol=1e-12, atol=1e-13)
+
+
+def test_forward_rows_matches_full_forward():
+    B, H, N, d = 1, 3, 64, 8
+    q, k, v = rnd(30, B, H, N, d), rnd(31, B, H, N, d), rnd(32, B, H, N, d)
+    rows = np.array([0, 1, 5, 31, 32, 63])
+    for causal in (False, True):
+        of, lf = oracle.forward(q, k, v, 0.3, causal)
+        orow, lrow = oracle.forward_rows(q, k, v, 0.3, causal, rows)
+        np.testing.assert_allclose(orow, of[:, :, rows], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lrow, lf[:, :, rows], rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- brute force
+def _brute_forward(q, k, v, scale, causal):
+    N, d = q.shape
+    L = k.shape[0]
+    o = np.zeros((N, v.shape[1]))
+    lse = np.zeros(N)
+    for i in range(N):
+        s = [scale * math.fsum(q[i, c] * k[j, c] for c in range(d)) for j in range(L)
+             if not (causal and j > i)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = math.fsum(e)
+        lse[i] = m + math.log(z)
+        for c in range(v.shape[1]):
+            o[i, c] = math.fsum(e[j] / z * v[j, c] for j in range(len(s)))
+    return o, lse
+
+
+@pytest.mark.parametrize("N,d", [(1, 1), (2, 3), (5, 4), (8, 2), (7, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(N, d, causal):
+    q, k, v = rnd(33 + N, N, d), rnd(44 + N, N, d), rnd(55 + N, N, d)
+    o, lse = oracle.forward(q[None, None], k[None, None], v[None, None], 0.61, causal)
+    ob, lb = _brute_forward(q, k, v, 0.61, causal)
+    np.testing.assert_allclose(o[0, 0], ob, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], lb, rtol=1e-13, atol=1e-13)
+
+
+def _online_blocked(q, k, v, scale, causal, block, order):
+    """Online softmax of "FlashAttention optimisation" §3.2.1 over key blocks in any order.
+    A debug model of the method (fp64), used only to pin order independence (§3.2.2)."""
+    N, L = q.shape[0], k.shape[0]
+    m = np.full(N, -np.inf)
+    l = np.zeros(N)
+    acc = np.zeros((N, v.shape[1]))
+    for j0 in order:
+        kb, vb = k[j0:j0 + block], v[j0:j0 + block]
+        s = scale * q @ kb.T
+        if causal:
+            s = np.where(np.arange(j0, j0 + kb.shape[0])[None, :] > np.arange(N)[:, None], -np.inf, s)
+        m_new = np.maximum(m, s.max(axis=1))
+        alpha = np.where(np.isfinite(m), np.exp(m - np.where(np.isfinite(m_new), m_new, 0)), 0.0)
+        p = np.exp(s - np.where(np.isfinite(m_new), m_new, 0)[:, None])
+        l = alpha * l + p.sum(axis=1)
+        acc = alpha[:, None] * acc + p @ vb
+        m = m_new
+    return acc / l[:, None], m + np.log(l)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_softmax_any_block_order_equals_oracle(causal):
+    N, d, blk = 48, 8, 8
+    q, k, v = rnd(70, N, d) * 2, rnd(71, N, d) * 2, rnd(72, N, d)
+    o, lse = oracle.forward(q[None, None], k[None, None], v[None, None], 0.5, causal)
+    rng = np.random.default_rng(73)
+    for _ in range(4):
+        order = rng.permutation(np.arange(0, N, blk))
+        ob, lb = _online_blocked(q, k, v, 0.5, causal, blk, order)
+        np.testing.assert_allclose(ob, o[0, 0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lb, lse[0, 0], rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- gradients
+def _loss(q, k, v, dout, scale, causal):
+    o, _ = oracle.forward(q, k, v, scale, causal)
+    return float(np.sum(o * dout))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1)])
+def test_backward_matches_central_differences(causal, hq, hkv):
+    N, d, scale, h = 6, 3, 0.7, 1e-6
+    q, k, v = rnd(80, 1, hq, N, d), rnd(81, 1, hkv, N, d), rnd(82, 1, hkv, N, d)
+    dout = rnd(83, 1, hq, N, d)
+    grads = oracle.backward(q, k, v, dout, scale, causal)
+    for idx, x in enumerate((q, k, v)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            args_p = [q, k, v]; args_p[idx] = xp
+            args_m = [q, k, v]; args_m[idx] = xm
+            num[pos] = (_loss(*args_p, dout, scale, causal) - _loss(*args_m, dout, scale, causal)) / (2 * h)
+        err = np.linalg.norm(num - grads[idx]) / np.linalg.norm(grads[idx])
+        assert err < 1e-6, (idx, err)
+
+
+def test_gradient_sum_identities():
+    B, H, N, d = 1, 2, 21, 8
+    q, k, v, do = (rnd(90 + i, B, H, N, d) for i in range(4))
+    for causal in (False, True):
+        dq, dk, dv = oracle.backward(q, k, v, do, 0.3, causal)
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+        np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), rtol=1e-12, atol=1e-12)
+
+
+def test_equal_value_rows_give_zero_query_and_key_gradients():
+    B, H, N, d = 1, 1, 15, 4
+    q, k, do = rnd(95, B, H, N, d), rnd(96, B, H, N, d), rnd(97, B, H, N, d)
+    v = np.broadcast_to(rnd(98, d), (B, H, N, d)).copy()
+    for causal in (False, True):
+        dq, dk, _ = oracle.backward(q, k, v, do, 0.9, causal)
+        np.testing.assert_allclose(dq, 0.0, atol=1e-13)
+        np.testing.assert_allclose(dk, 0.0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- decode + merge
+def test_decode_equals_single_row_forward_and_gqa():
+    B, Hq, Hkv, L, d = 2, 8, 2, 40, 8
+    q, kc, vc = rnd(100, B, Hq, d), rnd(101, B, Hkv, L, d), rnd(102, B, Hkv, L, d)
+    o, lse = oracle.decode(q, kc, vc, 0.2)
+    of, lf = oracle.forward(q[:, :, None, :], kc, vc, 0.2, False)
+    np.testing.assert_allclose(o, of[:, :, 0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lf[:, :, 0], rtol=1e-13)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 40])
+def test_split_kv_merge_is_independent_of_split_count(splits):
+    B, Hq, Hkv, L, d = 1, 4, 1, 40, 8
+    q, kc, vc = rnd(103, B, Hq, d) * 2, rnd(104, B, Hkv, L, d) * 2, rnd(105, B, Hkv, L, d)
+    o, lse = oracle.decode(q, kc, vc, 0.4)
+    os_, ls = oracle.split_kv_decode(q, kc, vc, 0.4, splits)
+    np.testing.assert_allclose(os_, o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ls, lse, rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- inputs
+def test_bf16_rounding_matches_torch_rne():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(5).standard_normal(100000).astype(np.float32) * 7
+    x[:4] = [1.00390625, 1.01171875, -1.00390625, 3.0e-39]  # ties and a denormal
+    ours = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(bf16_bits_to_f32(ours), torch.from_numpy(ours.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_inputs_are_deterministic_and_upcast_exact():
+    a = make_prefill(1, 2, 2, 16, 8, "bf16", seed=7, qk_mult=2.0, with_dout=True)
+    b = make_prefill(1, 2, 2, 16, 8, "bf16", seed=7, qk_mult=2.0, with_dout=True)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+    np.testing.assert_array_equal(oracle.upcast(a["q"]), bf16_bits_to_f32(a["q"]).astype(np.float64))
+    assert default_scale(128) == float(np.float32(1 / math.sqrt(128)))
+
+
+# ----------------------------------------------------------------------------- planted slips
+@pytest.mark.parametrize("slip", ["no_max_shift_in_lse", "mask_includes_diagonal", "transpose_v"])
+def test_planted_mistakes_are_caught(monkeypatch, slip):
+    """Plant a plausible mistake in the oracle (CPU only) and check that a pin fails."""
+    if slip == "no_max_shift_in_lse":
+        orig = A._softmax_rows
+
+        def bad(s):
+            p, lse = orig(s)
+            return p, lse - np.max(s, axis=1)
+        monkeypatch.setattr(A, "_softmax_rows", bad)
+        with pytest.raises(AssertionError):
+            test_causal_row0_is_v0()
+    elif slip == "mask_includes_diagonal":
+        orig = A._scores
+
+        def bad(q, k, scale, causal, row_ids=None):
+            s = orig(q, k, scale, causal, row_ids)
+            if causal:
+                n = min(s.shape)
+                s = s.copy()
+                s[np.arange(1, n), np.arange(1, n)] = -np.inf
+            return s
+        monkeypatch.setattr(A, "_scores", bad)
+        with pytest.raises(AssertionError):
+            test_zero_query_gives_prefix_mean(True)
+    else:
+        def bad_forward(q, k, v, scale, causal):
+            q, k, v = A.upcast(q), A.upcast(k), A.upcast(v)
+            o = np.empty(q.shape[:3] + (v.shape[3],))
+            lse = np.empty(q.shape[:3])
+            for b in range(q.shape[0]):
+                for h in range(q.shape[1]):
+                    p, lse[b, h] = A._softmax_rows(A._scores(q[b, h], k[b, h], scale, causal))
+                    o[b, h] = p @ v[b, h].T  # square [N, d] tiles only
+            return o, lse
+        monkeypatch.setattr(oracle, "forward", bad_forward)
+        with pytest.raises(AssertionError):
+            test_hand_derived_2x2_fixture()
