@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path on synthetic inputs already resident in HBM:
+  * forward (causal, with LSE) and backward (recompute) on the training workload
+    B=2, H=16, N=4096, d=128, bf16 — the attention shape whose FLOP rate is the metric;
+  * single-token grouped-query decode: batch 64, Hq=32, Hkv=8, d=128, KV cache L=8192, bf16.
+
+Reported value: forward+backward TFLOP/s with the algorithmic count 4 N^2 d per head
+(halved for causal) for the forward and 2.5x that for the backward.  Decode is reported as
+algorithmic HBM GB/s (K + V + Q + O + LSE bytes).  Phase times come from HIP events on the
+stream the kernels run on.  The fp64 CPU oracle is timed beside it on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def flops_fwd(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f * 0.5 if causal else f
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_71_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, digest):
+    """Per-launch HBM bytes measured by rocprofv3 counters for `kernel`, if the stored
+    measurement was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s=15.0):
+    """fp64 oracle forward+backward on whole heads of the training workload, one head at a
+    time until the time budget is spent; scaled to TFLOP/s with the same algorithmic count."""
+    import numpy as np
+    import oracle
+    from synth import default_scale, make_prefill
+    B, H, N, d = 2, 16, 4096, 128
+    scale = default_scale(d)
+    inp = make_prefill(1, 1, 1, N, d, "bf16", seed=1004, with_dout=True)
+    heads, t_total = 0, 0.0
+    while t_total < budget_s and heads < B * H:
+        t0 = time.perf_counter()
+        oracle.forward(inp["q"], inp["k"], inp["v"], scale, True)
+        oracle.backward(inp["q"], inp["k"], inp["v"], inp["dout"], scale, True)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    flops = heads * 3.5 * flops_fwd(1, 1, N, d, True)
+    cores = len(os.sched_getaffinity(0))
+    threads = os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS") or str(cores)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads) if threads.isdigit() else cores,
+            "kind": "oracle",
+            "sample": f"{heads} whole head(s) (N={N}, d={d}, causal) of the B={B},H={H} training workload: "
+                      f"fp64 forward + backward materialising S and P, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from exact_io_aware_71_amd import binding as attn
+    from synth import default_scale, make_decode, make_prefill
+
+    attn.load()
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    B, H, N, d = 2, 16, 4096, 128
+    scale = default_scale(d)
+    log("generating inputs")
+    tr = make_prefill(B, H, H, N, d, "bf16", seed=1004, with_dout=True)
+    q, k, v, do = (to_dev(tr[x]) for x in ("q", "k", "v", "dout"))
+    del tr
+    DB, DHq, DHkv, DL = 64, 32, 8, 8192
+    dec = make_decode(DB, DHq, DHkv, DL, d, seed=1005)
+    dq_, dk_, dv_ = (to_dev(dec[x]) for x in ("q", "k", "v"))
+    del dec
+
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_b = torch.empty(attn.attn_bwd_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device=dev)
+    splits = attn.attn_decode_auto_splits(DB, DHq, DHkv, DL, d)
+    ws_d = torch.empty(attn.attn_decode_workspace_bytes(DB, DHq, DHkv, DL, d, 0), dtype=torch.uint8, device=dev)
+    dec_o = torch.empty_like(dq_)
+    dec_lse = torch.empty((DB, DHq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        attn.attn_fwd(q, k, v, True, scale, o=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        attn.attn_bwd(q, k, v, o, lse, do, True, scale, dq=gq, dk=gk, dv=gv, workspace=ws_b)
+        if ev is not None:
+            ev[2].record(stream)
+        attn.attn_decode(dq_, dk_, dv_, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = [e[0].elapsed_time(e[1]) for e in evs]
+    t_bwd = [e[1].elapsed_time(e[2]) for e in evs]
+    t_dec = [e[2].elapsed_time(e[3]) for e in evs]
+    t_step = [e[0].elapsed_time(e[3]) for e in evs]
+    ms_fwd, ms_bwd, ms_dec = (float(np.mean(x)) for x in (t_fwd, t_bwd, t_dec))
+    ms_step = float(np.mean(t_step))
+
+    f_fwd = flops_fwd(B, H, N, d, True)
+    f_bwd = 2.5 * f_fwd
+    tflops = (f_fwd + f_bwd) / ((ms_fwd + ms_bwd) * 1e-3) / 1e12
+    dec_bytes = 2 * DB * DHkv * DL * d * 2 + 2 * DB * DHq * d * 2 + DB * DHq * 4
+    dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
+
+    log(f"timed {args.steps} steps: {wall:.3f} s")
+    # Quick spot check of the timed outputs against the oracle (a few rows / one batch).
+    import oracle
+    from synth import make_prefill as mp
+    tr = mp(B, H, H, N, d, "bf16", seed=1004)
+    rows = np.array([0, 1, 1000, N - 1])
+    o_ref, _ = oracle.forward_rows(tr["q"][:1, :2], tr["k"][:1, :2], tr["v"][:1, :2], scale, True, rows)
+    spot = float(np.abs(o[:1, :2, rows].float().cpu().numpy() - o_ref).max())
+    del tr
+
+    fwd_digest = source_digest("fwd.hip", "common.h")
+    dec_digest = source_digest("decode.hip", "common.h")
+    roofline = {
+        "kernel": "fwd_bf16_kernel (attn_fwd, causal, B*H=32, N=4096, d=128)",
+        "bound": "mfma", "achieved": f_fwd / (ms_fwd * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+    }
+    roofline["frac"] = roofline["achieved"] / roofline["peak"]
+    roofline["traffic"] = load_traffic("fwd_bf16_kernel", fwd_digest)
+    roofline_decode = {
+        "kernel": "decode_split_kernel + decode_merge_kernel (attn_decode, B=64, Hq=32, Hkv=8, L=8192, d=128)",
+        "bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS,
+        "traffic": load_traffic("decode_split_kernel", dec_digest), "splits": splits,
+    }
+
+    result = {
+        "metric": "attn fwd/bwd TFLOP/s (4N^2d, causal halved) bf16 N=4096 d=128; decode HBM GB/s",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "attention training step B=2 H=16 N=4096 d=128 causal (fwd+bwd) + GQA decode "
+                               "B=64 Hq=32 Hkv=8 L=8192 d=128", "parallelism": "none (one GPU)"},
+        "fwd_TFLOPs": f_fwd / (ms_fwd * 1e-3) / 1e12, "bwd_TFLOPs": f_bwd / (ms_bwd * 1e-3) / 1e12,
+        "decode_GBps": dec_gbs,
+        "ms": {"fwd": ms_fwd, "bwd": ms_bwd, "decode": ms_dec, "fwd_min": min(t_fwd), "bwd_min": min(t_bwd),
+               "decode_min": min(t_dec), "wall_per_step": wall / args.steps * 1e3},
+        "roofline": roofline, "roofline_decode": roofline_decode,
+        "spot_check_max_abs_err": spot,
+        "gpu": torch.cuda.get_device_properties(0).gcnArchName,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+"""ctypes binding of libexact_attn.so: argument marshalling only.
+
+Every step of attention runs in the HIP library; this module only checks tensor metadata,
+passes raw device pointers, sizes and the current HIP stream, and turns non-OK status codes
+into exceptions.  It fails loudly when the library has not been built — there is no
+fallback path.
+
+Function names match the C entry points declared in include/attn.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libexact_attn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_F32, ATTN_BF16 = 0, 1
+
+EXPORTS = (
+    "attn_abi_version", "attn_status_str", "attn_last_error", "attn_fwd",
+    "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_auto_splits",
+    "attn_decode_workspace_bytes", "attn_decode",
+)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+
+
+_STATUS_NAMES = {1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once; raises if it is missing (build it with exact_io_aware_71_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m exact_io_aware_71_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_abi_version.restype = i
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_status_str.argtypes = [i]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_fwd.restype = i
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_decode_auto_splits.restype = i
+    lib.attn_decode_auto_splits.argtypes = [i, i, i, i, i]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_decode.restype = i
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, load().attn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def attn_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, want_lse: bool = True, stream=None):
+    """O (and LSE [B,Hq,N] fp32) for q [B,Hq,N,d], k/v [B,Hkv,N,d] on the GPU."""
+    import torch
+    lib = load()
+    _require(q.is_cuda and q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D CUDA tensors")
+    _require(all(t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    _require(tuple(k.shape) == (B, Hkv, N, d) and tuple(v.shape) == (B, Hkv, N, d), "k/v shape mismatch")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, _dtype_code(q),
+                        int(bool(causal)), float(scale), _stream(stream)))
+    return o, lse
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
+    return int(load().attn_bwd_workspace_bytes(B, Hq, Hkv, N, d))
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """dQ, dK, dV by recomputation from the forward's O and LSE."""
+    import torch
+    lib = load()
+    for t in (q, k, v, o, lse, dout):
+        _require(t.is_cuda and t.is_contiguous(), "all inputs must be contiguous CUDA tensors")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    _require(tuple(lse.shape) == (B, Hq, N) and lse.dtype == torch.float32, "lse must be fp32 [B,Hq,N]")
+    _require(tuple(dout.shape) == tuple(q.shape) and tuple(o.shape) == tuple(q.shape), "o/dout shape mismatch")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                        B, Hq, Hkv, N, d, _dtype_code(q), int(bool(causal)), float(scale), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_decode_auto_splits(B, Hq, Hkv, L, d) -> int:
+    return int(load().attn_decode_auto_splits(B, Hq, Hkv, L, d))
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, L, d, num_splits=0) -> int:
+    return int(load().attn_decode_workspace_bytes(B, Hq, Hkv, L, d, num_splits))
+
+
+def attn_decode(q, k_cache, v_cache, scale: float, num_splits: int = 0, o=None, lse=None, want_lse=True,
+                workspace=None, stream=None):
+    """Single-token decode: q [B,Hq,d] against caches [B,Hkv,L,d]."""
+    import torch
+    lib = load()
+    _require(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4, "q [B,Hq,d], caches [B,Hkv,L,d]")
+    for t in (q, k_cache, v_cache):
+        _require(t.is_cuda and t.is_contiguous(), "inputs must be contiguous CUDA tensors")
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _require(tuple(k_cache.shape) == (B, Hkv, L, d) == tuple(v_cache.shape), "cache shape mismatch")
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, L, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d,
+                           _dtype_code(q), float(scale), int(num_splits), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, lse

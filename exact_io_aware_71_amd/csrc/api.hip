@@ -1,0 +1,197 @@
+// C-ABI entry points of libexact_attn.so (declared in include/attn.h).
+//
+// Every argument is validated on the host before any HIP call, so the validation paths are
+// exercised without a GPU.  The library allocates nothing: scratch space comes from the
+// caller's workspace, which keeps every call capturable in a HIP graph.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+thread_local char g_err[512] = "";
+
+attn_status_t fail(attn_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+attn_status_t ok() {
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+attn_status_t check_scale(float scale) {
+  if (!(isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  return ATTN_OK;
+}
+
+attn_status_t check_heads(int B, int Hq, int Hkv, int N, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d N=%d d=%d)", B, Hq, Hkv, N, d);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  // Element offsets are formed in 64-bit, row indices in 32-bit: keep B*H*N in int range.
+  if ((long long)B * Hq * N > 0x7fffffffLL || (long long)B * Hkv * N > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "B*H*N exceeds 2^31-1");
+  return ATTN_OK;
+}
+
+#define RETURN_IF(expr)                 \
+  do {                                  \
+    attn_status_t _s = (expr);          \
+    if (_s != ATTN_OK) return _s;       \
+  } while (0)
+
+attn_status_t from_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Split choice for decode: enough workgroups to fill 256 CUs several times over, chunks
+// of whole 32-key blocks, at least 256 keys per chunk.
+int auto_splits(int B, int Hkv, int L) {
+  const long long groups = (long long)B * Hkv;
+  const int max_by_len = (L + 255) / 256;
+  long long s = (2048 + groups - 1) / groups;
+  if (s > max_by_len) s = max_by_len;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return (int)s;
+}
+
+// Effective (splits, keys per split) for a requested count.
+void decode_plan(int L, int requested, int* splits, int* kps) {
+  const int blocks = (L + 31) / 32;
+  int s = requested;
+  if (s > blocks) s = blocks;
+  if (s < 1) s = 1;
+  const int per = (blocks + s - 1) / s;  // 32-key blocks per split
+  *kps = per * 32;
+  *splits = (L + *kps - 1) / *kps;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                       int Hkv, int N, int d, attn_dtype_t dtype, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  RETURN_IF(check_heads(B, Hq, Hkv, N, d));
+  RETURN_IF(check_scale(scale));
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (dtype == ATTN_BF16) {
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "bf16 forward supports d in {64, 128} (got %d)", d);
+  } else if (dtype == ATTN_F32) {
+    if (d != 64) return fail(ATTN_ERR_UNSUPPORTED, "fp32 forward supports d == 64 only (got %d)", d);
+  } else {
+    return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  }
+  xattn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, dtype == ATTN_BF16 ? 1 : 0, causal ? 1 : 0, scale,
+                   (hipStream_t)stream};
+  return from_hip(xattn::launch_fwd(a), "attn_fwd launch");
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  (void)Hkv;
+  (void)d;
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  return align_up((size_t)B * Hq * N * sizeof(float), 256);
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                       attn_dtype_t dtype, int causal, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID_ARG, "all tensor pointers of attn_bwd must be non-null");
+  RETURN_IF(check_heads(B, Hq, Hkv, N, d));
+  RETURN_IF(check_scale(scale));
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (dtype != ATTN_BF16) return fail(dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG,
+                                      "backward supports bf16 only");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
+  if (Hq != Hkv) return fail(ATTN_ERR_UNSUPPORTED, "grouped-query backward (Hq=%d, Hkv=%d) is not implemented", Hq, Hkv);
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  xattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal ? 1 : 0, scale,
+                   (float*)workspace, (hipStream_t)stream};
+  return from_hip(xattn::launch_bwd(a), "attn_bwd launch");
+}
+
+int attn_decode_auto_splits(int B, int Hq, int Hkv, int L, int d) {
+  (void)Hq;
+  (void)d;
+  if (B <= 0 || Hkv <= 0 || L <= 0) return 0;
+  return auto_splits(B, Hkv, L);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || d <= 0 || num_splits < 0) return 0;
+  int splits, kps;
+  decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
+  const size_t rows = (size_t)splits * B * Hq;
+  return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+}
+
+attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B,
+                          int Hq, int Hkv, int L, int d, attn_dtype_t dtype, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-null");
+  RETURN_IF(check_heads(B, Hq, Hkv, L, d));
+  RETURN_IF(check_scale(scale));
+  if (num_splits < 0) return fail(ATTN_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", num_splits);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (dtype != ATTN_BF16) return fail(dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG,
+                                      "decode supports bf16 only");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
+  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, L, d, num_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "attn_decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
+  if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int splits, kps;
+  decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
+  const size_t rows = (size_t)splits * B * Hq;
+  float* part_o = (float*)workspace;
+  float* part_lse = (float*)((char*)workspace + align_up(rows * d * sizeof(float), 256));
+  xattn::DecodeArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, L, d, scale, splits, kps, part_o, part_lse,
+                      (hipStream_t)stream};
+  return from_hip(xattn::launch_decode(a), "attn_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Shared device helpers for the gfx950 (CDNA4) attention kernels.
+//
+// Register layouts used throughout (wave64, verified on gfx950):
+//   v_mfma_f32_32x32x16_bf16  A[32 x 16]: lane l holds row l%32, k-group l/32 (8 values)
+//                             B[16 x 32]: lane l holds col l%32, k-group l/32 (8 values)
+//                             C[32 x 32]: lane l, register r holds
+//                                         row 8*(r/4) + 4*(l/32) + r%4, col l%32
+//   v_mfma_f32_16x16x32_bf16  A: row l%16, k-group l/16; B: col l%16, k-group l/16;
+//                             C: lane l, register r holds row 4*(l/16) + r, col l%16
+//   v_mfma_f32_32x32x2_f32    A: row l%32, k = l/32; B: col l%32, k = l/32; C as above
+// The hardware pairs A's k-slot (group, element) with B's same slot, so any consistent
+// assignment of contraction indices to slots gives the exact product.
+//
+// ds_read_b64_tr_b16 (transposing LDS read): within each 16-lane group, lane j supplies an
+// address of 4 contiguous 16-bit values; output lane i receives, as element e, value (i%4)
+// of source lane 4*e + i/4.  With source lanes reading rows r0 + j/4 at columns
+// c0 + 4*(j%4), output lane i gets the column c0 + i over rows r0..r0+3: a row-major LDS
+// tile read as a column, which is what an MFMA operand needs when its contraction index
+// is the tile's row index.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the hardware exp unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Broadcast lane `src` of each 16-lane row to the whole row (DPP row_newbcast).
+template <int src>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + src, 0xf, 0xf, false));
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = {lo, hi};
+  const bf16x2 v = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const void* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, lds_addr));
+}
+__device__ __forceinline__ bf16x8 join_tr(const s16x4& a, const s16x4& b) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace xattn

@@ -1,0 +1,241 @@
+// Single-token grouped-query decode for gfx950: split-KV partials, then an LSE merge.
+//
+// Pages cited by title:
+//   [OPT]  "FlashAttention optimisation: breaking the attention memory bottleneck"
+//   [FUND] "Attention fundamentals: the standard attention flow, complexity analysis,
+//          memory bottleneck and inference challenges"
+//
+// Decode reads the whole KV cache once per token and does O(L d) work ([OPT] §4.2.2,
+// [FUND] §2.3.1), so the kernel is bound by HBM bandwidth, not by arithmetic.  Design:
+//   * One workgroup per (batch, KV head, key chunk).  All g = Hq/Hkv query heads that share
+//     the KV head ([OPT] §5.3) are processed together, so every K/V byte is read from HBM
+//     exactly once and used g times.
+//   * Scores: v_mfma_f32_16x16x32_bf16 with the K rows as the A operand straight from
+//     global memory (16-byte loads) and the g query vectors as the B operand (columns
+//     g..15 zero).  In the C layout lane (16*j + h) holds head h's scores for keys 4j..4j+3
+//     of the 16-key block.
+//   * P V on the vector ALU: lane (16*j + c) owns features [c*D/16, (c+1)*D/16) of keys
+//     4j + r; the probability p[h][key] sits in lane 16*j + h of the same 16-lane row and
+//     is broadcast with a DPP row_newbcast move.  V rows are read with coalesced 16-byte
+//     loads (D = 128) and no LDS staging.
+//   * Online softmax per 32-key chunk ([OPT] §3.2.1); the four row groups of a wave and the
+//     four waves of a workgroup share one running max per head, so only the final
+//     cross-wave combine needs LDS.
+//   * Each chunk writes (O_s normalised, lse_s); the merge kernel combines the chunks with
+//     weights 2^(lse_s - max) — exact by the order independence of [OPT] §3.2.2.
+#include <utility>
+
+#include "common.h"
+#include "launch.h"
+
+namespace xattn {
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+constexpr int kDecWaves = 4;
+
+template <int D, int GP>
+__global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq, int Hkv, int L,
+    int splits, int keys_per_split, float scale_log2) {
+  constexpr int EPL = D / 16;  // features per lane in the P V product
+  constexpr int DC = D / 32;   // 32-wide feature chunks of the score MFMA
+  __shared__ float s_m[kDecWaves][GP];
+  __shared__ float s_l[kDecWaves][GP];
+  __shared__ float s_acc[kDecWaves][GP][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int g = Hq / Hkv;
+  const int split = blockIdx.x % splits;
+  const int bk = blockIdx.x / splits;  // b * Hkv + kv head
+  const int b = bk / Hkv, kvh = bk - b * Hkv;
+  const int kbeg = split * keys_per_split;
+  const int kend = min(L, kbeg + keys_per_split);
+  const uint16_t* kp = kc + (size_t)bk * L * D;
+  const uint16_t* vp = vc + (size_t)bk * L * D;
+
+  bf16x8 qB[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (col < g) u = ld_global16(q + (size_t)(b * Hq + kvh * g + col) * D + 32 * c + 8 * grp);
+    qB[c] = as_bf16x8(u);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[GP][EPL];
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+
+  const int nchunks = (kend - kbeg + 31) / 32;
+  for (int ci = wave; ci < nchunks; ci += kDecWaves) {
+    const int k0 = kbeg + ci * 32;
+    f32x4 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = k0 + blk * 16 + col;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        u32x4 u = {0u, 0u, 0u, 0u};
+        if (key < kend) u = ld_global16(kp + (size_t)key * D + 32 * c + 8 * grp);
+        sc[blk] = mfma16(as_bf16x8(u), qB[c], sc[blk]);
+      }
+    }
+    // Lane (16*grp + col): head col, keys k0 + 16*blk + 4*grp + r.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (k0 + blk * 16 + 4 * grp + r >= kend) sc[blk][r] = -INFINITY;
+        mx = fmaxf(mx, sc[blk][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(sc[blk][r], scale_log2, -m_use));
+        sc[blk][r] = p;
+        rs += p;
+      }
+    l_run = fmaf(l_run, alpha, rs);
+    static_for<GP>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float a_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= a_h;
+    });
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + blk * 16 + 4 * grp + r;
+        float vf[EPL];
+        if constexpr (EPL == 8) {
+          u32x4 u = {0u, 0u, 0u, 0u};
+          if (key < kend) u = ld_global16(vp + (size_t)key * D + EPL * col);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { vf[2 * e] = bf16_lo(u[e]); vf[2 * e + 1] = bf16_hi(u[e]); }
+        } else {
+          u32x2 u = {0u, 0u};
+          if (key < kend) u = *reinterpret_cast<const u32x2*>(vp + (size_t)key * D + EPL * col);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) { vf[2 * e] = bf16_lo(u[e]); vf[2 * e + 1] = bf16_hi(u[e]); }
+        }
+        const float pr = sc[blk][r];
+        static_for<GP>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          const float p_h = row_bcast<h>(pr);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p_h, vf[e], acc[h][e]);
+        });
+      }
+  }
+
+  // Combine the four row groups of the wave (they share m_run), then the four waves.
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = acc[h][e] + __shfl_xor(acc[h][e], 16);
+      acc[h][e] = x + __shfl_xor(x, 32);
+    }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][h][EPL * col + e] = acc[h][e];
+  }
+  if (lane < GP) {
+    s_m[wave][lane] = m_run;
+    s_l[wave][lane] = l_tot;
+  }
+  __syncthreads();
+  for (int i = tid; i < g * D; i += kDecWaves * 64) {
+    const int h = i / D, d = i - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      if (s_m[w][h] != -INFINITY) {
+        const float wt = fast_exp2(s_m[w][h] - M);
+        num = fmaf(wt, s_acc[w][h][d], num);
+        den = fmaf(wt, s_l[w][h], den);
+      }
+    }
+    const size_t row = (size_t)(split * B + b) * Hq + kvh * g + h;
+    part_o[row * D + d] = num / den;
+    if (d == 0) part_lse[row] = M + fast_log2(den);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int BHq, int splits) {
+  const int row = blockIdx.x, d = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_lse[(size_t)s * BHq + row]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float w = fast_exp2(part_lse[(size_t)s * BHq + row] - M);
+    num = fmaf(w, part_o[((size_t)s * BHq + row) * D + d], num);
+    den += w;
+  }
+  const float val = num / den;
+  const uint32_t packed = pack_bf16x2(val, 0.f);
+  o[(size_t)row * D + d] = (uint16_t)(packed & 0xffffu);
+  if (lse != nullptr && d == 0) lse[row] = (M + fast_log2(den)) * kLn2;
+}
+
+template <int D, int GP>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+  const float sl2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((decode_split_kernel<D, GP>), dim3(a.B * a.Hkv * a.splits), dim3(kDecWaves * 64), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.part_o,
+                     a.part_lse, a.B, a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, a.stream, a.part_o, a.part_lse,
+                     (uint16_t*)a.o, a.lse, a.B * a.Hq, a.splits);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs& a) {
+  const int g = a.Hq / a.Hkv;
+  if (g <= 1) return launch_decode_t<D, 1>(a);
+  if (g <= 2) return launch_decode_t<D, 2>(a);
+  if (g <= 4) return launch_decode_t<D, 4>(a);
+  if (g <= 8) return launch_decode_t<D, 8>(a);
+  return launch_decode_t<D, 16>(a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  return a.d == 128 ? launch_decode_d<128>(a) : launch_decode_d<64>(a);
+}
+
+}  // namespace xattn

@@ -1,0 +1,392 @@
+// Forward attention kernels for gfx950.
+//
+// Pages cited by title:
+//   [FUND] "Attention fundamentals: the standard attention flow, complexity analysis,
+//          memory bottleneck and inference challenges"
+//   [OPT]  "FlashAttention optimisation: breaking the attention memory bottleneck"
+//   [NOTE] "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+//
+// One workgroup owns BM query rows of one (batch, head) and streams the key/value rows of
+// that head through LDS in tiles of BN keys ([OPT] §3.1, [NOTE] Method item 1).  Per tile
+// each wave computes its score block, updates the running row max m and running sum l and
+// rescales its output accumulator by 2^(m_old - m_new) ([OPT] §3.2.1, [NOTE] Method item
+// 2), then adds P V.  Normalisation by l happens once at the end ([OPT] §7.1).  Only O and
+// the per-row log-sum-exp reach HBM ([OPT] §3.1).
+//
+// MI355X mapping:
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is the
+//     A operand read from LDS, Q^T the B operand held in registers for the whole kernel.
+//     In the C layout each lane then owns one query column and 16 keys, so the row max and
+//     row sum are 16 in-lane operations plus one v_permlane32_swap, and the probabilities
+//     are already in the B-operand layout of the P V product (O^T = V^T P^T): no LDS round
+//     trip for P.
+//   * V^T, the A operand of that product, is read from the row-major V tile with the
+//     transposing ds_read_b64_tr_b16, so the tile is stored exactly as it arrives.
+//   * K/V tiles are double buffered: the global loads for tile t+1 are issued before the
+//     MFMA work on tile t and written to the other LDS stage afterwards (one barrier per
+//     tile), hiding HBM/L2 latency behind compute ([OPT] §5.2).
+//   * Causal: tiles past the diagonal are never loaded, waves whose rows all precede a tile
+//     skip its MFMA work, and only diagonal tiles evaluate the mask.  Heavy (late) query
+//     tiles are dispatched first; all query tiles of one head land on one XCD when the
+//     head count is a multiple of 8, so the head's K/V stay in that XCD's L2.
+//   * The exponentials use the base-2 hardware exp with scale*log2(e) folded into one FMA.
+#include "common.h"
+#include "launch.h"
+
+namespace xattn {
+
+constexpr int kFwdBN = 64;  // keys per tile
+
+template <int D>
+struct FwdLds {
+  static constexpr int KP = D * 2 + 16;  // padded row pitch (bytes) of the K tile
+  static constexpr int VP = D * 2 + 16;  // padded row pitch (bytes) of the V tile
+  static constexpr int KBYTES = kFwdBN * KP;
+  static constexpr int VBYTES = kFwdBN * VP;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int TOTAL = 2 * STAGE;
+};
+
+// Work-item -> (head, query tile): heavy-first for causal, head index fastest.
+__device__ __forceinline__ void fwd_tile_of(int id, int BH, int n_qtiles, bool causal, int& bh, int& qt) {
+  bh = id % BH;
+  int t = id / BH;
+  qt = causal ? (n_qtiles - 1 - t) : t;
+}
+
+template <int D, int NQ, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
+    int n_qtiles, int BH) {
+  constexpr int BM = NW * NQ * 32;
+  constexpr int BN = kFwdBN;
+  constexpr int KB = BN / 32;             // 32-key blocks per tile
+  constexpr int DC = D / 16;              // k-chunks of the QK^T product
+  constexpr int DB = D / 32;              // 32-row blocks of O^T
+  constexpr int CHUNKS = BN * D / 8;      // 16-byte chunks per K (or V) tile
+  constexpr int CPT = CHUNKS / (NW * 64); // chunks per thread per tensor
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split evenly over the workgroup");
+  using Lds = FwdLds<D>;
+  __shared__ __attribute__((aligned(16))) char smem[Lds::TOTAL];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int h32 = lane >> 5;
+
+  int bh, qt;
+  fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hk = hq / (Hq / Hkv);
+  const uint16_t* qp = q + (size_t)bh * N * D;
+  const uint16_t* kp = k + (size_t)(b * Hkv + hk) * N * D;
+  const uint16_t* vp = v + (size_t)(b * Hkv + hk) * N * D;
+
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * NQ * 32;
+
+  // Q^T operand: lane holds query qw0 + qb*32 + l32, features 16c + 8*h32 .. +7.
+  bf16x8 qreg[NQ][DC];
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) {
+    const int qi = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (qi < N) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
+      qreg[qb][c] = as_bf16x8(u);
+    }
+  }
+
+  f32x16 acc[DB][NQ];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.f;
+  float m_run[NQ], l_run[NQ];
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntiles = (kv_end + BN - 1) / BN;
+
+  u32x4 pk[CPT], pv[CPT];
+  auto load_tile = [&](int t) {
+    const int t0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NW * 64;
+      const int row = c / (D / 8);
+      const int col = c % (D / 8);
+      const int key = t0 + row;
+      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+      if (key < N) {
+        zk = ld_global16(kp + (size_t)key * D + col * 8);
+        zv = ld_global16(vp + (size_t)key * D + col * 8);
+      }
+      pk[i] = zk;
+      pv[i] = zv;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* ks = smem + stage * Lds::STAGE;
+    char* vs = ks + Lds::KBYTES;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NW * 64;
+      const int row = c / (D / 8);
+      const int col = c % (D / 8);
+      *reinterpret_cast<u32x4*>(ks + row * Lds::KP + col * 16) = pk[i];
+      *reinterpret_cast<u32x4*>(vs + row * Lds::VP + col * 16) = pv[i];
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const int t0 = t * BN;
+    const char* ks = smem + (t & 1) * Lds::STAGE;
+    const char* vs = ks + Lds::KBYTES;
+    // A wave whose queries all precede this tile has nothing to add (causal skip).
+    const bool active = !CAUSAL || (t0 <= qw0 + NQ * 32 - 1);
+    if (active) {
+      f32x16 s[KB][NQ];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * Lds::KP + (16 * c + 8 * h32) * 2);
+#pragma unroll
+          for (int qb = 0; qb < NQ; ++qb) s[kb][qb] = mfma32(a, qreg[qb][c], s[kb][qb]);
+        }
+      }
+      // Mask keys past the end and, on diagonal tiles, keys after the query.
+      const bool need_mask = (t0 + BN > N) || (CAUSAL && t0 + BN - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < NQ; ++qb) {
+            const int qi = qw0 + qb * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+              if (kj >= N || (CAUSAL && kj > qi)) s[kb][qb][r] = -INFINITY;
+            }
+          }
+      }
+      // Online softmax ([OPT] §3.2.1) in the base-2 domain: t = s * scale * log2(e).
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+        mx = max_xor32(mx);
+        const float m_new = fmaxf(m_run[qb], mx * scale_log2);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[qb] - m_use);
+        m_run[qb] = m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(s[kb][qb][r], scale_log2, -m_use));
+            s[kb][qb][r] = p;
+            rs += p;
+          }
+        l_run[qb] = fmaf(l_run[qb], alpha, rs);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][qb][r] *= alpha;
+      }
+      // O^T += V^T P^T over the tile's keys, 16 keys per MFMA.
+      const int G = lane >> 4;
+      const int j16 = lane & 15;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          bf16x8 pb[NQ];
+#pragma unroll
+          for (int qb = 0; qb < NQ; ++qb) {
+            u32x4 u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(s[kb][qb][8 * sh + 2 * e], s[kb][qb][8 * sh + 2 * e + 1]);
+            pb[qb] = as_bf16x8(u);
+          }
+          const int row = kb * 32 + 16 * sh + 4 * (G >> 1) + (j16 >> 2);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (G & 1) + 4 * (j16 & 3);
+            const char* a0 = vs + row * Lds::VP + col * 2;
+            const bf16x8 a = join_tr(ds_read_tr16(a0), ds_read_tr16(a0 + 8 * Lds::VP));
+#pragma unroll
+            for (int qb = 0; qb < NQ; ++qb) acc[db][qb] = mfma32(a, pb[qb], acc[db][qb]);
+          }
+        }
+      }
+    }
+    if (t + 1 < ntiles) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
+  uint16_t* op = o + (size_t)bh * N * D;
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) {
+    const float lt = sum_xor32(l_run[qb]);
+    const float inv = 1.f / lt;
+    const int qi = qw0 + qb * 32 + l32;
+    if (qi < N) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = db * 32 + 8 * jj + 4 * h32;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[db][qb][4 * jj + 0] * inv, acc[db][qb][4 * jj + 1] * inv);
+          w[1] = pack_bf16x2(acc[db][qb][4 * jj + 2] * inv, acc[db][qb][4 * jj + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
+        }
+      if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run[qb] + fast_log2(lt)) * kLn2;
+    }
+  }
+}
+
+// fp32 inputs (d = 64): the same tiled online softmax with v_mfma_f32_32x32x2_f32, one
+// wave per 32 queries and 32-key tiles, single-buffered.  Keeps full fp32 precision.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
+    int n_qtiles, int BH) {
+  constexpr int D = 64, BM = 128, BN = 32, P = D + 1;  // P: padded pitch in floats
+  __shared__ float ks[BN * P];
+  __shared__ float vs[BN * P];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  int bh, qt;
+  fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / Hq, hq = bh - b * Hq, hk = hq / (Hq / Hkv);
+  const float* qp = q + (size_t)bh * N * D;
+  const float* kp = k + (size_t)(b * Hkv + hk) * N * D;
+  const float* vp = v + (size_t)(b * Hkv + hk) * N * D;
+  const int q0 = qt * BM, qw0 = q0 + wave * 32, qi = qw0 + l32;
+
+  float qr[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) qr[c] = (qi < N) ? qp[(size_t)qi * D + 2 * c + h32] : 0.f;
+  f32x16 acc[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { acc[0][r] = 0.f; acc[1][r] = 0.f; }
+  float m_run = -INFINITY, l_run = 0.f;
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = t * BN;
+    for (int i = tid; i < BN * D; i += 256) {
+      const int row = i / D, col = i % D, key = t0 + row;
+      ks[row * P + col] = key < N ? kp[(size_t)key * D + col] : 0.f;
+      vs[row * P + col] = key < N ? vp[(size_t)key * D + col] : 0.f;
+    }
+    __syncthreads();
+    if (!CAUSAL || t0 <= qw0 + 31) {
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 2; ++c) s = mfma32_f32(ks[l32 * P + 2 * c + h32], qr[c], s);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kj = t0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        if (kj >= N || (CAUSAL && kj > qi)) s[r] = -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[r] = fast_exp2(fmaf(s[r], scale_log2, -m_use)); rs += s[r]; }
+      l_run = fmaf(l_run, alpha, rs);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { acc[0][r] *= alpha; acc[1][r] *= alpha; }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * h32 + (r & 3);
+        acc[0] = mfma32_f32(vs[key * P + l32], s[r], acc[0]);
+        acc[1] = mfma32_f32(vs[key * P + 32 + l32], s[r], acc[1]);
+      }
+    }
+    __syncthreads();
+  }
+  const float lt = sum_xor32(l_run);
+  if (qi < N) {
+    float* op = o + (size_t)bh * N * D + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) op[db * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)] = acc[db][r] / lt;
+    if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run + fast_log2(lt)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------------------- host launchers
+template <int D, int NQ, int NW>
+static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
+  constexpr int BM = NW * NQ * 32;
+  const int n_qtiles = (a.N + BM - 1) / BM;
+  const int BH = a.B * a.Hq;
+  const dim3 grid(n_qtiles * BH), block(NW * 64);
+  const float sl2 = a.scale * kLog2e;
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, true>), grid, block, 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       a.lse, a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, false>), grid, block, 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       a.lse, a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.dtype == 0) {  // fp32, d = 64
+    const int n_qtiles = (a.N + 127) / 128;
+    const int BH = a.B * a.Hq;
+    const float sl2 = a.scale * kLog2e;
+    if (a.causal)
+      hipLaunchKernelGGL(fwd_f32_kernel<true>, dim3(n_qtiles * BH), dim3(256), 0, a.stream,
+                         (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                         a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
+    else
+      hipLaunchKernelGGL(fwd_f32_kernel<false>, dim3(n_qtiles * BH), dim3(256), 0, a.stream,
+                         (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                         a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
+    return hipGetLastError();
+  }
+  if (a.d == 128) return launch_fwd_bf16_t<128, 1, 4>(a);
+  return launch_fwd_bf16_t<64, 1, 4>(a);
+}
+
+}  // namespace xattn

@@ -1,0 +1,41 @@
+// Internal launcher interface between the C-ABI layer (api.hip) and the kernel files.
+// Arguments reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace xattn {
+
+struct FwdArgs {
+  const void* q; const void* k; const void* v; void* o; float* lse;
+  int B, Hq, Hkv, N, d, dtype, causal;
+  float scale;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q; const void* k; const void* v; const void* o; const float* lse; const void* dout;
+  void* dq; void* dk; void* dv;
+  int B, Hq, Hkv, N, d, causal;
+  float scale;
+  float* delta;  // [B,Hq,N] fp32 scratch inside the caller's workspace
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  const void* q; const void* k; const void* v; void* o; float* lse;
+  int B, Hq, Hkv, L, d;
+  float scale;
+  int splits;           // effective number of key chunks (>= 1, every chunk non-empty)
+  int keys_per_split;   // multiple of 32
+  float* part_o;        // [splits, B, Hq, d] fp32
+  float* part_lse;      // [splits, B, Hq] fp32 (base-2 log-sum-exp of the scaled scores)
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace xattn

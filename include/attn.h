@@ -1,0 +1,130 @@
+/*
+ * exact_attn — exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libexact_attn.so.  Plain pointers and sizes only.
+ *
+ * Pages cited by title:
+ *   [FUND] "Attention fundamentals: the standard attention flow, complexity analysis,
+ *          memory bottleneck and inference challenges" (FlashAttention inference tutorial,
+ *          chapter 2)
+ *   [OPT]  "FlashAttention optimisation: breaking the attention memory bottleneck"
+ *   [NOTE] "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+ *          (paper note)
+ *
+ * What is computed ([FUND] §2.1): per (batch b, query head h) with KV head
+ * kv = h / (Hq / Hkv) ([OPT] §5.3, consecutive query heads share a KV head):
+ *     S = scale * Q K^T,   S_ij = -inf for j > i when causal (the diagonal is kept),
+ *     P = row-softmax(S),  O = P V,   LSE_i = ln(sum_j exp(S_ij))  (natural log).
+ * The kernels never write S or P to memory: Q, K and V are processed in tiles with the
+ * running max / running sum of [OPT] §3.1-§3.2 and [NOTE] Method items 1-2; the backward
+ * recomputes S and P from Q, K, V and the saved LSE ([NOTE] Method item 3).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library allocates
+ *     nothing and keeps no device state, so every call may be captured in a HIP graph.
+ *   - Layouts are dense, row-major: Q/O/dQ/dO [B, Hq, N, d]; K/V/dK/dV [B, Hkv, N, d];
+ *     LSE and D are fp32 [B, Hq, N]; decode Q/O are [B, Hq, d] (one token each), the KV
+ *     cache [B, Hkv, L, d].  Element type is given by `dtype` for Q/K/V/O/dO/dQ/dK/dV.
+ *   - Pointers must be 16-byte aligned.  `scale` must be finite and > 0.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only
+ *     enqueue work and return; kernel faults surface at the caller's synchronisation.
+ *   - Arguments are validated before any HIP call.  On a non-OK return nothing has been
+ *     enqueued and attn_last_error() (thread-local) describes the problem.
+ *   - Calls are thread-safe.  Calls that write the same buffers must be ordered by the
+ *     caller (same stream or events).
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, Hq % Hkv != 0, bad scale */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement (see each call) */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the matching *_workspace_bytes() */
+  ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* ABI revision of this header; bumped on any incompatible change. */
+int attn_abi_version(void);
+
+/* Static description of a status code. */
+const char* attn_status_str(attn_status_t status);
+
+/* Thread-local detail of the last non-OK return on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * Forward attention ([FUND] §2.1; tiled online softmax of [OPT] §3.1-§3.2, deferred
+ * normalisation of [OPT] §7.1).
+ *   q [B,Hq,N,d], k/v [B,Hkv,N,d]  inputs (read only)
+ *   o [B,Hq,N,d]                   output, same dtype as q
+ *   lse [B,Hq,N] fp32              optional output (NULL to skip); needed by attn_bwd
+ *   causal != 0                    mask j > i (square attention, query i vs key j)
+ * Supported: dtype BF16 with d in {64, 128}; dtype F32 with d == 64.  Other d or dtype
+ * combinations return ATTN_ERR_UNSUPPORTED.  No workspace.  Bitwise deterministic.
+ */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int N, int d, attn_dtype_t dtype, int causal,
+                       float scale, void* stream);
+
+/* Bytes of device workspace attn_bwd needs (fp32 row statistics D = rowsum(dO * O)). */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * Backward attention by recomputation ([NOTE] Method item 3): S and P are rebuilt per tile
+ * from q, k, v and the forward's lse; nothing of size N x N is stored.
+ *   q, k, v, o, lse                 exactly what attn_fwd consumed and produced
+ *   dout [B,Hq,N,d]                 upstream gradient dL/dO
+ *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d] outputs (overwritten, same dtype as q)
+ *   workspace                        >= attn_bwd_workspace_bytes(...) device bytes, 256-byte
+ *                                    aligned; contents on entry are ignored
+ * Supported: BF16, d in {64, 128}, Hq == Hkv (grouped-query backward returns
+ * ATTN_ERR_UNSUPPORTED).  Deterministic (no atomics).
+ */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int B, int Hq, int Hkv, int N, int d, attn_dtype_t dtype, int causal,
+                       float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Split count attn_decode uses for num_splits == 0 (the automatic choice), so callers can
+ * size the workspace and reproduce the split.
+ */
+int attn_decode_auto_splits(int B, int Hq, int Hkv, int L, int d);
+
+/* Bytes of workspace attn_decode needs for the given split count (0 = automatic). */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int num_splits);
+
+/*
+ * Single-token decode against a KV cache ([OPT] §4.2.2 and §5.3; [FUND] §2.3.1), no mask.
+ * The key axis is split into `num_splits` contiguous chunks processed in parallel; each
+ * chunk yields a partial (O_s, lse_s) and a second pass merges them by log-sum-exp, which
+ * is exact by the order independence of the online softmax ([OPT] §3.2.2).
+ *   q [B,Hq,d]                 one query token per sequence and head
+ *   k_cache/v_cache [B,Hkv,L,d] caches (read only)
+ *   o [B,Hq,d]                 output, same dtype as q
+ *   lse [B,Hq] fp32            optional output (NULL to skip)
+ *   num_splits                 0 = attn_decode_auto_splits(), else 1..L (clamped to
+ *                              ceil(L/32) chunks of whole 32-key blocks)
+ *   workspace                  >= attn_decode_workspace_bytes(...) bytes, 256-byte aligned
+ * Supported: BF16, d in {64, 128}, 1 <= Hq/Hkv <= 16.  Bitwise deterministic for a fixed
+ * split count.
+ */
+attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          float* lse, int B, int Hq, int Hkv, int L, int d, attn_dtype_t dtype,
+                          float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

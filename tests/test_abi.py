@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/attn.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_71_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# Fake, 256-byte-aligned addresses: validation rejects every call below before any
+# HIP call could touch them.
+P = 0x10000
+lib = None
+
+
+def setup_module(module):
+    global lib
+    lib = binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "attn_fwd" in names and "attn_bwd" in names and "attn_decode" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert lib.attn_abi_version() == 1
+    assert lib.attn_status_str(0) == b"ok"
+    assert lib.attn_status_str(3) == b"workspace too small"
+
+
+def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=64, d=128, dt=1, causal=1, scale=0.1):
+    return lib.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, dt, causal, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(N=-3), 1), (dict(Hq=3, Hkv=2), 1),
+    (dict(scale=0.0), 1), (dict(scale=float("nan")), 1), (dict(scale=-1.0), 1), (dict(k=P + 8), 1),
+    (dict(d=96), 2), (dict(d=256), 2), (dict(dt=0, d=128), 2), (dict(dt=7), 1),
+    (dict(B=1 << 16, Hq=1 << 10, Hkv=1 << 10, N=1 << 10), 2),
+])
+def test_fwd_validation(kwargs, status):
+    assert fwd(**kwargs) == status
+    assert lib.attn_last_error() != b""
+
+
+def bwd(ws=P, ws_bytes=1 << 30, Hq=2, Hkv=2, d=128, dt=1, scale=0.1, dq=P):
+    return lib.attn_bwd(P, P, P, P, P, P, dq, P, P, 1, Hq, Hkv, 64, d, dt, 1, ctypes.c_float(scale),
+                        ws, ws_bytes, None)
+
+
+def test_bwd_validation():
+    need = lib.attn_bwd_workspace_bytes(1, 2, 2, 64, 128)
+    assert need == 512
+    assert bwd(dq=None) == 1
+    assert bwd(Hq=4, Hkv=2) == 2           # grouped-query backward not implemented
+    assert bwd(dt=0) == 2
+    assert bwd(d=80) == 2
+    assert bwd(ws=None) == 3
+    assert bwd(ws_bytes=need - 1) == 3
+    assert bwd(ws=P + 16) == 1               # workspace must be 256-byte aligned
+
+
+def test_decode_plan_and_validation():
+    s = lib.attn_decode_auto_splits(64, 32, 8, 8192, 128)
+    assert 1 <= s <= 64
+    need = lib.attn_decode_workspace_bytes(64, 32, 8, 8192, 128, 0)
+    assert need >= s * 64 * 32 * (128 + 1) * 4
+    # Requests beyond the number of 32-key blocks are clamped.
+    assert lib.attn_decode_workspace_bytes(1, 4, 1, 40, 64, 1000) == \
+        lib.attn_decode_workspace_bytes(1, 4, 1, 40, 64, 2)
+
+    def dec(Hq=32, Hkv=8, d=128, dt=1, splits=0, ws=P, ws_bytes=need, scale=0.1):
+        return lib.attn_decode(P, P, P, P, P, 64, Hq, Hkv, 8192, d, dt, ctypes.c_float(scale), splits, ws,
+                               ws_bytes, None)
+    assert dec(Hq=34, Hkv=2) == 2   # 17 heads per group
+    assert dec(d=32) == 2
+    assert dec(dt=0) == 2
+    assert dec(splits=-1) == 1
+    assert dec(ws=None) == 3
+    assert dec(ws_bytes=need - 4) == 3
+    assert dec(scale=float("inf")) == 1
+
+
+def test_binding_raises_typed_error():
+    with pytest.raises(binding.AttnError) as ei:
+        binding._check(fwd(d=96))
+    assert ei.value.status == 2

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP kernels against the fp64 oracle on the same seeded inputs.
+
+Sizes: every workload shape at full size on the GPU, compared element by element where the
+oracle finishes in seconds, else on sampled rows (exact per row: an output row depends only
+on its query and all keys/values) or sampled heads; plus ragged, grouped-query and
+degenerate shapes, closed forms and determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, default_scale, make_decode, make_prefill
+from tests._util import assert_fwd_ok, fwd_errors, rel_l2, to_dev, to_host64, BWD_REL_L2
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(lib, inp, causal, scale):
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = lib.attn_fwd(q, k, v, causal, scale)
+    import torch
+    torch.cuda.synchronize()
+    return to_host64(o), lse.cpu().numpy().astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- forward
+def test_fwd_tiny_fp32(gpu_lib):
+    w = WORKLOADS["tiny"]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "f32", seed=w.seed)
+    scale = default_scale(w.d)
+    o, lse = run_fwd(gpu_lib, inp, w.causal, scale)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], scale, w.causal)
+    err = fwd_errors(o, o_ref, lse, lse_ref)
+    assert_fwd_ok(err, "tiny")
+    assert err["max"] <= 5e-5 and err["lse"] <= 5e-5, err  # fp32 path keeps fp32 precision
+
+
+@pytest.mark.parametrize("seed_off", [0, 1, 2])
+def test_fwd_batched_prefill(gpu_lib, seed_off):
+    w = WORKLOADS["prefill"]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed + seed_off)
+    scale = default_scale(w.d)
+    o, lse = run_fwd(gpu_lib, inp, w.causal, scale)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], scale, w.causal)
+    assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), "prefill")
+
+
+def sample_rows(N, seed, extra=120):
+    fixed = {0, 1, 63, 64, 127, 128, N // 2, N - 1}
+    rng = np.random.default_rng(seed)
+    return np.array(sorted(fixed | set(rng.integers(0, N, extra).tolist())))
+
+
+@pytest.mark.parametrize("name", ["long4k", "long8k", "long16k"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fwd_long_prefill_sampled_rows(gpu_lib, name, causal):
+    w = WORKLOADS[name]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed, qk_mult=w.qk_mult)
+    scale = default_scale(w.d)
+    o, lse = run_fwd(gpu_lib, inp, causal, scale)
+    rows = sample_rows(w.N, w.seed + int(causal))
+    o_ref, lse_ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], scale, causal, rows)
+    assert_fwd_ok(fwd_errors(o[:, :, rows], o_ref, lse[:, :, rows], lse_ref), name)
+
+
+def test_fwd_long4k_full_heads(gpu_lib):
+    w = WORKLOADS["long4k"]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed, qk_mult=w.qk_mult)
+    scale = default_scale(w.d)
+    for causal in (True, False):
+        o, lse = run_fwd(gpu_lib, inp, causal, scale)
+        for h in (0, 31):
+            sl = {kk: inp[kk][:, h:h + 1] for kk in ("q", "k", "v")}
+            o_ref, lse_ref = oracle.forward(sl["q"], sl["k"], sl["v"], scale, causal)
+            assert_fwd_ok(fwd_errors(o[:, h:h + 1], o_ref, lse[:, h:h + 1], lse_ref), f"h{h} causal={causal}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 17, 100, 257, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_ragged(gpu_lib, N, d, causal):
+    inp = make_prefill(2, 3, 3, N, d, "bf16", seed=N * 7 + d)
+    scale = default_scale(d)
+    o, lse = run_fwd(gpu_lib, inp, causal, scale)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], scale, causal)
+    assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), f"N={N} d={d}")
+
+
+@pytest.mark.parametrize("N", [5, 200])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_ragged_fp32(gpu_lib, N, causal):
+    inp = make_prefill(1, 2, 2, N, 64, "f32", seed=N)
+    o, lse = run_fwd(gpu_lib, inp, causal, 0.125)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], 0.125, causal)
+    err = fwd_errors(o, o_ref, lse, lse_ref)
+    assert err["max"] <= 5e-5 and err["lse"] <= 5e-5, err
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_grouped_query(gpu_lib, d, causal):
+    inp = make_prefill(2, 8, 2, 333, d, "bf16", seed=5 + d)
+    scale = default_scale(d)
+    o, lse = run_fwd(gpu_lib, inp, causal, scale)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], scale, causal)
+    assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), "gqa")
+
+
+def test_fwd_closed_forms(gpu_lib):
+    """Q = 0: O_i is the (prefix) mean of V and LSE_i = ln(#keys); causal row 0 is V[0]."""
+    import torch
+    B, H, N, d = 1, 2, 200, 128
+    inp = make_prefill(B, H, H, N, d, "bf16", seed=99)
+    q0 = np.zeros_like(inp["q"])
+    for causal in (False, True):
+        o, lse = run_fwd(gpu_lib, {"q": q0, "k": inp["k"], "v": inp["v"]}, causal, 0.1)
+        v = oracle.upcast(inp["v"])
+        cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+        ref = (np.cumsum(v, axis=2) / cnt[:, None]) if causal else np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+        assert_fwd_ok(fwd_errors(o, ref, lse, np.broadcast_to(np.log(cnt), lse.shape)), f"q0 causal={causal}")
+    o, _ = run_fwd(gpu_lib, inp, True, 0.1)
+    np.testing.assert_array_equal(o[:, :, 0], oracle.upcast(inp["v"])[:, :, 0])
+
+
+def test_fwd_bitwise_deterministic(gpu_lib):
+    import torch
+    inp = make_prefill(1, 4, 4, 1000, 128, "bf16", seed=3)
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o1, l1 = gpu_lib.attn_fwd(q, k, v, True, 0.09)
+    o2, l2 = gpu_lib.attn_fwd(q, k, v, True, 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------- decode
+@pytest.fixture(scope="module")
+def decode_inputs():
+    w = WORKLOADS["decode"]
+    return w, make_decode(w.B, w.Hq, w.Hkv, w.L, w.d, seed=w.seed)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+def test_decode_full_size_sampled_batches(gpu_lib, decode_inputs, splits):
+    import torch
+    w, inp = decode_inputs
+    scale = default_scale(w.d)
+    q, kc, vc = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = gpu_lib.attn_decode(q, kc, vc, scale, num_splits=splits)
+    torch.cuda.synchronize()
+    o, lse = to_host64(o), lse.cpu().numpy().astype(np.float64)
+    bs = [0, 17, 63]
+    o_ref, lse_ref = oracle.decode(inp["q"][bs], inp["k"][bs], inp["v"][bs], scale)
+    assert_fwd_ok(fwd_errors(o[bs], o_ref, lse[bs], lse_ref), f"decode splits={splits}")
+    del q, kc, vc
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("L", [1, 33, 1000])
+@pytest.mark.parametrize("g", [1, 3, 4, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_small(gpu_lib, L, g, d):
+    import torch
+    inp = make_decode(3, 2 * g, 2, L, d, seed=L + g + d)
+    scale = default_scale(d)
+    for splits in (0, 2, 7):
+        o, lse = gpu_lib.attn_decode(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), scale, num_splits=splits)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.decode(inp["q"], inp["k"], inp["v"], scale)
+        assert_fwd_ok(fwd_errors(to_host64(o), o_ref, lse.cpu().numpy(), lse_ref), f"L={L} g={g} s={splits}")
+
+
+def test_decode_matches_forward_single_row(gpu_lib):
+    """Decode equals the forward of one query row against the same keys."""
+    import torch
+    inp = make_decode(2, 4, 4, 300, 128, seed=8)
+    o, lse = gpu_lib.attn_decode(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), 0.088)
+    of, lf = oracle.forward(inp["q"][:, :, None, :], inp["k"], inp["v"], 0.088, False)
+    torch.cuda.synchronize()
+    assert_fwd_ok(fwd_errors(to_host64(o), of[:, :, 0], lse.cpu().numpy(), lf[:, :, 0]))
+
+
+# ----------------------------------------------------------------------------- backward
+def run_fwd_bwd(lib, inp, causal, scale):
+    import torch
+    q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "dout"))
+    o, lse = lib.attn_fwd(q, k, v, causal, scale)
+    dq, dk, dv = lib.attn_bwd(q, k, v, o, lse, do, causal, scale)
+    torch.cuda.synchronize()
+    return [to_host64(t) for t in (dq, dk, dv)]
+
+
+def check_bwd(grads, inp, scale, causal, heads=None, tag=""):
+    sl = (lambda a: a) if heads is None else (lambda a: a[:, heads])
+    ref = oracle.backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["dout"]), scale, causal)
+    for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+        if not np.any(r):
+            # A single key makes the softmax constant: dQ = dK = 0 exactly, so the relative
+            # error is undefined; require the GPU result to vanish up to rounding instead.
+            assert np.abs(sl(g)).max() <= 1e-3, (tag, name, np.abs(sl(g)).max())
+            continue
+        err = rel_l2(sl(g), r)
+        assert err <= BWD_REL_L2, (tag, name, err)
+
+
+@pytest.mark.parametrize("seed_off", [0, 1])
+def test_bwd_training_step_sampled_heads(gpu_lib, seed_off):
+    w = WORKLOADS["train"]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed + seed_off, with_dout=True)
+    scale = default_scale(w.d)
+    grads = run_fwd_bwd(gpu_lib, inp, True, scale)
+    # Per-head gradients depend only on that head's Q, K, V, dO: check two heads per batch.
+    for b in range(w.B):
+        for h in ([0, 15] if seed_off == 0 else [7]):
+            sub = {x: inp[x][b:b + 1, h:h + 1] for x in inp}
+            check_bwd([g[b:b + 1, h:h + 1] for g in grads], sub, scale, True, tag=f"b{b}h{h}")
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 200, 333])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ragged(gpu_lib, N, d, causal):
+    inp = make_prefill(2, 2, 2, N, d, "bf16", seed=N + d + 11, with_dout=True)
+    scale = default_scale(d)
+    grads = run_fwd_bwd(gpu_lib, inp, causal, scale)
+    check_bwd(grads, inp, scale, causal, tag=f"N={N} d={d}")
+
+
+def test_bwd_from_oracle_forward(gpu_lib):
+    """Feed the oracle's O (as bf16) and LSE into attn_bwd: isolates the backward kernels."""
+    import torch
+    from synth import f32_to_bf16_bits
+    inp = make_prefill(1, 2, 2, 500, 128, "bf16", seed=77, with_dout=True)
+    scale = default_scale(128)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], scale, True)
+    q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "dout"))
+    o = to_dev(f32_to_bf16_bits(o_ref.astype(np.float32)))
+    lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    dq, dk, dv = gpu_lib.attn_bwd(q, k, v, o, lse, do, True, scale)
+    torch.cuda.synchronize()
+    check_bwd([to_host64(t) for t in (dq, dk, dv)], inp, scale, True, tag="oracle-fwd")
