@@ -51,17 +51,6 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   if (row < rows && c == 0) delta[row] = s;
 }
 
-// Transposed MFMA operand from a row-major bf16 LDS tile: lane gets the column
-// col0 + (lane%32) over the 8 rows row0 + {8t + 4*(lane/32) + i : t in 0..1, i in 0..3},
-// which are the contraction slots that pair with the C-layout registers 8*sh .. 8*sh+7.
-__device__ __forceinline__ bf16x8 ld_tr_operand(const char* tile, int pitch, int row0, int col0, int lane) {
-  const int G = lane >> 4, j = lane & 15;
-  const int row = row0 + 4 * (G >> 1) + (j >> 2);
-  const int col = col0 + 16 * (G & 1) + 4 * (j & 3);
-  const char* p = tile + row * pitch + col * 2;
-  return join_tr(ds_read_tr16(p), ds_read_tr16(p + 8 * pitch));
-}
-
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int sh) {
   u32x4 u;
 #pragma unroll
@@ -75,8 +64,7 @@ constexpr int kBwdBK = 64;   // keys per streamed tile (dQ kernel)
 
 template <int D>
 struct BwdTile {
-  static constexpr int P = D * 2 + 16;      // padded pitch (bytes)
-  static constexpr int BYTES = 64 * P;       // one 64-row tile
+  static constexpr int BYTES = 64 * D * 2;   // one swizzled 64-row tile
 };
 
 template <int D, bool CAUSAL>
@@ -157,8 +145,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NW * 64;
       const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(base + row * T::P + col * 16) = pq[i];
-      *reinterpret_cast<u32x4*>(base + T::BYTES + row * T::P + col * 16) = pdo[i];
+      *reinterpret_cast<u32x4*>(base + swz<D>(row, col)) = pq[i];
+      *reinterpret_cast<u32x4*>(base + T::BYTES + swz<D>(row, col)) = pdo[i];
     }
     if (tid < BQ) {
       reinterpret_cast<float*>(base + 2 * T::BYTES)[tid] = plse;
@@ -189,7 +177,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const int off = (qb * 32 + l32) * T::P + (16 * c + 8 * h32) * 2;
+        const int off = swz<D>(qb * 32 + l32, 2 * c + h32);
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + off);
         const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dos + off);
         s = mfma32(aq, kreg[c], s);
@@ -219,8 +207,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         const bf16x8 dsa = pack8(dp, sh);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 bdo = ld_tr_operand(dos, T::P, qb * 32 + 16 * sh, db * 32, lane);
-          const bf16x8 bq = ld_tr_operand(qs, T::P, qb * 32 + 16 * sh, db * 32, lane);
+          const bf16x8 bdo = ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane);
+          const bf16x8 bq = ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane);
           dv_acc[db] = mfma32(pa, bdo, dv_acc[db]);
           dk_acc[db] = mfma32(dsa, bq, dk_acc[db]);
         }
@@ -312,8 +300,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NW * 64;
       const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(base + row * T::P + col * 16) = pk[i];
-      *reinterpret_cast<u32x4*>(base + T::BYTES + row * T::P + col * 16) = pv[i];
+      *reinterpret_cast<u32x4*>(base + swz<D>(row, col)) = pk[i];
+      *reinterpret_cast<u32x4*>(base + T::BYTES + swz<D>(row, col)) = pv[i];
     }
   };
 
@@ -333,7 +321,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-          const int off = (kb * 32 + l32) * T::P + (16 * c + 8 * h32) * 2;
+          const int off = swz<D>(kb * 32 + l32, 2 * c + h32);
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(ks + off);
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + off);
           s = mfma32(ak, qreg[c], s);
@@ -356,7 +344,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
           const bf16x8 dsa = pack8(dp, sh);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x8 bk = ld_tr_operand(ks, T::P, kb * 32 + 16 * sh, db * 32, lane);
+            const bf16x8 bk = ld_tr_operand<D>(ks, kb * 32 + 16 * sh, db * 32, lane);
             dq_acc[db] = mfma32(dsa, bk, dq_acc[db]);
           }
         }

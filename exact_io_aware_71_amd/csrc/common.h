@@ -93,6 +93,35 @@ __device__ __forceinline__ bf16x8 join_tr(const s16x4& a, const s16x4& b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// LDS tiles of 64 rows x D bf16 columns are stored unpadded with the 16-byte chunks of each
+// row XOR-permuted by a function of the row index, chosen so that
+//   (i)  a 16-byte read of one chunk from 16 consecutive rows (an MFMA operand whose rows
+//        are the tile rows), and
+//   (ii) a ds_read_b64_tr_b16 over a 4-row x 4-chunk block starting at a row multiple of 4
+// each touch 16 distinct 4-bank groups of the 64-bank LDS, i.e. run without bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  static_assert(D == 64 || D == 128, "tile width");
+  if constexpr (D == 128) return row * 256 + 16 * (chunk ^ (4 * (row & 3) + ((row >> 2) & 3)));
+  else return row * 128 + 16 * (chunk ^ (4 * ((row >> 1) & 1) + ((row >> 2) & 3)));
+}
+// Byte offset of element (row, col) in the swizzled tile (col multiple of 4 for 8-byte reads).
+template <int D>
+__device__ __forceinline__ int swz_elem(int row, int col) {
+  return swz<D>(row, col >> 3) + (col & 7) * 2;
+}
+
+// Transposed MFMA operand from a swizzled 64 x D LDS tile: lane gets column col0 + lane%32
+// over rows row0 + {8t + 4*(lane/32) + i : t in 0..1, i in 0..3}, the contraction slots that
+// pair with C-layout registers 8*sh .. 8*sh+7 of a 32x32 MFMA output (row0 = 16*sh + ...).
+template <int D>
+__device__ __forceinline__ bf16x8 ld_tr_operand(const char* tile, int row0, int col0, int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const int row = row0 + 4 * (G >> 1) + (j >> 2);
+  const int col = col0 + 16 * (G & 1) + 4 * (j & 3);
+  return join_tr(ds_read_tr16(tile + swz_elem<D>(row, col)), ds_read_tr16(tile + swz_elem<D>(row + 8, col)));
+}
+
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -23,6 +23,7 @@
 //     cross-wave combine needs LDS.
 //   * Each chunk writes (O_s normalised, lse_s); the merge kernel combines the chunks with
 //     weights 2^(lse_s - max) — exact by the order independence of [OPT] §3.2.2.
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -40,6 +41,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kDecWaves = 4;
+constexpr float kDecLazy = 8.f;
 
 template <int D, int GP>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
@@ -81,17 +83,36 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
   const int nchunks = (kend - kbeg + 31) / 32;
   for (int ci = wave; ci < nchunks; ci += kDecWaves) {
     const int k0 = kbeg + ci * 32;
-    f32x4 sc[2];
+    // Issue this chunk's K and V loads together (V is consumed after the softmax), so each
+    // wave keeps 2 x 8 KB in flight.
+    u32x4 kraw[2][DC];
+    using VRaw = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
+    VRaw vraw[2][4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int key = k0 + blk * 16 + col;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         u32x4 u = {0u, 0u, 0u, 0u};
         if (key < kend) u = ld_global16(kp + (size_t)key * D + 32 * c + 8 * grp);
-        sc[blk] = mfma16(as_bf16x8(u), qB[c], sc[blk]);
+        kraw[blk][c] = u;
       }
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + blk * 16 + 4 * grp + r;
+        VRaw u = {};
+        if (key < kend) u = *reinterpret_cast<const VRaw*>(vp + (size_t)key * D + EPL * col);
+        vraw[blk][r] = u;
+      }
+    f32x4 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) sc[blk] = mfma16(as_bf16x8(kraw[blk][c]), qB[c], sc[blk]);
     }
     // Lane (16*grp + col): head col, keys k0 + 16*blk + 4*grp + r.
     float mx = -INFINITY;
@@ -104,43 +125,38 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    mx *= scale_log2;
+    // Lazy reference max (as in the forward kernel): move m_run and rescale only when some
+    // head's chunk max exceeds it by more than 2^kDecLazy; the result is unchanged.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kDecLazy) != 0) {
+      const float m_new = fmaxf(m_run, mx);  // finite: the chunk holds >= 1 valid key
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      static_for<GP>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const float a_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= a_h;
+      });
+    }
     float rs = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(sc[blk][r], scale_log2, -m_use));
+        const float p = fast_exp2(fmaf(sc[blk][r], scale_log2, -m_run));
         sc[blk][r] = p;
         rs += p;
       }
-    l_run = fmaf(l_run, alpha, rs);
-    static_for<GP>([&](auto hc) {
-      constexpr int h = decltype(hc)::value;
-      const float a_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= a_h;
-    });
+    l_run += rs;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = k0 + blk * 16 + 4 * grp + r;
         float vf[EPL];
-        if constexpr (EPL == 8) {
-          u32x4 u = {0u, 0u, 0u, 0u};
-          if (key < kend) u = ld_global16(vp + (size_t)key * D + EPL * col);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { vf[2 * e] = bf16_lo(u[e]); vf[2 * e + 1] = bf16_hi(u[e]); }
-        } else {
-          u32x2 u = {0u, 0u};
-          if (key < kend) u = *reinterpret_cast<const u32x2*>(vp + (size_t)key * D + EPL * col);
-#pragma unroll
-          for (int e = 0; e < 2; ++e) { vf[2 * e] = bf16_lo(u[e]); vf[2 * e + 1] = bf16_hi(u[e]); }
-        }
+        for (int e = 0; e < EPL / 2; ++e) { vf[2 * e] = bf16_lo(vraw[blk][r][e]); vf[2 * e + 1] = bf16_hi(vraw[blk][r][e]); }
         const float pr = sc[blk][r];
         static_for<GP>([&](auto hc) {
           constexpr int h = decltype(hc)::value;

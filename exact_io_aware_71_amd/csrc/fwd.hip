@@ -33,16 +33,36 @@
 #include "common.h"
 #include "launch.h"
 
+// Tile shape per head size: query blocks of 32 per wave (NQ), waves per workgroup (NW) and
+// the waves-per-SIMD occupancy target (WPE) the register budget is sized for.
+#ifndef XATTN_FWD128_NQ
+#define XATTN_FWD128_NQ 1
+#endif
+#ifndef XATTN_FWD128_NW
+#define XATTN_FWD128_NW 8
+#endif
+#ifndef XATTN_FWD128_WPE
+#define XATTN_FWD128_WPE 2
+#endif
+#ifndef XATTN_FWD64_NQ
+#define XATTN_FWD64_NQ 1
+#endif
+#ifndef XATTN_FWD64_NW
+#define XATTN_FWD64_NW 4
+#endif
+#ifndef XATTN_FWD64_WPE
+#define XATTN_FWD64_WPE 2
+#endif
+
 namespace xattn {
 
 constexpr int kFwdBN = 64;  // keys per tile
+constexpr float kLazy = 8.f; // log2 of the largest un-normalised probability allowed
 
 template <int D>
 struct FwdLds {
-  static constexpr int KP = D * 2 + 16;  // padded row pitch (bytes) of the K tile
-  static constexpr int VP = D * 2 + 16;  // padded row pitch (bytes) of the V tile
-  static constexpr int KBYTES = kFwdBN * KP;
-  static constexpr int VBYTES = kFwdBN * VP;
+  static constexpr int KBYTES = kFwdBN * D * 2;  // swizzled K tile
+  static constexpr int VBYTES = kFwdBN * D * 2;  // swizzled V tile
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int TOTAL = 2 * STAGE;
 };
@@ -54,8 +74,8 @@ __device__ __forceinline__ void fwd_tile_of(int id, int BH, int n_qtiles, bool c
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
-template <int D, int NQ, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
+template <int D, int NQ, int NW, int WPE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
     int n_qtiles, int BH) {
@@ -141,8 +161,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
       const int c = tid + i * NW * 64;
       const int row = c / (D / 8);
       const int col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + row * Lds::KP + col * 16) = pk[i];
-      *reinterpret_cast<u32x4*>(vs + row * Lds::VP + col * 16) = pv[i];
+      *reinterpret_cast<u32x4*>(ks + swz<D>(row, col)) = pk[i];
+      *reinterpret_cast<u32x4*>(vs + swz<D>(row, col)) = pv[i];
     }
   };
 
@@ -169,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
       for (int c = 0; c < DC; ++c) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * Lds::KP + (16 * c + 8 * h32) * 2);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + swz<D>(kb * 32 + l32, 2 * c + h32));
 #pragma unroll
           for (int qb = 0; qb < NQ; ++qb) s[kb][qb] = mfma32(a, qreg[qb][c], s[kb][qb]);
         }
@@ -189,7 +209,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
             }
           }
       }
-      // Online softmax ([OPT] §3.2.1) in the base-2 domain: t = s * scale * log2(e).
+      // Online softmax ([OPT] §3.2.1) in the base-2 domain, t = s * scale * log2(e).
+      // The reference max m_run moves only when a row's tile max exceeds it by more than
+      // kLazy (i.e. p could exceed 2^kLazy); otherwise p = 2^(t - m_run) <= 2^kLazy is
+      // accumulated against the stale reference.  Final O = acc / l and LSE = m + log2 l
+      // are identical in exact arithmetic, and the O rescale is skipped on most tiles.
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb) {
         float mx = -INFINITY;
@@ -197,29 +221,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = max_xor32(mx);
-        const float m_new = fmaxf(m_run[qb], mx * scale_log2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qb] - m_use);
-        m_run[qb] = m_new;
+        mx = max_xor32(mx) * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kLazy) != 0) {  // wave-uniform branch
+          const float m_new = fmaxf(m_run[qb], mx);
+          const float alpha = fast_exp2(m_run[qb] - m_new);  // m_new finite: key 0 is never masked
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][qb][r] *= alpha;
+        }
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(s[kb][qb][r], scale_log2, -m_use));
+            const float p = fast_exp2(fmaf(s[kb][qb][r], scale_log2, -m_run[qb]));
             s[kb][qb][r] = p;
             rs += p;
           }
-        l_run[qb] = fmaf(l_run[qb], alpha, rs);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][qb][r] *= alpha;
+        l_run[qb] += rs;
       }
       // O^T += V^T P^T over the tile's keys, 16 keys per MFMA.
-      const int G = lane >> 4;
-      const int j16 = lane & 15;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -232,12 +256,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
             for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(s[kb][qb][8 * sh + 2 * e], s[kb][qb][8 * sh + 2 * e + 1]);
             pb[qb] = as_bf16x8(u);
           }
-          const int row = kb * 32 + 16 * sh + 4 * (G >> 1) + (j16 >> 2);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int col = db * 32 + 16 * (G & 1) + 4 * (j16 & 3);
-            const char* a0 = vs + row * Lds::VP + col * 2;
-            const bf16x8 a = join_tr(ds_read_tr16(a0), ds_read_tr16(a0 + 8 * Lds::VP));
+            const bf16x8 a = ld_tr_operand<D>(vs, kb * 32 + 16 * sh, db * 32, lane);
 #pragma unroll
             for (int qb = 0; qb < NQ; ++qb) acc[db][qb] = mfma32(a, pb[qb], acc[db][qb]);
           }
@@ -352,7 +373,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 }
 
 // ------------------------------------------------------------------------- host launchers
-template <int D, int NQ, int NW>
+template <int D, int NQ, int NW, int WPE>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   constexpr int BM = NW * NQ * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
@@ -360,11 +381,11 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   const dim3 grid(n_qtiles * BH), block(NW * 64);
   const float sl2 = a.scale * kLog2e;
   if (a.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, true>), grid, block, 0, a.stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, WPE, true>), grid, block, 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                        a.lse, a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, false>), grid, block, 0, a.stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, WPE, false>), grid, block, 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                        a.lse, a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
   return hipGetLastError();
@@ -385,8 +406,8 @@ hipError_t launch_fwd(const FwdArgs& a) {
                          a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
     return hipGetLastError();
   }
-  if (a.d == 128) return launch_fwd_bf16_t<128, 1, 4>(a);
-  return launch_fwd_bf16_t<64, 1, 4>(a);
+  if (a.d == 128) return launch_fwd_bf16_t<128, XATTN_FWD128_NQ, XATTN_FWD128_NW, XATTN_FWD128_WPE>(a);
+  return launch_fwd_bf16_t<64, XATTN_FWD64_NQ, XATTN_FWD64_NW, XATTN_FWD64_WPE>(a);
 }
 
 }  // namespace xattn
