@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def log(msg):
@@ -48,21 +48,41 @@ def source_digest(*names):
 
 
 def load_traffic(kernel, digest):
-    """Per-launch HBM bytes measured by rocprofv3 counters for `kernel`, if the stored
-    measurement was taken on the current kernel source; else None."""
+    """Per-launch HBM bytes that rocprofv3 counters measured for `kernel`, if they were taken
+    on the current kernel source; else None.  The summary file holds one line per kernel:
+    `traffic <kernel> digest=<hex> bytes_per_launch=<int> ...`."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(kernel)
-    except (OSError, ValueError):
+            lines = f.read().splitlines()
+    except OSError:
         return None
-    if not rec or rec.get("source_digest") != digest:
-        return None
-    return rec.get("bytes_per_launch")
+    for line in lines:
+        parts = line.split()
+        if len(parts) < 3 or parts[0] != "traffic" or parts[1] != kernel:
+            continue
+        kv = dict(p.split("=", 1) for p in parts[2:] if "=" in p)
+        if kv.get("digest") == digest and "bytes_per_launch" in kv:
+            return int(kv["bytes_per_launch"])
+    return None
+
+
+def blas_threads():
+    """Threads the oracle's BLAS actually runs with, as the BLAS library reports it."""
+    try:
+        import numpy  # noqa: F401  (threadpoolctl reports only libraries already loaded)
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"]), info[0].get("internal_api", "blas")
+    except ImportError:
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
 
 
 def cpu_baseline(budget_s=15.0):
-    """fp64 oracle forward+backward on whole heads of the training workload, one head at a
-    time until the time budget is spent; scaled to TFLOP/s with the same algorithmic count."""
+    """fp64 oracle forward+backward on whole heads of the training workload's shape
+    (N=4096, d=128, causal), one head at a time until the time budget is spent or as many
+    heads as the workload has were done; scaled to TFLOP/s with the same algorithmic count."""
     import numpy as np
     import oracle
     from synth import default_scale, make_prefill
@@ -77,12 +97,26 @@ def cpu_baseline(budget_s=15.0):
         t_total += time.perf_counter() - t0
         heads += 1
     flops = heads * 3.5 * flops_fwd(1, 1, N, d, True)
-    cores = len(os.sched_getaffinity(0))
-    threads = os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS") or str(cores)
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads) if threads.isdigit() else cores,
-            "kind": "oracle",
-            "sample": f"{heads} whole head(s) (N={N}, d={d}, causal) of the B={B},H={H} training workload: "
-                      f"fp64 forward + backward materialising S and P, {t_total:.1f} s"}
+    threads, blas = blas_threads()
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} passes over one synthetic head (N={N}, d={d}, causal, seed 1004) of the "
+                      f"training workload's shape: fp64 forward + backward materialising S and P, "
+                      f"{t_total:.1f} s on {threads} {blas} threads "
+                      f"({len(os.sched_getaffinity(0))} host cores visible)"}
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """Plain device-to-device copies of a known size, for scaling rocprofv3's FETCH_SIZE /
+    WRITE_SIZE counters to bytes (each copy reads and writes `nbytes`)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
 def main():
@@ -91,10 +125,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
