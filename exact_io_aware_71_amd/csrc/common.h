@@ -22,6 +22,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace xattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -31,6 +34,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -125,5 +138,40 @@ __device__ __forceinline__ bf16x8 ld_tr_operand(const char* tile, int row0, int 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4, SGPR base + 32-bit
+// VGPR byte offset): lane i's bytes land at lds + 16 * i.  `base` and `lds` must be the same
+// for every lane of the wave.  Issued from inline assembly so that the compiler does not tie
+// later LDS reads of other buffers to its completion; the caller waits explicitly with
+// wait_vmem*() before a barrier that publishes the data.  M0 holds the LDS destination;
+// nothing else in these kernels keeps a value in M0.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, const void* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0v) : "memory");
+}
+
+// s_waitcnt vmcnt(0): every global load (register or LDS destination) of this wave has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(n): all but the n most recent global loads of this wave have landed (loads
+// complete in order).
+template <int n>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations (lgkmcnt(0)), not for
+// outstanding global loads, so prefetches may stay in flight across it.  The wavefront-scope
+// fences keep the compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Pins the instruction order: the scheduler moves nothing across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 }  // namespace xattn

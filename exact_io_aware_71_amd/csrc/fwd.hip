@@ -44,6 +44,9 @@
 #ifndef XATTN_FWD128_WPE
 #define XATTN_FWD128_WPE 2
 #endif
+#ifndef XATTN_FWD_PP
+#define XATTN_FWD_PP 1
+#endif
 #ifndef XATTN_FWD64_NQ
 #define XATTN_FWD64_NQ 1
 #endif
@@ -292,6 +295,356 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
+// Ping-pong forward (bf16).  Eight waves, two per SIMD; each wave owns 32 query rows of a
+// 256-row block.  Every key tile is processed by each wave in two phases:
+//   M(t): O^T += V_{t-1}^T P_{t-1}^T and S_t^T = K_t Q^T   (MFMA + LDS reads),
+//   V(t): online softmax of S_t into P_t                   (vector ALU only).
+// Waves 0-3 (group 0) and 4-7 (group 1) run the same sequence one phase apart, so on every
+// SIMD one wave issues MFMAs while its partner does the softmax, and the matrix core and the
+// vector ALU work at the same time.  Phases are separated by workgroup barriers ("slots").
+// The LDS holds two stages; stage t&1 holds the pair {K_t, V_{t-1}} that the M(t) phases of
+// both groups read in slots 2t and 2t+1.  The pair t+1 is copied global -> LDS directly
+// (no registers) starting in slot 2t and must have landed by the end of slot 2t+1.
+#ifndef XATTN_PP_LOOKAHEAD
+#define XATTN_PP_LOOKAHEAD 8
+#endif
+#ifndef XATTN_PP_PRIO
+#define XATTN_PP_PRIO 1
+#endif
+
+template <int D>
+struct PPShape {
+  static constexpr int BN = kFwdBN, KB = BN / 32, DC = D / 16, DB = D / 32;
+  static constexpr int TILE = BN * D * 2;          // bytes of one K or V tile
+  static constexpr int NPV = KB * 2 * DB;          // P V MFMAs per tile
+  static constexpr int NQK = DC * KB;              // Q K^T MFMAs per tile
+};
+
+// One M phase: NPV MFMAs of O^T += V^T P^T (if PV) then NQK MFMAs of S^T = K Q^T (if QK), each
+// operand read from LDS LOOKAHEAD MFMAs ahead of its use, in a fixed issue order.
+// Lane-dependent LDS byte offsets of the M-phase operands inside a swizzled 64 x D tile.  The
+// swizzle depends on the row modulo 16 only, so for row blocks starting at multiples of 16
+// the block's row offset is a compile-time constant added to these.
+template <int D>
+struct PPOffsets {
+  uint32_t k[PPShape<D>::DC];      // K operand (A of S^T = K Q^T): row l32, chunk 2c + h32
+  uint32_t v[PPShape<D>::DB][2];   // V^T operand (transposing reads): rows rl and rl + 8
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, h32 = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < PPShape<D>::DC; ++c) k[c] = swz<D>(l32, 2 * c + h32);
+    const int G = lane >> 4, j = lane & 15;
+    const int rl = 4 * (G >> 1) + (j >> 2), cl = 16 * (G & 1) + 4 * (j & 3);
+#pragma unroll
+    for (int db = 0; db < PPShape<D>::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v[db][e] = swz_elem<D>(rl + 8 * e, db * 32 + cl);
+  }
+  // Switch between the two LDS stages (stage size a power of two larger than every offset).
+  __device__ __forceinline__ void toggle(uint32_t stage_bytes) {
+#pragma unroll
+    for (int c = 0; c < PPShape<D>::DC; ++c) k[c] ^= stage_bytes;
+#pragma unroll
+    for (int db = 0; db < PPShape<D>::DB; ++db) {
+      v[db][0] ^= stage_bytes;
+      v[db][1] ^= stage_bytes;
+    }
+  }
+};
+
+// hook(k), k = 0 .. NHOOK-1, is called at evenly spaced points between the MFMAs.
+template <int D, bool PV, bool QK, int NHOOK, typename Hook>
+__device__ __forceinline__ void pp_mphase(const char* ks, const char* vs, const bf16x8 (&pb)[PPShape<D>::KB][2],
+                                          const bf16x8 (&qreg)[PPShape<D>::DC], f32x16 (&acc)[PPShape<D>::DB],
+                                          f32x16 (&s)[PPShape<D>::KB], const PPOffsets<D>& ofs, Hook&& hook) {
+  using S = PPShape<D>;
+  constexpr int L = XATTN_PP_LOOKAHEAD;
+  constexpr int N0 = PV ? S::NPV : 0;
+  constexpr int NOPS = N0 + (QK ? S::NQK : 0);
+  auto operand = [&](auto ic) -> bf16x8 {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < N0) {  // (kb, sh, db) with db fastest; rows kb*32 + 16*sh + {rl, rl+8}
+      constexpr int db = i % S::DB, sh = (i / S::DB) % 2, kb = i / (2 * S::DB);
+      const char* base = vs + (kb * 32 + 16 * sh) * (2 * D);
+      return join_tr(ds_read_tr16(base + ofs.v[db][0]), ds_read_tr16(base + ofs.v[db][1]));
+    } else {                 // (c, kb) with kb fastest; rows kb*32 + l32
+      constexpr int j = i - N0, kb = j % S::KB, c = j / S::KB;
+      return *reinterpret_cast<const bf16x8*>(ks + kb * 32 * (2 * D) + ofs.k[c]);
+    }
+  };
+  if constexpr (QK) {
+#pragma unroll
+    for (int kb = 0; kb < S::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  }
+  bf16x8 buf[L];
+  static_for<(L < NOPS ? L : NOPS)>([&](auto ic) { buf[decltype(ic)::value] = operand(ic); });
+  sched_fence();
+  static_for<NOPS>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < N0) {
+      constexpr int db = i % S::DB, sh = (i / S::DB) % 2, kb = i / (2 * S::DB);
+      acc[db] = mfma32(buf[i % L], pb[kb][sh], acc[db]);
+    } else {
+      constexpr int j = i - N0, kb = j % S::KB, c = j / S::KB;
+      s[kb] = mfma32(buf[i % L], qreg[c], s[kb]);
+    }
+    if constexpr (i + L < NOPS) buf[i % L] = operand(std::integral_constant<int, i + L>{});
+    static_for<NHOOK>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      if constexpr (i == (2 * kk + 1) * NOPS / (2 * NHOOK)) hook(kk);
+    });
+    sched_fence();
+  });
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
+    int n_qtiles, int BH) {
+  using S = PPShape<D>;
+  constexpr int NW = 8, BM = 256, BN = S::BN, KB = S::KB, DC = S::DC, DB = S::DB, TILE = S::TILE;
+  constexpr int STAGE = 2 * TILE;                // one pair {K_t, V_{t-1}}
+  constexpr int NSTAGE = 4;
+  constexpr int RPC = 1024 / (2 * D);            // tile rows covered by one 1 KB wave copy
+  constexpr int CPT = TILE / 1024;               // wave copies per tile
+  constexpr int CPW = CPT / NW;                  // copies per wave and tile
+  static_assert(CPW >= 1 && CPT % NW == 0, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];  // [stage][K | V]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int grp = wave >> 2;                     // wave w runs on SIMD w % 4
+  const int rb = 2 * (wave & 3) + grp;           // the two waves of a SIMD own adjacent rows
+
+  int bh, qt;
+  fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hk = hq / (Hq / Hkv);
+  const uint16_t* qp = q + (size_t)bh * N * D;
+  const uint16_t* kp = k + (size_t)(b * Hkv + hk) * N * D;
+  const uint16_t* vp = v + (size_t)(b * Hkv + hk) * N * D;
+  const int q0 = qt * BM;
+  const int qw0 = q0 + rb * 32;
+
+  // Q^T operand: lane holds query qw0 + l32, features 16c + 8*h32 .. +7.
+  bf16x8 qreg[DC];
+  {
+    const int qi = qw0 + l32;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (qi < N) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
+      qreg[c] = as_bf16x8(u);
+    }
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  f32x16 s[KB];
+  bf16x8 pb[KB][2];
+  float m_run = -INFINITY, l_run = 0.f;
+  PPOffsets<D> ofs;
+  ofs.init(lane);
+
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int T = (kv_end + BN - 1) / BN;
+
+  // Pair t lives in LDS stage gray(t mod 4), so consecutive pairs differ in one stage bit and
+  // the M phase moves its operand offsets on with one XOR.  Every wave copies CPW of the 1 KB
+  // blocks of each tile: wave copy j covers tile bytes [1024 j, 1024 j + 1024), i.e. rows
+  // RPC*j .. RPC*j + RPC-1.  Lane l fills physical chunk l of the block: row RPC*j + l/(D/8),
+  // swizzled chunk l%(D/8), so it reads logical chunk (l%(D/8)) ^ swizzle(row); that offset
+  // is fixed per wave and copy.  Rows past N read row N-1 (finite data whose probabilities
+  // are zero).
+  auto stage_of = [](int t) { const int m = t & 3; return m ^ (m >> 1); };
+  const int lrow = lane / (D / 8);
+  uint32_t loff[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int r = RPC * (wave * CPW + i) + lrow;
+    loff[i] = lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(r, 0) >> 4) & (D / 8 - 1)));
+  }
+  // This wave's copy i of tile `tile` of K (is_k) or V into the stage of pair p.
+  auto copy = [&](int tile, bool is_k, int p, int i) __attribute__((always_inline)) {
+    const int j = wave * CPW + i;
+    const int row0 = tile * BN + RPC * j;
+    const char* base = reinterpret_cast<const char*>(is_k ? kp : vp);
+    const char* dst = smem + stage_of(p) * STAGE + (is_k ? 0 : TILE) + 1024 * j;
+    // Byte offsets stay below 2^31: the API bounds N*d*2 per head well under that.
+    if (row0 + RPC <= N) {
+      dma16(base, (uint32_t)row0 * (2 * D) + loff[i], dst);
+    } else {
+      const int row = min(row0 + lrow, N - 1);
+      dma16(base, (uint32_t)row * (2 * D) + (loff[i] - lrow * (2 * D)), dst);
+    }
+  };
+  // A wave whose queries all precede tile t has nothing to add for it (causal skip).
+  auto active = [&](int t) __attribute__((always_inline)) { return !CAUSAL || t * BN <= qw0 + 31; };
+
+  // V(t): online softmax of S_t ([OPT] §3.2.1) in base 2 with a lazy reference max; hook(k)
+  // is called at four points spread over the phase (to issue tile copies evenly).
+  auto vphase = [&](int t, auto&& hook) __attribute__((always_inline)) {
+    const int t0 = t * BN;
+    if ((t0 + BN > N) || (CAUSAL && t0 + BN - 1 > qw0)) {
+      const int qi = qw0 + l32;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          if (kj >= N || (CAUSAL && kj > qi)) s[kb][r] = -INFINITY;
+        }
+    }
+    // Independent chains throughout, so that one wave keeps the ALU busy on its own.
+    float mx4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx4[j] = fmaxf(s[0][4 * j], s[0][4 * j + 1]);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 2 : 0); r < 4; r += 2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx4[j] = fmaxf(fmaxf(mx4[j], s[kb][4 * j + r]), s[kb][4 * j + r + 1]);
+    hook(0);
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    mx = max_xor32(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {  // wave-uniform branch
+      const float m_new = fmaxf(m_run, mx);  // finite: key 0 is never masked
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    // p = 2^(s * scale * log2 e - m), in place.
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], scale_log2, -m_run);
+    hook(1);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(s[kb][r]);
+    hook(2);
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs4[r & 3] += s[kb][r];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        u32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(s[kb][8 * sh + 2 * e], s[kb][8 * sh + 2 * e + 1]);
+        pb[kb][sh] = as_bf16x8(u);
+      }
+    hook(3);
+    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+  };
+
+  // Prologue: pairs 0 and 1, a zero V half in stage 0 and zero P (so M(0)'s P V part adds
+  // nothing).
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    copy(0, true, 0, i);
+    if (1 < T) copy(1, true, 1, i);
+    copy(0, false, 1, i);
+  }
+  for (int i = tid; i < TILE / 16; i += NW * 64)
+    *reinterpret_cast<u32x4*>(smem + TILE + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) pb[kb][sh] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  wait_vmem();  // also covers the Q loads
+  lds_barrier();
+
+  // Slot schedule (2T + 2 slots, one barrier each).  Group 0: slot 2t = M(t), slot 2t+1 =
+  // V(t); group 1 runs one slot later.  Copies run two pairs ahead: every wave copies its
+  // blocks of K_{t+2} in slot 2t and of V_{t+1} in slot 2t+1, spread over whatever phase it
+  // is in, into stage gray((t+2) mod 4), last read in slot 2t-3.  Pair t+1 is waited for at
+  // the end of slot 2t+1.  M(T) computes an S that is never used.  A wave whose rows all
+  // precede tile t-1 (causal) has no M(t) or later work.
+  const int slots = 2 * T + 2;
+  for (int sl = 0; sl < slots; ++sl) {
+    const int cpair = (sl >> 1) + 2;
+    const bool cis_k = !(sl & 1);
+    const int ctile = cis_k ? cpair : cpair - 1;
+    const bool has_copy = ctile < T;
+    auto hook = [&](int kq) __attribute__((always_inline)) {
+      if (has_copy) copy(ctile, cis_k, cpair, kq);
+    };
+    const int ls = sl - grp;
+    if (ls >= 0 && ls <= 2 * T) {
+      const int t = ls >> 1;
+      if (!(ls & 1)) {
+        if (t == 0 || active(t - 1)) {
+          if (XATTN_PP_PRIO) __builtin_amdgcn_s_setprio(1);
+          pp_mphase<D, true, true, CPW>(smem, smem + TILE, pb, qreg, acc, s, ofs, hook);
+          if (XATTN_PP_PRIO) __builtin_amdgcn_s_setprio(0);
+          ofs.toggle(((t & 1) ? 2 : 1) * STAGE);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CPW; ++i) hook(i);
+        }
+      } else if (t < T) {
+        // Also run for a causally finished wave: its tile is fully masked, so P = 0 and the
+        // statistics do not move.
+        vphase(t, [&](int kq) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < CPW; ++i)
+            if (i * 4 / CPW == kq) hook(i);
+        });
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) hook(i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) hook(i);
+    }
+    if (sl & 1) {
+      // Pair t+1 (t = sl/2) must have landed; this wave's newer copies (K_{t+2}, V_{t+1})
+      // may stay in flight.
+      const int t = sl >> 1;
+      if (t + 2 < T) wait_vmem_n<2 * CPW>();
+      else if (t + 1 < T) wait_vmem_n<CPW>();
+      else wait_vmem();
+    }
+    lds_barrier();
+  }
+
+  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
+  uint16_t* op = o + (size_t)bh * N * D;
+  const float lt = sum_xor32(l_run);
+  const float inv = 1.f / lt;
+  const int qi = qw0 + l32;
+  if (qi < N) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = db * 32 + 8 * jj + 4 * h32;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv);
+        w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
+      }
+    if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run + fast_log2(lt)) * kLn2;
+  }
+}
+
 // fp32 inputs (d = 64): the same tiled online softmax with v_mfma_f32_32x32x2_f32, one
 // wave per 32 queries and 32-key tiles, single-buffered.  Keeps full fp32 precision.
 template <bool CAUSAL>
@@ -373,6 +726,24 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 }
 
 // ------------------------------------------------------------------------- host launchers
+template <int D>
+static hipError_t launch_fwd_pp_t(const FwdArgs& a) {
+  constexpr int BM = 256;
+  const int n_qtiles = (a.N + BM - 1) / BM;
+  const int BH = a.B * a.Hq;
+  const dim3 grid(n_qtiles * BH), block(512);
+  const float sl2 = a.scale * kLog2e;
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_pp_kernel<D, true>), grid, block, 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
+                       n_qtiles, BH);
+  else
+    hipLaunchKernelGGL((fwd_pp_kernel<D, false>), grid, block, 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
+                       n_qtiles, BH);
+  return hipGetLastError();
+}
+
 template <int D, int NQ, int NW, int WPE>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
   constexpr int BM = NW * NQ * 32;
@@ -406,6 +777,9 @@ hipError_t launch_fwd(const FwdArgs& a) {
                          a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
     return hipGetLastError();
   }
+#if XATTN_FWD_PP
+  if (a.d == 128) return launch_fwd_pp_t<128>(a);
+#endif
   if (a.d == 128) return launch_fwd_bf16_t<128, XATTN_FWD128_NQ, XATTN_FWD128_NW, XATTN_FWD128_WPE>(a);
   return launch_fwd_bf16_t<64, XATTN_FWD64_NQ, XATTN_FWD64_NW, XATTN_FWD64_WPE>(a);
 }
