@@ -121,11 +121,14 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   return from_hip(xattn::launch_fwd(a), "attn_fwd launch");
 }
 
+// Rows of the backward's per-row statistics are padded to whole 64-query tiles.
+int bwd_npad(int N) { return (N + 63) / 64 * 64; }
+
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   (void)Hkv;
   (void)d;
   if (B <= 0 || Hq <= 0 || N <= 0) return 0;
-  return align_up((size_t)B * Hq * N * sizeof(float), 256);
+  return align_up(2 * (size_t)B * Hq * bwd_npad(N) * sizeof(float), 256);
 }
 
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -148,7 +151,7 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     return fail(ATTN_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   xattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal ? 1 : 0, scale,
-                   (float*)workspace, (hipStream_t)stream};
+                   (float*)workspace, bwd_npad(N), (hipStream_t)stream};
   return from_hip(xattn::launch_bwd(a), "attn_bwd launch");
 }
 

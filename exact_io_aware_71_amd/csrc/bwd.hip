@@ -13,7 +13,8 @@
 //   dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
 // Three launches, deterministic (no atomics):
-//   1. bwd_delta_kernel: D = rowsum(dO * O) (HBM-bound streaming pass).
+//   1. bwd_prep_kernel: D = rowsum(dO * O) and LSE * log2(e), into row-padded arrays of the
+//      caller's workspace (padding rows get LSE = +inf, so their probabilities vanish).
 //   2. bwd_dkdv_kernel: one workgroup per 128 keys; each wave keeps its 32 keys' K and V
 //      rows in registers (B operands of S = Q K^T and dP = dO V^T) and the dK, dV
 //      accumulators in registers while Q/dO tiles of 64 queries stream through a double-
@@ -27,28 +28,41 @@
 #include "common.h"
 #include "launch.h"
 
+#ifndef XATTN_DKDV_NS
+#define XATTN_DKDV_NS 2
+#endif
+
 namespace xattn {
 
-// ------------------------------------------------------------------ D = rowsum(dO * O)
+// ------------------------------------------------------------------ D = rowsum(dO * O), LSE2
+// Row r of the padded [BH, Npad] arrays: r % Npad < N holds real statistics, the rest padding.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
-                                                        const uint16_t* __restrict__ dout,
-                                                        float* __restrict__ delta, int rows) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
+                                                       const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ lse2, float* __restrict__ delta,
+                                                       int N, int Npad, int rows_pad) {
   constexpr int LPR = D / 8;             // lanes per row, 8 features each
   constexpr int RPB = 256 / LPR;         // rows per block
   const int tid = threadIdx.x;
   const int row = blockIdx.x * RPB + tid / LPR;
   const int c = tid % LPR;
+  const int bh = row / Npad, i = row - bh * Npad;
+  const bool real = row < rows_pad && i < N;
   float s = 0.f;
-  if (row < rows) {
-    const u32x4 a = ld_global16(o + (size_t)row * D + 8 * c);
-    const u32x4 g = ld_global16(dout + (size_t)row * D + 8 * c);
+  if (real) {
+    const size_t off = ((size_t)bh * N + i) * D + 8 * c;
+    const u32x4 a = ld_global16(o + off);
+    const u32x4 g = ld_global16(dout + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) s += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && c == 0) delta[row] = s;
+  if (row < rows_pad && c == 0) {
+    delta[row] = s;
+    lse2[row] = real ? lse[(size_t)bh * N + i] * kLog2e : INFINITY;
+  }
 }
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int sh) {
@@ -68,180 +82,218 @@ struct BwdTile {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ lse, const float* __restrict__ delta, const uint16_t* __restrict__ dout,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, float scale, float scale_log2,
-    int n_ktiles, int BH) {
-  constexpr int NW = 4, BK = NW * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32;
-  constexpr int CPT = BQ * D / 8 / (NW * 64);
+    const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int N, int Npad, float scale, float scale_log2, int BH) {
+  constexpr int NW = 8, NG = 4, BK = NG * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32;
   using T = BwdTile<D>;
-  constexpr int STAGE = 2 * T::BYTES + 2 * BQ * 4;  // Q, dO, lse2, delta
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int STAGE = 2 * T::BYTES + 2 * BQ * 4;  // Q, dO, LSE2, D
+  constexpr int NS = XATTN_DKDV_NS;                 // LDS ring: tile t+NS-1 loads during tile t
+  static_assert(NS == 2 || NS == 3, "ring depth");
+  constexpr int RPC = 1024 / (2 * D), CPTT = T::BYTES / 1024, CPW = 2 * CPTT / NW;
+  static_assert(CPTT % NW == 0 || (2 * CPTT) % NW == 0, "tile pieces split over the waves");
+  static_assert(NW % (16 / RPC) == 0, "pieces of a wave share their swizzle");
+  // Tile ring, then the P hand-over buffers: [key group][32-query block][register][lane] fp32.
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + NG * (BQ / 32) * 16 * 64 * 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  // Waves g and g + NG run on the same SIMD and own the same 32 keys: the first accumulates
+  // dV, the second dK (see the tile loop below).
+  const int grp = wave & (NG - 1), role = wave / NG;
   const int bh = blockIdx.x % BH;
   // Causal: early key tiles see the most queries and are dispatched first.
-  const int ktile = blockIdx.x / BH;
-  const int k0 = ktile * BK;
-  const int kw0 = k0 + wave * 32;
+  const int k0 = (blockIdx.x / BH) * BK;
+  const int kw0 = k0 + grp * 32;
   const uint16_t* qp = q + (size_t)bh * N * D;
   const uint16_t* kp = k + (size_t)bh * N * D;
   const uint16_t* vp = v + (size_t)bh * N * D;
   const uint16_t* dop = dout + (size_t)bh * N * D;
-  const float* lsep = lse + (size_t)bh * N;
-  const float* dlp = delta + (size_t)bh * N;
-
-  // K^T and V^T operands (B of S = Q K^T, dP = dO V^T): lane owns key kw0 + l32.
-  bf16x8 kreg[DC], vreg[DC];
-  {
-    const int kj = kw0 + l32;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      u32x4 a = {0u, 0u, 0u, 0u}, bb = {0u, 0u, 0u, 0u};
-      if (kj < N) {
-        a = ld_global16(kp + (size_t)kj * D + 16 * c + 8 * h32);
-        bb = ld_global16(vp + (size_t)kj * D + 16 * c + 8 * h32);
-      }
-      kreg[c] = as_bf16x8(a);
-      vreg[c] = as_bf16x8(bb);
-    }
-  }
-  f32x16 dk_acc[DB], dv_acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { dk_acc[db][r] = 0.f; dv_acc[db][r] = 0.f; }
+  // stats = [LSE2 | D], each [BH, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
+  const uint32_t lse_off = (uint32_t)((size_t)bh * Npad * 4);
+  const uint32_t dl_off = (uint32_t)(((size_t)BH + bh) * Npad * 4);
 
   const int qt_begin = CAUSAL ? (k0 / BQ) : 0;
   const int qt_end = (N + BQ - 1) / BQ;
 
-  u32x4 pq[CPT], pdo[CPT];
-  float plse = 0.f, pdl = 0.f;
-  auto load_tile = [&](int t) {
-    const int q0 = t * BQ;
+  // Tile copies: wave w copies 1 KB pieces j = w, w + NW, ... of [Q tile | dO tile]; piece j
+  // covers tile rows RPC*(j % CPTT) ...; lane l fills physical chunk l, i.e. logical chunk
+  // (l%(D/8)) ^ swizzle(row), the same swizzle for all pieces of a wave.  Rows past N read
+  // row N-1 (their LSE2 is +inf, so they contribute nothing).  Waves 0 and 1 also copy the
+  // tile's 64 LSE2 and 64 D values (the padded rows hold +inf and 0).
+  const int lrow = lane / (D / 8);
+  const uint32_t loff0 =
+      lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(RPC * wave + lrow, 0) >> 4) & (D / 8 - 1)));
+  auto copy_tile = [&](int t, int st) __attribute__((always_inline)) {
+    char* dst = smem + st * STAGE;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NW * 64;
-      const int row = c / (D / 8), col = c % (D / 8), qi = q0 + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u};
-      if (qi < N) {
-        a = ld_global16(qp + (size_t)qi * D + col * 8);
-        g = ld_global16(dop + (size_t)qi * D + col * 8);
+    for (int i = 0; i < CPW; ++i) {
+      const int j = wave + NW * i;
+      const bool is_q = j < CPTT;
+      const int jt = is_q ? j : j - CPTT;
+      const int row0 = t * BQ + RPC * jt;
+      const uint16_t* base = is_q ? qp : dop;
+      char* d = dst + (is_q ? 0 : T::BYTES) + 1024 * jt;
+      if (row0 + RPC <= N) {
+        dma16(base, (uint32_t)row0 * (2 * D) + loff0, d);
+      } else {
+        const int row = min(row0 + lrow, N - 1);
+        dma16(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), d);
       }
-      pq[i] = a;
-      pdo[i] = g;
     }
-    if (tid < BQ) {
-      const int qi = q0 + tid;
-      // Rows past N get lse = +inf so that their probabilities vanish.
-      plse = qi < N ? lsep[qi] * kLog2e : INFINITY;
-      pdl = qi < N ? dlp[qi] : 0.f;
-    }
+    if (wave < 2) dma4(stats, (wave == 0 ? lse_off : dl_off) + 4 * (t * BQ + lane), dst + 2 * T::BYTES + wave * BQ * 4);
   };
-  auto store_tile = [&](int stage) {
-    char* base = smem + stage * STAGE;
+  constexpr int CPW0 = CPW + 1;  // copies per tile issued by waves 0 and 1
+
+  // Ring prologue: tiles qt_begin .. qt_begin + NS - 2.
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NW * 64;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(base + swz<D>(row, col)) = pq[i];
-      *reinterpret_cast<u32x4*>(base + T::BYTES + swz<D>(row, col)) = pdo[i];
+  for (int j = 0; j < NS - 1; ++j)
+    if (qt_begin + j < qt_end) copy_tile(qt_begin + j, j);
+
+  // K^T (dV wave) or V^T (dK wave), the B operand of S = Q K^T or dP = dO V^T: lane owns key
+  // kw0 + l32.
+  const int kj = kw0 + l32;
+  const uint16_t* kvp = role == 0 ? kp : vp;
+  bf16x8 kreg[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (kj < N) a = ld_global16(kvp + (size_t)kj * D + 16 * c + 8 * h32);
+    kreg[c] = as_bf16x8(a);
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  wait_vmem();
+  lds_barrier();
+
+  // End of tile t: tile t+1 must have landed; with three stages this wave's copies of tile
+  // t+2 may stay in flight.
+  auto end_tile = [&](int t) __attribute__((always_inline)) {
+    if (NS > 2 && t + 2 < qt_end) {
+      if (wave < 2) wait_vmem_n<CPW0>();
+      else wait_vmem_n<CPW>();
+    } else {
+      wait_vmem();
     }
-    if (tid < BQ) {
-      reinterpret_cast<float*>(base + 2 * T::BYTES)[tid] = plse;
-      reinterpret_cast<float*>(base + 2 * T::BYTES + BQ * 4)[tid] = pdl;
-    }
+    lds_barrier();
   };
 
-  if (qt_begin < qt_end) {
-    load_tile(qt_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int t = qt_begin; t < qt_end; ++t) {
-    const int st = (t - qt_begin) & 1;
-    if (t + 1 < qt_end) load_tile(t + 1);
-    const char* qs = smem + st * STAGE;
-    const char* dos = qs + T::BYTES;
-    const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
-    const float* dls = ls + BQ;
-    const int q0 = t * BQ;
+  // Per tile, two phases separated by a barrier.  Phase A: the dV wave computes S = Q K^T,
+  // P = 2^(S scale log2 e - LSE2) (masked) and hands P (fp32) to its partner through LDS;
+  // the dK wave computes dP = dO V^T meanwhile.  Phase B: the dV wave adds P^T dO to dV; the
+  // dK wave reads P, forms dS = P (dP - D) and adds dS^T Q to dK.  Every product is computed
+  // once, 16 MFMAs per 32-query block on each wave of the pair.
+  constexpr int NQB = BQ / 32;
+  float* pbuf = reinterpret_cast<float*>(smem + NS * STAGE) + grp * (NQB * 16 * 64);  // [qb][r][lane]
+  if (role == 0) {
+    for (int t = qt_begin; t < qt_end; ++t) {
+      const int it = t - qt_begin;
+      if (t + NS - 1 < qt_end) copy_tile(t + NS - 1, (it + NS - 1) % NS);
+      const char* qs = smem + (it % NS) * STAGE;
+      const char* dos = qs + T::BYTES;
+      const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
+      const int q0 = t * BQ;
+      bf16x8 pa[NQB][2];
 #pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      const int qb0 = q0 + qb * 32;
-      // Causal: a query block entirely before this wave's keys contributes nothing.
-      if (CAUSAL && qb0 + 31 < kw0) continue;
-      f32x16 s, dp;
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qb0 = q0 + qb * 32;
+        f32x16 sv;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+        for (int r = 0; r < 16; ++r) sv[r] = 0.f;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const int off = swz<D>(qb * 32 + l32, 2 * c + h32);
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qs + off);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dos + off);
-        s = mfma32(aq, kreg[c], s);
-        dp = mfma32(ad, vreg[c], dp);
-      }
-      // Lane owns key kw0 + l32; register r holds query qb0 + 8(r/4) + 4*h32 + r%4.
-      const int kj = kw0 + l32;
-      const bool need_mask = CAUSAL && (qb0 < kw0 + 31);
+        for (int c = 0; c < DC; ++c)
+          sv = mfma32(*reinterpret_cast<const bf16x8*>(qs + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], sv);
+        // Lane owns key kj; register r holds query qb0 + 8(r/4) + 4*h32 + r%4.  Queries before
+        // the key (causal) get P = 0, which also covers blocks wholly before this wave's keys.
+        const bool need_mask = CAUSAL && (qb0 < kw0 + 31);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qoff = qb * 32 + 8 * r4 + 4 * h32;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qoff);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qoff);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * r4 + 4 * h32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * r4 + i;
-          float p = fast_exp2(fmaf(s[r], scale_log2, -l4[i]));
-          if (need_mask && kj > qb0 + 8 * r4 + 4 * h32 + i) p = 0.f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[i]);
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * r4 + i;
+            float p = fast_exp2(fmaf(sv[r], scale_log2, -l4[i]));
+            if (need_mask && kj > qb0 + 8 * r4 + 4 * h32 + i) p = 0.f;
+            sv[r] = p;
+          }
         }
-      }
-      // dV += P^T dO ; dK += dS^T Q  (contraction over the 32 queries, 16 per MFMA).
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const bf16x8 pa = pack8(s, sh);
-        const bf16x8 dsa = pack8(dp, sh);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 bdo = ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane);
-          const bf16x8 bq = ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane);
-          dv_acc[db] = mfma32(pa, bdo, dv_acc[db]);
-          dk_acc[db] = mfma32(dsa, bq, dk_acc[db]);
-        }
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<f32x4*>(pbuf + (qb * 4 + r4) * 256 + 4 * lane) =
+              f32x4{sv[4 * r4], sv[4 * r4 + 1], sv[4 * r4 + 2], sv[4 * r4 + 3]};
+        pa[qb][0] = pack8(sv, 0);
+        pa[qb][1] = pack8(sv, 1);
       }
+      lds_barrier();  // P visible to the dK wave
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mfma32(pa[qb][sh], ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+      end_tile(t);
     }
-    if (t + 1 < qt_end) store_tile(st ^ 1);
-    __syncthreads();
+  } else {
+    for (int t = qt_begin; t < qt_end; ++t) {
+      const int it = t - qt_begin;
+      if (t + NS - 1 < qt_end) copy_tile(t + NS - 1, (it + NS - 1) % NS);
+      const char* qs = smem + (it % NS) * STAGE;
+      const char* dos = qs + T::BYTES;
+      const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
+      f32x16 dp[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+          dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dos + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], dp[qb]);
+      }
+      lds_barrier();  // P of this tile written by the dV wave
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(pbuf + (qb * 4 + r4) * 256 + 4 * lane);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * r4 + 4 * h32);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dp[qb][4 * r4 + i] = p4[i] * (dp[qb][4 * r4 + i] - d4[i]);
+        }
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const bf16x8 dsa = pack8(dp[qb], sh);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mfma32(dsa, ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+        }
+      }
+      end_tile(t);
+    }
   }
 
   // C layout: lane holds feature db*32 + l32 of keys kw0 + 8(r/4) + 4*h32 + r%4.
-  uint16_t* dkp = dk + (size_t)bh * N * D;
-  uint16_t* dvp = dv + (size_t)bh * N * D;
+  uint16_t* outp = (role == 0 ? dv : dk) + (size_t)bh * N * D;
+  const float oscale = role == 0 ? 1.f : scale;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kj = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      if (kj < N) {
-        const size_t off = (size_t)kj * D + db * 32 + l32;
-        dkp[off] = (uint16_t)(pack_bf16x2(dk_acc[db][r] * scale, 0.f) & 0xffffu);
-        dvp[off] = (uint16_t)(pack_bf16x2(dv_acc[db][r], 0.f) & 0xffffu);
-      }
+      const int kr = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      if (kr < N) outp[(size_t)kr * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(acc[db][r] * oscale, 0.f) & 0xffffu);
     }
 }
 
 // ------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ lse, const float* __restrict__ delta, const uint16_t* __restrict__ dout,
-    uint16_t* __restrict__ dq, int N, float scale, float scale_log2, int n_qtiles, int BH) {
+    const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, int N,
+    int Npad, float scale, float scale_log2, int n_qtiles, int BH) {
   constexpr int NW = 4, BM = NW * 32, BN = kBwdBK, KB = BN / 32, DC = D / 16, DB = D / 32;
-  constexpr int CPT = BN * D / 8 / (NW * 64);
   using T = BwdTile<D>;
   constexpr int STAGE = 2 * T::BYTES;  // K, V
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
@@ -267,8 +319,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     qreg[c] = as_bf16x8(a);
     doreg[c] = as_bf16x8(g);
   }
-  const float lse2 = qi < N ? lse[(size_t)bh * N + qi] * kLog2e : INFINITY;
-  const float dl = qi < N ? delta[(size_t)bh * N + qi] : 0.f;
+  // stats = [LSE2 | D], each [BH, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
+  const float lse2 = qi < N ? stats[(size_t)bh * Npad + qi] : INFINITY;
+  const float dl = qi < N ? stats[((size_t)BH + bh) * Npad + qi] : 0.f;
 
   f32x16 dq_acc[DB];
 #pragma unroll
@@ -278,38 +331,40 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
-  u32x4 pk[CPT], pv[CPT];
-  auto load_tile = [&](int t) {
-    const int t0 = t * BN;
+  // K/V tiles arrive by direct global -> LDS copies (no staging registers, which lets two
+  // workgroups share a CU).  Wave w copies 1 KB pieces j = w, w + NW, ... of [K tile | V
+  // tile]; piece j covers tile rows RPC*(j % CPTT) ...; lane l fills physical chunk l, i.e.
+  // logical chunk (l%(D/8)) ^ swizzle(row).  The swizzle depends on the row modulo 16 only,
+  // which is the same for all pieces of a wave.  Rows past N read row N-1 (masked below).
+  constexpr int RPC = 1024 / (2 * D), CPTT = T::BYTES / 1024, CPW = 2 * CPTT / NW;
+  static_assert(CPTT % NW == 0 && NW % (16 / RPC) == 0, "pieces of a wave share their swizzle");
+  const int lrow = lane / (D / 8);
+  const uint32_t loff0 =
+      lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(RPC * wave + lrow, 0) >> 4) & (D / 8 - 1)));
+  auto copy_tile = [&](int t, int stage) __attribute__((always_inline)) {
+    char* dst = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NW * 64;
-      const int row = c / (D / 8), col = c % (D / 8), key = t0 + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, bb = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        a = ld_global16(kp + (size_t)key * D + col * 8);
-        bb = ld_global16(vp + (size_t)key * D + col * 8);
+    for (int i = 0; i < CPW; ++i) {
+      const int j = wave + NW * i;
+      const bool is_k = j < CPTT;
+      const int jt = is_k ? j : j - CPTT;
+      const int row0 = t * BN + RPC * jt;
+      const uint16_t* base = is_k ? kp : vp;
+      char* d = dst + (is_k ? 0 : T::BYTES) + 1024 * jt;
+      if (row0 + RPC <= N) {
+        dma16(base, (uint32_t)row0 * (2 * D) + loff0, d);
+      } else {
+        const int row = min(row0 + lrow, N - 1);
+        dma16(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), d);
       }
-      pk[i] = a;
-      pv[i] = bb;
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NW * 64;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(base + swz<D>(row, col)) = pk[i];
-      *reinterpret_cast<u32x4*>(base + T::BYTES + swz<D>(row, col)) = pv[i];
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  copy_tile(0, 0);
+  wait_vmem();  // also covers the Q/dO loads
+  lds_barrier();
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1);
+    if (t + 1 < ntiles) copy_tile(t + 1, (t + 1) & 1);
     const int t0 = t * BN;
     const char* ks = smem + (t & 1) * STAGE;
     const char* vs = ks + T::BYTES;
@@ -350,8 +405,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         }
       }
     }
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
-    __syncthreads();
+    wait_vmem();  // tile t+1 has landed
+    lds_barrier();
   }
   // C layout: lane holds feature db*32 + l32 of queries qw0 + 8(r/4) + 4*h32 + r%4.
   uint16_t* dqp = dq + (size_t)bh * N * D;
@@ -368,22 +423,25 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int BH = a.B * a.Hq;
-  const int rows = BH * a.N;
+  const int rows_pad = BH * a.Npad;
   const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((rows + 256 / (D / 8) - 1) / (256 / (D / 8))), dim3(256), 0,
-                     a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+  float* lse2 = a.stats;
+  float* delta = a.stats + (size_t)BH * a.Npad;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((rows_pad + RPB - 1) / RPB), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, lse2, delta, a.N, a.Npad, rows_pad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_kt = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.delta,
-                     (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.scale, sl2, n_kt, BH);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(512), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
+                     (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Npad, a.scale, sl2, BH);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.N + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.delta,
-                     (const uint16_t*)a.dout, (uint16_t*)a.dq, a.N, a.scale, sl2, n_qt, BH);
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
+                     (const uint16_t*)a.dout, (uint16_t*)a.dq, a.N, a.Npad, a.scale, sl2, n_qt, BH);
   return hipGetLastError();
 }
 

@@ -145,10 +145,25 @@ __device__ __forceinline__ u32x4 ld_global16(const void* p) {
 // later LDS reads of other buffers to its completion; the caller waits explicitly with
 // wait_vmem*() before a barrier that publishes the data.  M0 holds the LDS destination;
 // nothing else in these kernels keeps a value in M0.
+__device__ __forceinline__ const void* wave_uniform(const void* p) {
+  const uintptr_t u = (uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(((uintptr_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const void* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0v) : "memory");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(wave_uniform(base)), "s"(m0v)
+               : "memory");
+}
+
+// As dma16 with 4 bytes per lane (global_load_lds_dword): lane i's word lands at lds + 4 * i.
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, const void* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(wave_uniform(base)), "s"(m0v)
+               : "memory");
 }
 
 // s_waitcnt vmcnt(0): every global load (register or LDS destination) of this wave has landed.

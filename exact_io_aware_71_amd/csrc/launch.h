@@ -19,7 +19,8 @@ struct BwdArgs {
   void* dq; void* dk; void* dv;
   int B, Hq, Hkv, N, d, causal;
   float scale;
-  float* delta;  // [B,Hq,N] fp32 scratch inside the caller's workspace
+  float* stats;  // [2, B*Hq, Npad] fp32 scratch in the caller's workspace: LSE*log2(e), then D
+  int Npad;      // N rounded up to a multiple of 64
   hipStream_t stream;
 };
 

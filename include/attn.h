@@ -75,7 +75,9 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int B, int Hq, int Hkv, int N, int d, attn_dtype_t dtype, int causal,
                        float scale, void* stream);
 
-/* Bytes of device workspace attn_bwd needs (fp32 row statistics D = rowsum(dO * O)). */
+/* Bytes of device workspace attn_bwd needs: fp32 per-row statistics (LSE * log2(e) and
+ * D = rowsum(dO * O)) for every query row padded to a multiple of 64, i.e.
+ * 2 * B * Hq * roundup(N, 64) * 4 bytes, rounded up to 256. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /*

@@ -64,7 +64,8 @@ def bwd(ws=P, ws_bytes=1 << 30, Hq=2, Hkv=2, d=128, dt=1, scale=0.1, dq=P):
 
 def test_bwd_validation():
     need = lib.attn_bwd_workspace_bytes(1, 2, 2, 64, 128)
-    assert need == 512
+    assert need == 1024                      # LSE2 and D rows, padded to 64 queries
+    assert lib.attn_bwd_workspace_bytes(1, 2, 2, 65, 128) == 2 * 2 * 128 * 4
     assert bwd(dq=None) == 1
     assert bwd(Hq=4, Hkv=2) == 2           # grouped-query backward not implemented
     assert bwd(dt=0) == 2
