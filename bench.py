@@ -215,13 +215,21 @@ def main():
     del tr
 
     fwd_digest = source_digest("fwd.hip", "common.h")
+    bwd_digest = source_digest("bwd.hip", "common.h")
     dec_digest = source_digest("decode.hip", "common.h")
     roofline = {
-        "kernel": "fwd_bf16_kernel (attn_fwd, causal, B*H=32, N=4096, d=128)",
+        "kernel": "fwd_pp_kernel (attn_fwd, causal, B*H=32, N=4096, d=128)",
         "bound": "mfma", "achieved": f_fwd / (ms_fwd * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
     }
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
-    roofline["traffic"] = load_traffic("fwd_bf16_kernel", fwd_digest)
+    roofline["traffic"] = load_traffic("fwd_pp_kernel", fwd_digest)
+    bwd_traffic = [load_traffic(kn, bwd_digest) for kn in ("bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")]
+    roofline_bwd = {
+        "kernel": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd, causal, B*H=32, N=4096, d=128)",
+        "bound": "mfma", "achieved": f_bwd / (ms_bwd * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": f_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "traffic": None if None in bwd_traffic else sum(bwd_traffic),
+    }
     roofline_decode = {
         "kernel": "decode_split_kernel + decode_merge_kernel (attn_decode, B=64, Hq=32, Hkv=8, L=8192, d=128)",
         "bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS,
@@ -239,7 +247,7 @@ def main():
         "decode_GBps": dec_gbs,
         "ms": {"fwd": ms_fwd, "bwd": ms_bwd, "decode": ms_dec, "fwd_min": min(t_fwd), "bwd_min": min(t_bwd),
                "decode_min": min(t_dec), "wall_per_step": wall / args.steps * 1e3},
-        "roofline": roofline, "roofline_decode": roofline_decode,
+        "roofline": roofline, "roofline_bwd": roofline_bwd, "roofline_decode": roofline_decode,
         "spot_check_max_abs_err": spot,
         "gpu": torch.cuda.get_device_properties(0).gcnArchName,
     }
