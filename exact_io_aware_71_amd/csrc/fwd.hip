@@ -645,6 +645,373 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Interleaved forward (bf16, d = 128).  Four waves, one per SIMD, each owning 64 query rows
+// (two 32-row blocks) of a 256-row block, so every K or V operand read from LDS feeds two
+// MFMAs.  Each wave software-pipelines its own work over 32-key blocks u: in step u it issues
+//   O^T += V_{u-1}^T P_{u-1}^T  and  S_{u+1}^T = K_{u+1} Q^T        (32 MFMAs)
+// and, between those MFMAs, the online softmax of S_u into P_u       (vector ALU),
+// which are independent of each other, so the matrix core and the vector ALU of the SIMD
+// work at the same time without a second wave.  The S and P register sets alternate roles
+// between even and odd steps.  K and V arrive in 64-key tiles through direct global -> LDS
+// copies into two rings of four stages (128 KB); the two steps of tile t read K_t, K_{t+1},
+// V_{t-1}, V_t, copy K_{t+3} and V_{t+2}, and end with one barrier.  A rescale of O forced
+// by a moved running max is applied after the step's MFMAs, before P_u is added.
+#ifndef XATTN_FWD_ILV
+#define XATTN_FWD_ILV 1
+#endif
+#ifndef XATTN_ILV_LOOKAHEAD
+#define XATTN_ILV_LOOKAHEAD 4
+#endif
+
+// S^T = K Q^T block products for the interleaved kernel, written to vector registers (the
+// softmax reads them there), while O^T accumulates in accumulation registers.  Issued from inline
+// assembly because the compiler picks one register file for all MFMA results of a kernel.
+// The hardware chains back-to-back MFMAs on the same accumulator; a vector-ALU read of the
+// result must follow the last MFMA by at least 19 wait states (qk_result_fence).
+#ifndef XATTN_ILV_QKASM
+#define XATTN_ILV_QKASM 0
+#endif
+#ifndef XATTN_ILV_RB
+#define XATTN_ILV_RB 1
+#endif
+__device__ __forceinline__ void mfma_qk_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
+#if XATTN_ILV_QKASM == 1
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "a"(b));
+#elif XATTN_ILV_QKASM == 2
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
+#else
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  c = mfma32(a, b, z);
+#endif
+}
+__device__ __forceinline__ void mfma_qk_next(f32x16& c, const bf16x8& a, const bf16x8& b) {
+#if XATTN_ILV_QKASM == 1
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+#elif XATTN_ILV_QKASM == 2
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+#else
+  c = mfma32(a, b, c);
+#endif
+}
+__device__ __forceinline__ void qk_result_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+template <int D, int RB_>
+struct IlvShape {
+  static constexpr int BN = kFwdBN, DC = D / 16, DB = D / 32;
+  static constexpr int RB = RB_, NW = 8 / RB, BM = NW * RB * 32;
+  static constexpr int TILE = BN * D * 2;          // bytes of one K or V tile
+  static constexpr int NS = 4;                     // stages per ring
+  static constexpr int RPC = 1024 / (2 * D);       // tile rows per 1 KB wave copy
+  static constexpr int CPW = TILE / 1024 / NW;     // copies per wave and tile
+  static constexpr int NPV = 2 * DB;               // V^T operands per 32-key block
+  static constexpr int NQK = DC;                   // K operands per 32-key block
+};
+
+template <int D, int RB_, bool CAUSAL>
+__global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 / RB_, 2 / RB_))) void fwd_ilv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
+    int n_qtiles, int BH) {
+  using S = IlvShape<D, RB_>;
+  constexpr int BN = S::BN, DC = S::DC, DB = S::DB, RB = S::RB, NS = S::NS, NW = S::NW;
+  constexpr int TILE = S::TILE, CPW = S::CPW, RPC = S::RPC, NPV = S::NPV, NQK = S::NQK;
+  constexpr int NOPS = NPV + NQK, NMF = RB * NOPS, L = XATTN_ILV_LOOKAHEAD;
+  static_assert(NS == 4 && CPW <= 4, "copy schedule");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];  // [K ring | V ring]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h32 = lane >> 5;
+
+  int bh, qt;
+  fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hk = hq / (Hq / Hkv);
+  const uint16_t* qp = q + (size_t)bh * N * D;
+  const uint16_t* kp = k + (size_t)(b * Hkv + hk) * N * D;
+  const uint16_t* vp = v + (size_t)(b * Hkv + hk) * N * D;
+  const int q0 = qt * S::BM;
+  const int qw0 = q0 + wave * (RB * 32);  // rows qw0 + 32 rb + l32
+
+  // Q^T operands: lane holds query qw0 + 32 rb + l32, features 16c + 8*h32 .. +7.
+  bf16x8 qreg[RB][DC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qi = qw0 + 32 * rb + l32;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (qi < N) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
+      qreg[rb][c] = as_bf16x8(u);
+    }
+  }
+  f32x16 acc[RB][DB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][db][r] = 0.f;
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) { m_run[rb] = -INFINITY; l_run[rb] = 0.f; }
+  PPOffsets<D> ofs;
+  ofs.init(lane);
+
+  const int kv_end = CAUSAL ? min(N, q0 + S::BM) : N;
+  const int T = (kv_end + BN - 1) / BN;
+
+  // Copies: tile i of K (V) lives in stage i % 4 of the K (V) ring.  Wave copy j covers tile
+  // rows RPC*j .. RPC*j + RPC-1; lane l fills physical chunk l of that 1 KB block (row
+  // RPC*j + l/(D/8), chunk l%(D/8)), so it reads logical chunk (l%(D/8)) ^ swizzle(row).
+  // Rows past N read row N-1 (finite data whose probabilities are zero).
+  const int lrow = lane / (D / 8);
+  uint32_t loff[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int r = RPC * (wave * CPW + i) + lrow;
+    loff[i] = lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(r, 0) >> 4) & (D / 8 - 1)));
+  }
+  // Branch-free (it sits inside the interleaved MFMA sequence): rows are clamped per lane.
+  // Byte offsets stay below 2^31: the API bounds N*d*2 per head well under that.  The LDS
+  // destination is computed in scalar registers from a wave index made uniform once.
+  const void* kbase = wave_uniform(kp);
+  const void* vbase = wave_uniform(vp);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
+  const uint32_t wdst = lds0 + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (CPW * 1024);
+  auto copy = [&](int tile, bool is_k, int i) __attribute__((always_inline)) {
+    const int row = min(tile * BN + RPC * (wave * CPW + i) + lrow, N - 1);
+    const uint32_t m0v = wdst + (is_k ? 0 : NS * TILE) + (tile & (NS - 1)) * TILE + 1024 * i;
+    dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff[i] - lrow * (2 * D)), m0v);
+  };
+  // LDS base of 32-key block u of K (V): tile u/2, rows 32*(u%2) ..
+  auto kblk = [&](int u) __attribute__((always_inline)) {
+    return smem + ((u >> 1) & (NS - 1)) * TILE + (u & 1) * 32 * (2 * D);
+  };
+  auto vblk = [&](int u) __attribute__((always_inline)) {
+    return smem + NS * TILE + ((u >> 1) & (NS - 1)) * TILE + (u & 1) * 32 * (2 * D);
+  };
+  // Operand j of a step: j < NPV are V^T operands (sh, db), db fastest; then the K operands c.
+  auto operand = [&](const char* ks, const char* vs, auto jc) __attribute__((always_inline)) -> bf16x8 {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < NPV) {
+      constexpr int db = j % DB, sh = j / DB;
+      const char* base = vs + 16 * sh * (2 * D);
+      return join_tr(ds_read_tr16(base + ofs.v[db][0]), ds_read_tr16(base + ofs.v[db][1]));
+    } else {
+      return *reinterpret_cast<const bf16x8*>(ks + ofs.k[j - NPV]);
+    }
+  };
+  // A wave has work in step u while key block u-1 still holds keys at or before its last row.
+  auto active = [&](int u) __attribute__((always_inline)) { return !CAUSAL || (u - 1) * 32 <= qw0 + RB * 32 - 1; };
+
+  // Prologue: K_0, K_1, K_2, V_0, V_1; V stage 3 (read as block -1, with P_{-1} = 0) is zeroed.
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    copy(0, true, i);
+    if (1 < T) copy(1, true, i);
+    if (2 < T) copy(2, true, i);
+    copy(0, false, i);
+    if (1 < T) copy(1, false, i);
+  }
+  for (int i = tid; i < TILE / 16; i += NW * 64)
+    *reinterpret_cast<u32x4*>(smem + NS * TILE + (NS - 1) * TILE + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  f32x16 sA[RB], sB[RB];
+  u32x4 pA[RB][2], pB[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) pA[rb][sh] = u32x4{0u, 0u, 0u, 0u};
+  wait_vmem();  // also covers the Q loads
+  lds_barrier();
+  // S_0.
+  {
+    const char* ks = kblk(0);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ofs.k[c]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if constexpr (RB == 1) {
+          if (c == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            sA[rb] = mfma32(a, qreg[rb][0], z);
+          } else {
+            sA[rb] = mfma32(a, qreg[rb][c], sA[rb]);
+          }
+        } else if (c == 0) {
+          mfma_qk_first(sA[rb], a, qreg[rb][0]);
+        } else {
+          mfma_qk_next(sA[rb], a, qreg[rb][c]);
+        }
+      }
+    }
+  }
+
+  // Step u: sc = S_u (complete), sn <- S_{u+1}, pp = P_{u-1}, pc <- P_u; copies of the
+  // step's half of the tile's copy list (K_{t+3} on even steps, V_{t+2} on odd ones).  Tiles
+  // past the end are copied too, clamped to row N-1, into stages nobody reads any more, so
+  // every step issues the same copies and the wait counts stay fixed.
+  auto step = [&](int u, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2], u32x4(&pc)[RB][2],
+                  int ctile, bool cis_k) __attribute__((always_inline)) {
+    if (active(u)) {
+      if constexpr (RB > 1 && XATTN_ILV_QKASM != 0) qk_result_fence();  // S_u came from asm MFMAs
+      const int u0 = u * 32;
+      if ((u0 + 32 > N) || (CAUSAL && u0 + 31 > qw0)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int qi = qw0 + 32 * rb + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kj = u0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+            if (kj >= N || (CAUSAL && kj > qi)) sc[rb][r] = -INFINITY;
+          }
+        }
+      }
+      const char* ks = kblk(u + 1);
+      const char* vs = vblk(u - 1);
+      float m4[RB][2];
+      float alpha[RB];
+      float rs[RB][4];
+      bool resc = false;
+      bf16x8 buf[L];
+      static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(ks, vs, jc); });
+      sched_fence();
+      static_for<NMF>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, j = i / RB, rb = i % RB;
+        if constexpr (j < NPV) {
+          constexpr int db = j % DB, sh = j / DB;
+          acc[rb][db] = mfma32(buf[j % L], as_bf16x8(pp[rb][sh]), acc[rb][db]);
+        } else {
+          constexpr int c = j - NPV;
+          if constexpr (RB == 1) {
+            if constexpr (c == 0) {
+              f32x16 z;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) z[r] = 0.f;
+              sn[rb] = mfma32(buf[j % L], qreg[rb][0], z);
+            } else {
+              sn[rb] = mfma32(buf[j % L], qreg[rb][c], sn[rb]);
+            }
+          } else if constexpr (c == 0) {
+            mfma_qk_first(sn[rb], buf[j % L], qreg[rb][0]);
+          } else {
+            mfma_qk_next(sn[rb], buf[j % L], qreg[rb][c]);
+          }
+        }
+        if constexpr (rb == RB - 1 && j + L < NOPS) buf[j % L] = operand(ks, vs, std::integral_constant<int, j + L>{});
+        // Vector work: row maxima (slots 0 .. 2RB-1), then the exponentials, spread evenly
+        // over slots 2RB+1 .. NMF-2.
+        if constexpr (i < RB) {
+          // Two chains of v_max3 over the lane's 16 scores of row block i.
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+            float m = fmaxf(sc[i][8 * ch], sc[i][8 * ch + 1]);
+#pragma unroll
+            for (int e = 2; e < 8; e += 2) m = fmaxf(fmaxf(m, sc[i][8 * ch + e]), sc[i][8 * ch + e + 1]);
+            m4[i][ch] = m;
+          }
+        } else if constexpr (i < 2 * RB) {
+          constexpr int vrb = i - RB;
+          float mx = fmaxf(m4[vrb][0], m4[vrb][1]);
+          mx = max_xor32(mx) * scale_log2;
+          // Lazy reference max ([OPT] §3.2.1 with a deferred rescale): it moves only when a
+          // row's block max exceeds it by more than 2^kLazy; finite, as key 0 is never masked.
+          const bool up = __builtin_amdgcn_ballot_w64(mx > m_run[vrb] + kLazy) != 0;
+          const float m_new = up ? fmaxf(m_run[vrb], mx) : m_run[vrb];
+          alpha[vrb] = fast_exp2(m_run[vrb] - m_new);
+          m_run[vrb] = m_new;
+          l_run[vrb] *= alpha[vrb];
+          resc = resc || up;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rs[vrb][e] = 0.f;
+        }
+        constexpr int E0 = 2 * RB + 1, NE = RB * 4, ESPAN = NMF - 2 - E0;
+        static_for<NE>([&](auto ec) {
+          constexpr int e = decltype(ec)::value;
+          if constexpr (E0 + e * ESPAN / NE == i) {
+          constexpr int erb = e / 4, jq = e % 4;
+          float p[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            p[w] = fast_exp2(fmaf(sc[erb][4 * jq + w], scale_log2, -m_run[erb]));
+            rs[erb][w] += p[w];
+          }
+          uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
+          // Keeps this step's vector work in its slot (the compiler would otherwise sink it).
+          asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs[erb][0]), "+v"(rs[erb][1]), "+v"(rs[erb][2]), "+v"(rs[erb][3]));
+          pc[erb][jq / 2][2 * (jq % 2)] = w0;
+          pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
+          if constexpr (jq == 3) l_run[erb] += (rs[erb][0] + rs[erb][1]) + (rs[erb][2] + rs[erb][3]);
+          }
+        });
+        if constexpr (i % 8 == 6 && i / 8 < CPW) copy(ctile, cis_k, i / 8);
+        sched_fence();
+      });
+      if (resc) {  // rare: a real branch (the fence keeps it from being flattened into selects)
+        sched_fence();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
+        sched_fence();
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) copy(ctile, cis_k, i);
+    }
+  };
+
+  for (int t = 0; t < T; ++t) {
+    step(2 * t, sA, sB, pA, pB, t + 3, true);
+    step(2 * t + 1, sB, sA, pB, pA, t + 2, false);
+    // K_{t+2} and V_{t+1} (copied in tile t-1) must have landed; this tile's copies may stay
+    // in flight.
+    wait_vmem_n<2 * CPW>();
+    lds_barrier();
+  }
+  wait_vmem();
+
+  // P_{2T-1} V_{2T-1}.
+  if (active(2 * T)) {
+    const char* vs = vblk(2 * T - 1);
+    static_for<NPV>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, db = j % DB, sh = j / DB;
+      const bf16x8 a = operand(vs, vs, jc);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb][db] = mfma32(a, as_bf16x8(pA[rb][sh]), acc[rb][db]);
+    });
+  }
+
+  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
+  uint16_t* op = o + (size_t)bh * N * D;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float lt = sum_xor32(l_run[rb]);
+    const float inv = 1.f / lt;
+    const int qi = qw0 + 32 * rb + l32;
+    if (qi < N) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = db * 32 + 8 * jj + 4 * h32;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[rb][db][4 * jj + 0] * inv, acc[rb][db][4 * jj + 1] * inv);
+          w[1] = pack_bf16x2(acc[rb][db][4 * jj + 2] * inv, acc[rb][db][4 * jj + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
+        }
+      if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run[rb] + fast_log2(lt)) * kLn2;
+    }
+  }
+}
+
 // fp32 inputs (d = 64): the same tiled online softmax with v_mfma_f32_32x32x2_f32, one
 // wave per 32 queries and 32-key tiles, single-buffered.  Keeps full fp32 precision.
 template <bool CAUSAL>
@@ -727,6 +1094,25 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 
 // ------------------------------------------------------------------------- host launchers
 template <int D>
+static hipError_t launch_fwd_ilv_t(const FwdArgs& a) {
+  constexpr int RB = XATTN_ILV_RB;
+  constexpr int BM = IlvShape<D, RB>::BM;
+  const int n_qtiles = (a.N + BM - 1) / BM;
+  const int BH = a.B * a.Hq;
+  const dim3 grid(n_qtiles * BH), block(IlvShape<D, RB>::NW * 64);
+  const float sl2 = a.scale * kLog2e;
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_ilv_kernel<D, RB, true>), grid, block, 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
+                       n_qtiles, BH);
+  else
+    hipLaunchKernelGGL((fwd_ilv_kernel<D, RB, false>), grid, block, 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
+                       n_qtiles, BH);
+  return hipGetLastError();
+}
+
+template <int D>
 static hipError_t launch_fwd_pp_t(const FwdArgs& a) {
   constexpr int BM = 256;
   const int n_qtiles = (a.N + BM - 1) / BM;
@@ -777,6 +1163,9 @@ hipError_t launch_fwd(const FwdArgs& a) {
                          a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
     return hipGetLastError();
   }
+#if XATTN_FWD_ILV
+  if (a.d == 128) return launch_fwd_ilv_t<128>(a);
+#endif
 #if XATTN_FWD_PP
   if (a.d == 128) return launch_fwd_pp_t<128>(a);
 #endif
