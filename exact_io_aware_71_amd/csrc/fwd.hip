@@ -674,6 +674,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #ifndef XATTN_ILV_RB
 #define XATTN_ILV_RB 1
 #endif
+// 1: the running max is checked through the row sums of the new probabilities instead of a
+// per-step row max (see the step below).
+#ifndef XATTN_ILV_SUMCHECK
+#define XATTN_ILV_SUMCHECK 1
+#endif
+// Largest lane-partial row sum of one 32-key step accepted without moving the reference max
+// (so every probability stays below it).
+constexpr float kSumMax = 256.f;
+
 __device__ __forceinline__ void mfma_qk_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
 #if XATTN_ILV_QKASM == 1
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "a"(b));
@@ -876,7 +885,9 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
       const char* vs = vblk(u - 1);
       float m4[RB][2];
       float alpha[RB];
-      float rs[RB][4];
+      float rs[RB][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) { rs[rb][0] = 0.f; rs[rb][1] = 0.f; alpha[rb] = 1.f; }
       bool resc = false;
       bf16x8 buf[L];
       static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(ks, vs, jc); });
@@ -904,9 +915,10 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
           }
         }
         if constexpr (rb == RB - 1 && j + L < NOPS) buf[j % L] = operand(ks, vs, std::integral_constant<int, j + L>{});
-        // Vector work: row maxima (slots 0 .. 2RB-1), then the exponentials, spread evenly
-        // over slots 2RB+1 .. NMF-2.
-        if constexpr (i < RB) {
+        // Vector work.  With the sum check: only the exponentials, spread evenly over slots
+        // 1 .. NMF-2.  Otherwise: row maxima (slots 0 .. 2RB-1), then the exponentials over
+        // slots 2RB+1 .. NMF-2.
+        if constexpr (!XATTN_ILV_SUMCHECK && i < RB) {
           // Two chains of v_max3 over the lane's 16 scores of row block i.
 #pragma unroll
           for (int ch = 0; ch < 2; ++ch) {
@@ -915,7 +927,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
             for (int e = 2; e < 8; e += 2) m = fmaxf(fmaxf(m, sc[i][8 * ch + e]), sc[i][8 * ch + e + 1]);
             m4[i][ch] = m;
           }
-        } else if constexpr (i < 2 * RB) {
+        } else if constexpr (!XATTN_ILV_SUMCHECK && i < 2 * RB) {
           constexpr int vrb = i - RB;
           float mx = fmaxf(m4[vrb][0], m4[vrb][1]);
           mx = max_xor32(mx) * scale_log2;
@@ -927,31 +939,76 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
           m_run[vrb] = m_new;
           l_run[vrb] *= alpha[vrb];
           resc = resc || up;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rs[vrb][e] = 0.f;
         }
-        constexpr int E0 = 2 * RB + 1, NE = RB * 4, ESPAN = NMF - 2 - E0;
+        constexpr int E0 = XATTN_ILV_SUMCHECK ? 1 : 2 * RB + 1, NE = RB * 4, ESPAN = NMF - 2 - E0;
         static_for<NE>([&](auto ec) {
           constexpr int e = decltype(ec)::value;
           if constexpr (E0 + e * ESPAN / NE == i) {
-          constexpr int erb = e / 4, jq = e % 4;
-          float p[4];
+            constexpr int erb = e / 4, jq = e % 4;
+            float p[4];
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            p[w] = fast_exp2(fmaf(sc[erb][4 * jq + w], scale_log2, -m_run[erb]));
-            rs[erb][w] += p[w];
-          }
-          uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
-          // Keeps this step's vector work in its slot (the compiler would otherwise sink it).
-          asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs[erb][0]), "+v"(rs[erb][1]), "+v"(rs[erb][2]), "+v"(rs[erb][3]));
-          pc[erb][jq / 2][2 * (jq % 2)] = w0;
-          pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
-          if constexpr (jq == 3) l_run[erb] += (rs[erb][0] + rs[erb][1]) + (rs[erb][2] + rs[erb][3]);
+            for (int w = 0; w < 4; ++w) p[w] = fast_exp2(fmaf(sc[erb][4 * jq + w], scale_log2, -m_run[erb]));
+            uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
+            // fp32 row sums (summing the bf16-rounded values would cost the LSE up to 2^-9).
+            rs[erb][0] += p[0] + p[2];
+            rs[erb][1] += p[1] + p[3];
+            // Keeps this step's vector work in its slot (the compiler would otherwise sink it).
+            asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs[erb][0]), "+v"(rs[erb][1]));
+            pc[erb][jq / 2][2 * (jq % 2)] = w0;
+            pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
           }
         });
         if constexpr (i % 8 == 6 && i / 8 < CPW) copy(ctile, cis_k, i / 8);
         sched_fence();
       });
+#if XATTN_ILV_SUMCHECK
+      // Reference max check ([OPT] §3.2.1, lazily): the step's probabilities were formed
+      // against the current reference m.  If every lane-partial row sum stays at or below
+      // kSumMax (so does every probability; NaN, from the first step's m = -inf, fails the
+      // test) they are kept.  Otherwise the wave redoes the step with m moved to the true
+      // running max (finite: key 0 is never masked) and rescales O and l by 2^(m_old - m_new);
+      // the P V products already issued this step used the old m, as O did.
+      {
+        bool bad = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) bad = bad || !(rs[rb][0] + rs[rb][1] <= kSumMax);
+        resc = __builtin_amdgcn_ballot_w64(bad) != 0;
+      }
+      if (resc) {
+        sched_fence();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float mx = sc[rb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[rb][r]);
+          mx = max_xor32(mx) * scale_log2;
+          const float m_new = fmaxf(m_run[rb], mx);
+          alpha[rb] = fast_exp2(m_run[rb] - m_new);
+          m_run[rb] = m_new;
+          l_run[rb] *= alpha[rb];
+          rs[rb][0] = 0.f;
+          rs[rb][1] = 0.f;
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            float pv[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pv[w] = fast_exp2(fmaf(sc[rb][4 * jq + w], scale_log2, -m_new));
+            const uint32_t w0 = pack_bf16x2(pv[0], pv[1]), w1 = pack_bf16x2(pv[2], pv[3]);
+            rs[rb][0] += pv[0] + pv[2];
+            rs[rb][1] += pv[1] + pv[3];
+            pc[rb][jq / 2][2 * (jq % 2)] = w0;
+            pc[rb][jq / 2][2 * (jq % 2) + 1] = w1;
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
+        sched_fence();
+      }
+#else
       if (resc) {  // rare: a real branch (the fence keeps it from being flattened into selects)
         sched_fence();
 #pragma unroll
@@ -962,6 +1019,10 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
             for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
         sched_fence();
       }
+#endif
+      // One branch only: a second one on the same condition costs the allocator ~40 registers.
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
     } else {
 #pragma unroll
       for (int i = 0; i < CPW; ++i) copy(ctile, cis_k, i);

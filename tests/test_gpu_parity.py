@@ -124,6 +124,33 @@ def test_fwd_closed_forms(gpu_lib):
     np.testing.assert_array_equal(o[:, :, 0], oracle.upcast(inp["v"])[:, :, 0])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("trend", ["rising", "falling", "spike"])
+def test_fwd_moving_running_max(gpu_lib, causal, trend):
+    """Inputs whose row maxima keep moving, so the kernels' lazily updated reference max has to
+    move many times (and by large amounts, for the spike) mid-row."""
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    B, H, N, d = 1, 2, 700, 128
+    inp = make_prefill(B, H, H, N, d, "bf16", seed=41)
+    k = bf16_bits_to_f32(inp["k"]).reshape(B, H, N, d)
+    ramp = np.linspace(0.2, 4.0, N, dtype=np.float32)
+    if trend == "falling":
+        ramp = ramp[::-1].copy()
+    elif trend == "spike":
+        ramp = np.full(N, 0.3, np.float32)
+        ramp[[37, 300, 301, 650]] = [6.0, 12.0, 20.0, 30.0]
+    k = k * ramp[None, None, :, None]
+    if trend == "spike":
+        # Spiked keys point along the mean query, so most rows see logit jumps of tens (log2).
+        q = bf16_bits_to_f32(inp["q"]).reshape(B, H, N, d)
+        k[:, :, ramp > 5] = np.sign(q.mean(axis=2, keepdims=True)) * ramp[ramp > 5][None, None, :, None] * 0.5
+    run = {"q": inp["q"], "k": f32_to_bf16_bits(k), "v": inp["v"]}
+    scale = default_scale(d)
+    o, lse = run_fwd(gpu_lib, run, causal, scale)
+    o_ref, lse_ref = oracle.forward(run["q"], run["k"], run["v"], scale, causal)
+    assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), f"{trend} causal={causal}")
+
+
 def test_fwd_bitwise_deterministic(gpu_lib):
     import torch
     inp = make_prefill(1, 4, 4, 1000, 128, "bf16", seed=3)
