@@ -31,6 +31,9 @@
 #ifndef XATTN_DKDV_NS
 #define XATTN_DKDV_NS 2
 #endif
+#ifndef XATTN_DKDV_LAG
+#define XATTN_DKDV_LAG 1
+#endif
 
 namespace xattn {
 
@@ -287,6 +290,200 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// dK, dV with a lagged dK wave.  As bwd_dkdv_kernel, waves g and g + 4 share a SIMD and the
+// same 32 keys, the first accumulating dV, the second dK, and P crosses from the first to the
+// second through LDS (here as bf16, the precision the dS product rounds to anyway).  The dK
+// wave works one query tile behind: in iteration t the dV wave forms S, P and P^T dO for
+// tile t while the dK wave forms dP, dS and dS^T Q for tile t-1 from the P written in
+// iteration t-1.  One barrier per tile instead of two, and each SIMD always holds one wave
+// in each kind of phase.  LDS: a three-stage ring of [Q | dO | LSE2 | D] tiles (t-1, t and
+// the copy of t+1) and two P buffers.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_lag_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int N, int Npad, float scale, float scale_log2, int BH) {
+  constexpr int NW = 8, NG = 4, BK = NG * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32, NQB = BQ / 32;
+  using T = BwdTile<D>;
+  constexpr int STAGE = (2 * T::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // Q, dO, LSE2, D
+  constexpr int NS = 3;
+  constexpr int PGRP = NQB * 2 * 1024;  // one group's P of a tile: [qb][sh][lane] x 16 B
+  constexpr int PBYTES = NG * PGRP;
+  constexpr int RPC = 1024 / (2 * D), CPTT = T::BYTES / 1024, CPW = 2 * CPTT / NW;
+  static_assert(CPTT % NW == 0 || (2 * CPTT) % NW == 0, "tile pieces split over the waves");
+  static_assert(NW % (16 / RPC) == 0, "pieces of a wave share their swizzle");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + 2 * PBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  const int grp = wave & (NG - 1), role = wave / NG;
+  const int bh = blockIdx.x % BH;
+  // Causal: early key blocks see the most queries and are dispatched first.
+  const int k0 = (blockIdx.x / BH) * BK;
+  const int kw0 = k0 + grp * 32;
+  const uint16_t* qp = q + (size_t)bh * N * D;
+  const uint16_t* kp = k + (size_t)bh * N * D;
+  const uint16_t* vp = v + (size_t)bh * N * D;
+  const uint16_t* dop = dout + (size_t)bh * N * D;
+  // stats = [LSE2 | D], each [BH, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
+  const uint32_t lse_off = (uint32_t)((size_t)bh * Npad * 4);
+  const uint32_t dl_off = (uint32_t)(((size_t)BH + bh) * Npad * 4);
+  const int qt_begin = CAUSAL ? (k0 / BQ) : 0;
+  const int qt_end = (N + BQ - 1) / BQ;
+
+  // Tile copies, as in bwd_dkdv_kernel: wave w copies 1 KB pieces w, w + NW, ... of [Q | dO];
+  // rows past N read row N-1 (their LSE2 is +inf); waves 0 and 1 copy the 64 LSE2 and D values.
+  const int lrow = lane / (D / 8);
+  const uint32_t loff0 =
+      lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(RPC * wave + lrow, 0) >> 4) & (D / 8 - 1)));
+  auto copy_tile = [&](int t) __attribute__((always_inline)) {
+    char* dst = smem + (t % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int j = wave + NW * i;
+      const bool is_q = j < CPTT;
+      const int jt = is_q ? j : j - CPTT;
+      const int row0 = t * BQ + RPC * jt;
+      const uint16_t* base = is_q ? qp : dop;
+      char* d = dst + (is_q ? 0 : T::BYTES) + 1024 * jt;
+      if (row0 + RPC <= N) {
+        dma16(base, (uint32_t)row0 * (2 * D) + loff0, d);
+      } else {
+        const int row = min(row0 + lrow, N - 1);
+        dma16(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), d);
+      }
+    }
+    if (wave < 2) dma4(stats, (wave == 0 ? lse_off : dl_off) + 4 * (t * BQ + lane), dst + 2 * T::BYTES + wave * BQ * 4);
+  };
+
+  copy_tile(qt_begin);
+  // K^T (dV wave) or V^T (dK wave), the B operand of S = Q K^T or dP = dO V^T: lane owns key
+  // kw0 + l32.
+  const int kj = kw0 + l32;
+  const uint16_t* kvp = role == 0 ? kp : vp;
+  bf16x8 kreg[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (kj < N) a = ld_global16(kvp + (size_t)kj * D + 16 * c + 8 * h32);
+    kreg[c] = as_bf16x8(a);
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  wait_vmem();
+  lds_barrier();
+
+  char* pbase = smem + NS * STAGE + grp * PGRP;
+  for (int t = qt_begin; t <= qt_end; ++t) {
+    if (t + 1 < qt_end) copy_tile(t + 1);
+    if (role == 0) {
+      if (t < qt_end) {
+        // dV wave, tile t: S = Q K^T, P = 2^(S scale log2 e - LSE2) (masked), P to LDS,
+        // dV += P^T dO.
+        const char* qs = smem + (t % NS) * STAGE;
+        const char* dos = qs + T::BYTES;
+        const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
+        char* pw = pbase + (t & 1) * PBYTES;
+        const int q0 = t * BQ;
+        f32x16 sv[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[qb][r] = 0.f;
+#pragma unroll
+          for (int c = 0; c < DC; ++c)
+            sv[qb] = mfma32(*reinterpret_cast<const bf16x8*>(qs + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], sv[qb]);
+        }
+        bf16x8 pa[NQB][2];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          // Lane owns key kj; register r holds query q0 + 32 qb + 8(r/4) + 4*h32 + r%4.
+          // Queries before the key (causal) get P = 0.
+          const int qb0 = q0 + qb * 32;
+          const bool need_mask = CAUSAL && (qb0 < kw0 + 31);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * r4 + 4 * h32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * r4 + i;
+              float pv = fast_exp2(fmaf(sv[qb][r], scale_log2, -l4[i]));
+              if (need_mask && kj > qb0 + 8 * r4 + 4 * h32 + i) pv = 0.f;
+              sv[qb][r] = pv;
+            }
+          }
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh) {
+            pa[qb][sh] = pack8(sv[qb], sh);
+            *reinterpret_cast<bf16x8*>(pw + (qb * 2 + sh) * 1024 + 16 * lane) = pa[qb][sh];
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+              acc[db] = mfma32(pa[qb][sh], ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+      }
+    } else if (t > qt_begin) {
+      // dK wave, tile t-1: dP = dO V^T, dS = P (dP - D) with P from LDS, dK += dS^T Q.
+      const int tt = t - 1;
+      const char* qs = smem + (tt % NS) * STAGE;
+      const char* dos = qs + T::BYTES;
+      const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
+      const char* pr = pbase + (tt & 1) * PBYTES;
+      f32x16 dp[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+          dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dos + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], dp[qb]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const u32x4 pw = *reinterpret_cast<const u32x4*>(pr + (qb * 2 + sh) * 1024 + 16 * lane);
+#pragma unroll
+          for (int r4 = 0; r4 < 2; ++r4) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * (2 * sh + r4) + 4 * h32);
+            const int r = 8 * sh + 4 * r4;
+            dp[qb][r + 0] = bf16_lo(pw[2 * r4]) * (dp[qb][r + 0] - d4[0]);
+            dp[qb][r + 1] = bf16_hi(pw[2 * r4]) * (dp[qb][r + 1] - d4[1]);
+            dp[qb][r + 2] = bf16_lo(pw[2 * r4 + 1]) * (dp[qb][r + 2] - d4[2]);
+            dp[qb][r + 3] = bf16_hi(pw[2 * r4 + 1]) * (dp[qb][r + 3] - d4[3]);
+          }
+        }
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const bf16x8 dsa = pack8(dp[qb], sh);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mfma32(dsa, ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+        }
+      }
+    }
+    if (t + 1 < qt_end) wait_vmem();  // tile t+1 has landed
+    lds_barrier();
+  }
+
+  // C layout: lane holds feature db*32 + l32 of keys kw0 + 8(r/4) + 4*h32 + r%4.
+  uint16_t* outp = (role == 0 ? dv : dk) + (size_t)bh * N * D;
+  const float oscale = role == 0 ? 1.f : scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      if (kr < N) outp[(size_t)kr * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(acc[db][r] * oscale, 0.f) & 0xffffu);
+    }
+}
+
 // ------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
@@ -433,6 +630,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_kt = (a.N + 127) / 128;
+  if (XATTN_DKDV_LAG)
+    hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(512), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
+                       (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Npad, a.scale, sl2, BH);
+  else
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
                      (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Npad, a.scale, sl2, BH);

@@ -662,6 +662,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #ifndef XATTN_ILV_LOOKAHEAD
 #define XATTN_ILV_LOOKAHEAD 4
 #endif
+#ifndef XATTN_ILV_COPY_SLOT
+#define XATTN_ILV_COPY_SLOT 6
+#endif
+#ifndef XATTN_ILV_PRIO
+#define XATTN_ILV_PRIO 0
+#endif
 
 // S^T = K Q^T block products for the interleaved kernel, written to vector registers (the
 // softmax reads them there), while O^T accumulates in accumulation registers.  Issued from inline
@@ -891,6 +897,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
       bool resc = false;
       bf16x8 buf[L];
       static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(ks, vs, jc); });
+      if (XATTN_ILV_PRIO) __builtin_amdgcn_s_setprio(1);
       sched_fence();
       static_for<NMF>([&](auto ic) {
         constexpr int i = decltype(ic)::value, j = i / RB, rb = i % RB;
@@ -958,9 +965,10 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
             pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
           }
         });
-        if constexpr (i % 8 == 6 && i / 8 < CPW) copy(ctile, cis_k, i / 8);
+        if constexpr (i % 8 == XATTN_ILV_COPY_SLOT && i / 8 < CPW) copy(ctile, cis_k, i / 8);
         sched_fence();
       });
+      if (XATTN_ILV_PRIO) __builtin_amdgcn_s_setprio(0);
 #if XATTN_ILV_SUMCHECK
       // Reference max check ([OPT] §3.2.1, lazily): the step's probabilities were formed
       // against the current reference m.  If every lane-partial row sum stays at or below
