@@ -34,6 +34,15 @@
 #ifndef XATTN_DKDV_LAG
 #define XATTN_DKDV_LAG 1
 #endif
+#ifndef XATTN_DKDV_ILV
+#define XATTN_DKDV_ILV 1
+#endif
+#ifndef XATTN_DKDV_LOOKAHEAD
+#define XATTN_DKDV_LOOKAHEAD 4
+#endif
+#ifndef XATTN_DKDV_SPREAD
+#define XATTN_DKDV_SPREAD 1
+#endif
 
 namespace xattn {
 
@@ -355,6 +364,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (wave < 2) dma4(stats, (wave == 0 ? lse_off : dl_off) + 4 * (t * BQ + lane), dst + 2 * T::BYTES + wave * BQ * 4);
   };
 
+  // Branch-free single pieces, for issue between the MFMAs of the interleaved tiles: piece i
+  // of this wave (rows clamped per lane), and the statistics (even waves copy LSE2, odd waves
+  // D; the copies of one kind write the same bytes).
+  const void* qbase = wave_uniform(qp);
+  const void* dobase = wave_uniform(dop);
+  const void* sbase = wave_uniform(stats);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto copy_piece = [&](int t, int i) __attribute__((always_inline)) {
+    const int j = wv + NW * i;
+    const bool is_q = j < CPTT;
+    const int jt = is_q ? j : j - CPTT;
+    const int row = min(t * BQ + RPC * jt + lrow, N - 1);
+    const uint32_t m0v = lds0 + (t % NS) * STAGE + (is_q ? 0 : T::BYTES) + 1024 * jt;
+    dma16_m0(is_q ? qbase : dobase, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
+  };
+  auto copy_stats = [&](int t) __attribute__((always_inline)) {
+    const uint32_t m0v = lds0 + (t % NS) * STAGE + 2 * T::BYTES + (wv & 1) * BQ * 4;
+    dma4_m0(sbase, ((wv & 1) ? dl_off : lse_off) + 4 * min(t * BQ + lane, Npad - 1), m0v);
+  };
+
   copy_tile(qt_begin);
   // K^T (dV wave) or V^T (dK wave), the B operand of S = Q K^T or dP = dO V^T: lane owns key
   // kw0 + l32.
@@ -376,97 +406,238 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lds_barrier();
 
   char* pbase = smem + NS * STAGE + grp * PGRP;
+  auto dv_tile_plain = [&](int t) __attribute__((always_inline)) {
+    // dV wave, tile t: S = Q K^T, P = 2^(S scale log2 e - LSE2) (masked), P to LDS,
+    // dV += P^T dO.
+    const char* qs = smem + (t % NS) * STAGE;
+    const char* dos = qs + T::BYTES;
+    const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
+    char* pw = pbase + (t & 1) * PBYTES;
+    const int q0 = t * BQ;
+    f32x16 sv[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[qb][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+        sv[qb] = mfma32(*reinterpret_cast<const bf16x8*>(qs + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], sv[qb]);
+    }
+    bf16x8 pa[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      // Lane owns key kj; register r holds query q0 + 32 qb + 8(r/4) + 4*h32 + r%4.
+      // Queries before the key (causal) get P = 0.
+      const int qb0 = q0 + qb * 32;
+      const bool need_mask = CAUSAL && (qb0 < kw0 + 31);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * r4 + 4 * h32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * r4 + i;
+          float pv = fast_exp2(fmaf(sv[qb][r], scale_log2, -l4[i]));
+          if (need_mask && kj > qb0 + 8 * r4 + 4 * h32 + i) pv = 0.f;
+          sv[qb][r] = pv;
+        }
+      }
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        pa[qb][sh] = pack8(sv[qb], sh);
+        *reinterpret_cast<bf16x8*>(pw + (qb * 2 + sh) * 1024 + 16 * lane) = pa[qb][sh];
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(pa[qb][sh], ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+  };
+  auto dk_tile_plain = [&](int tt) __attribute__((always_inline)) {
+    // dK wave, tile t-1: dP = dO V^T, dS = P (dP - D) with P from LDS, dK += dS^T Q.
+    const char* qs = smem + (tt % NS) * STAGE;
+    const char* dos = qs + T::BYTES;
+    const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
+    const char* pr = pbase + (tt & 1) * PBYTES;
+    f32x16 dp[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+        dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dos + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], dp[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const u32x4 pw = *reinterpret_cast<const u32x4*>(pr + (qb * 2 + sh) * 1024 + 16 * lane);
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * (2 * sh + r4) + 4 * h32);
+          const int r = 8 * sh + 4 * r4;
+          dp[qb][r + 0] = bf16_lo(pw[2 * r4]) * (dp[qb][r + 0] - d4[0]);
+          dp[qb][r + 1] = bf16_hi(pw[2 * r4]) * (dp[qb][r + 1] - d4[1]);
+          dp[qb][r + 2] = bf16_lo(pw[2 * r4 + 1]) * (dp[qb][r + 2] - d4[2]);
+          dp[qb][r + 3] = bf16_hi(pw[2 * r4 + 1]) * (dp[qb][r + 3] - d4[3]);
+        }
+      }
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const bf16x8 dsa = pack8(dp[qb], sh);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(dsa, ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+      }
+    }
+  };
+  // Interleaved versions (no mask needed): 32 MFMA slots per tile.  dV wave: S of block 0,
+  // then S of block 1 while the vector ALU forms P of block 0, then dV of block 0 while it
+  // forms P of block 1, then dV of block 1.  The dK wave does the same with dP, dS and dK.
+  // MFMA operands read from LDS run XATTN_DKDV_LOOKAHEAD slots ahead.
+  constexpr int LA = XATTN_DKDV_LOOKAHEAD;
+  constexpr bool kIlv = XATTN_DKDV_ILV && D == 128;  // the slot plan assumes 8 chunks, 4 blocks
+  auto dv_tile_ilv = [&](int t, int ct) __attribute__((always_inline)) {
+    const char* qs = smem + (t % NS) * STAGE;
+    const char* dos = qs + T::BYTES;
+    const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
+    char* pw = pbase + (t & 1) * PBYTES;
+    // Operand j: j < 16: Q rows of block j/8, chunk j%8 (A of S); else dO^T of block
+    // (j-16)/8, half ((j-16)/4)%2, features ((j-16)%4)*32 (B of dV).
+    auto opnd = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 16) {
+        return *reinterpret_cast<const bf16x8*>(qs + swz<D>((j / 8) * 32 + l32, 2 * (j % 8) + h32));
+      } else {
+        constexpr int jj = j - 16, qb = jj / 8, sh = (jj / 4) % 2, db = jj % 4;
+        return ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane);
+      }
+    };
+    f32x16 sv[NQB];
+    bf16x8 pa[NQB][2];
+    bf16x8 buf[LA];
+    static_for<LA>([&](auto jc) { buf[decltype(jc)::value] = opnd(jc); });
+    sched_fence();
+    static_for<32>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < 16) {
+        constexpr int qb = i / 8, c = i % 8;
+        if constexpr (c == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          sv[qb] = mfma32(buf[i % LA], kreg[0], z);
+        } else {
+          sv[qb] = mfma32(buf[i % LA], kreg[c], sv[qb]);
+        }
+      } else {
+        constexpr int jj = i - 16, qb = jj / 8, sh = (jj / 4) % 2, db = jj % 4;
+        acc[db] = mfma32(pa[qb][sh], buf[i % LA], acc[db]);
+      }
+      if constexpr (i + LA < 32) buf[i % LA] = opnd(std::integral_constant<int, i + LA>{});
+      // P of block (i-8)/8 over slots 8..23, two r4 groups every other slot.
+      if constexpr (i >= 8 && i < 24 && i % 2 == 0) {
+        constexpr int qb = (i - 8) / 8, r4 = ((i - 8) % 8) / 2;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * r4 + 4 * h32);
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = fast_exp2(fmaf(sv[qb][4 * r4 + e], scale_log2, -l4[e]));
+        u32x2 w;
+        w[0] = pack_bf16x2(pv[0], pv[1]);
+        w[1] = pack_bf16x2(pv[2], pv[3]);
+        asm volatile("" : "+v"(w));  // keeps this slot's vector work in place
+        u32x4 u = __builtin_bit_cast(u32x4, pa[qb][r4 / 2]);
+        u[2 * (r4 % 2)] = w[0];
+        u[2 * (r4 % 2) + 1] = w[1];
+        pa[qb][r4 / 2] = as_bf16x8(u);
+        if constexpr (r4 % 2 == 1) *reinterpret_cast<bf16x8*>(pw + (qb * 2 + r4 / 2) * 1024 + 16 * lane) = pa[qb][r4 / 2];
+      }
+      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(ct, i / 3);
+      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(ct);
+      sched_fence();
+    });
+  };
+  auto dk_tile_ilv = [&](int tt, int ct) __attribute__((always_inline)) {
+    const char* qs = smem + (tt % NS) * STAGE;
+    const char* dos = qs + T::BYTES;
+    const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
+    const char* pr = pbase + (tt & 1) * PBYTES;
+    auto opnd = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 16) {
+        return *reinterpret_cast<const bf16x8*>(dos + swz<D>((j / 8) * 32 + l32, 2 * (j % 8) + h32));
+      } else {
+        constexpr int jj = j - 16, qb = jj / 8, sh = (jj / 4) % 2, db = jj % 4;
+        return ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane);
+      }
+    };
+    f32x16 dp[NQB];
+    bf16x8 dsa[NQB][2];
+    bf16x8 buf[LA];
+    static_for<LA>([&](auto jc) { buf[decltype(jc)::value] = opnd(jc); });
+    sched_fence();
+    static_for<32>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < 16) {
+        constexpr int qb = i / 8, c = i % 8;
+        if constexpr (c == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          dp[qb] = mfma32(buf[i % LA], kreg[0], z);
+        } else {
+          dp[qb] = mfma32(buf[i % LA], kreg[c], dp[qb]);
+        }
+      } else {
+        constexpr int jj = i - 16, qb = jj / 8, sh = (jj / 4) % 2, db = jj % 4;
+        acc[db] = mfma32(dsa[qb][sh], buf[i % LA], acc[db]);
+      }
+      if constexpr (i + LA < 32) buf[i % LA] = opnd(std::integral_constant<int, i + LA>{});
+      // dS of block (i-8)/8 over slots 8..23: half sh every fourth slot.
+      if constexpr (i >= 8 && i < 24 && i % 4 == 0) {
+        constexpr int qb = (i - 8) / 8, sh = ((i - 8) % 8) / 4;
+        const u32x4 pw = *reinterpret_cast<const u32x4*>(pr + (qb * 2 + sh) * 1024 + 16 * lane);
+        u32x4 u;
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * (2 * sh + r4) + 4 * h32);
+          const int r = 8 * sh + 4 * r4;
+          const float e0 = bf16_lo(pw[2 * r4]) * (dp[qb][r + 0] - d4[0]);
+          const float e1 = bf16_hi(pw[2 * r4]) * (dp[qb][r + 1] - d4[1]);
+          const float e2 = bf16_lo(pw[2 * r4 + 1]) * (dp[qb][r + 2] - d4[2]);
+          const float e3 = bf16_hi(pw[2 * r4 + 1]) * (dp[qb][r + 3] - d4[3]);
+          u[2 * r4] = pack_bf16x2(e0, e1);
+          u[2 * r4 + 1] = pack_bf16x2(e2, e3);
+        }
+        asm volatile("" : "+v"(u));  // keeps this slot's vector work in place
+        dsa[qb][sh] = as_bf16x8(u);
+      }
+      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(ct, i / 3);
+      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(ct);
+      sched_fence();
+    });
+  };
+
+  // Tile t+1 is copied during iteration t: up front, or, with XATTN_DKDV_SPREAD, one piece
+  // every third MFMA of the first half of an interleaved tile.  A tile past the end is then
+  // copied too, its rows and statistics clamped to the last ones, into the stage nobody reads
+  // in this iteration.
   for (int t = qt_begin; t <= qt_end; ++t) {
-    if (t + 1 < qt_end) copy_tile(t + 1);
+    const int ct = t + 1;
+    const bool ilv_dv = kIlv && role == 0 && t < qt_end && !(CAUSAL && t * BQ < kw0 + 31);
+    const bool ilv_dk = kIlv && role == 1 && t > qt_begin;
+    if (!(XATTN_DKDV_SPREAD && (ilv_dv || ilv_dk)) && t + 1 < qt_end) copy_tile(t + 1);
     if (role == 0) {
       if (t < qt_end) {
-        // dV wave, tile t: S = Q K^T, P = 2^(S scale log2 e - LSE2) (masked), P to LDS,
-        // dV += P^T dO.
-        const char* qs = smem + (t % NS) * STAGE;
-        const char* dos = qs + T::BYTES;
-        const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
-        char* pw = pbase + (t & 1) * PBYTES;
-        const int q0 = t * BQ;
-        f32x16 sv[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sv[qb][r] = 0.f;
-#pragma unroll
-          for (int c = 0; c < DC; ++c)
-            sv[qb] = mfma32(*reinterpret_cast<const bf16x8*>(qs + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], sv[qb]);
-        }
-        bf16x8 pa[NQB][2];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          // Lane owns key kj; register r holds query q0 + 32 qb + 8(r/4) + 4*h32 + r%4.
-          // Queries before the key (causal) get P = 0.
-          const int qb0 = q0 + qb * 32;
-          const bool need_mask = CAUSAL && (qb0 < kw0 + 31);
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * r4 + 4 * h32);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * r4 + i;
-              float pv = fast_exp2(fmaf(sv[qb][r], scale_log2, -l4[i]));
-              if (need_mask && kj > qb0 + 8 * r4 + 4 * h32 + i) pv = 0.f;
-              sv[qb][r] = pv;
-            }
-          }
-#pragma unroll
-          for (int sh = 0; sh < 2; ++sh) {
-            pa[qb][sh] = pack8(sv[qb], sh);
-            *reinterpret_cast<bf16x8*>(pw + (qb * 2 + sh) * 1024 + 16 * lane) = pa[qb][sh];
-          }
-        }
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-              acc[db] = mfma32(pa[qb][sh], ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+        if (ilv_dv) dv_tile_ilv(t, ct);
+        else dv_tile_plain(t);
       }
     } else if (t > qt_begin) {
-      // dK wave, tile t-1: dP = dO V^T, dS = P (dP - D) with P from LDS, dK += dS^T Q.
-      const int tt = t - 1;
-      const char* qs = smem + (tt % NS) * STAGE;
-      const char* dos = qs + T::BYTES;
-      const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
-      const char* pr = pbase + (tt & 1) * PBYTES;
-      f32x16 dp[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < DC; ++c)
-          dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dos + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], dp[qb]);
-      }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const u32x4 pw = *reinterpret_cast<const u32x4*>(pr + (qb * 2 + sh) * 1024 + 16 * lane);
-#pragma unroll
-          for (int r4 = 0; r4 < 2; ++r4) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * (2 * sh + r4) + 4 * h32);
-            const int r = 8 * sh + 4 * r4;
-            dp[qb][r + 0] = bf16_lo(pw[2 * r4]) * (dp[qb][r + 0] - d4[0]);
-            dp[qb][r + 1] = bf16_hi(pw[2 * r4]) * (dp[qb][r + 1] - d4[1]);
-            dp[qb][r + 2] = bf16_lo(pw[2 * r4 + 1]) * (dp[qb][r + 2] - d4[2]);
-            dp[qb][r + 3] = bf16_hi(pw[2 * r4 + 1]) * (dp[qb][r + 3] - d4[3]);
-          }
-        }
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const bf16x8 dsa = pack8(dp[qb], sh);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            acc[db] = mfma32(dsa, ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
-        }
-      }
+      if (ilv_dk) dk_tile_ilv(t - 1, ct);
+      else dk_tile_plain(t - 1);
     }
     if (t + 1 < qt_end) wait_vmem();  // tile t+1 has landed
     lds_barrier();

@@ -165,6 +165,11 @@ __device__ __forceinline__ void dma16_m0(const void* base, uint32_t voff, uint32
                : "memory");
 }
 
+// As dma16_m0 with 4 bytes per lane.
+__device__ __forceinline__ void dma4_m0(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr) : "memory");
+}
+
 // As dma16 with 4 bytes per lane (global_load_lds_dword): lane i's word lands at lds + 4 * i.
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, const void* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(
