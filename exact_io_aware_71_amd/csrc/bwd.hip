@@ -728,15 +728,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // Branch-free single pieces of tile t (rows clamped per lane), issued between the MFMAs of
+  // the first key block so that the workgroups' copies do not all queue at the tile start.
+  const void* kbase = wave_uniform(kp);
+  const void* vbase = wave_uniform(vp);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto copy_piece = [&](int t, int i) __attribute__((always_inline)) {
+    const int j = wv + NW * i;
+    const bool is_k = j < CPTT;
+    const int jt = is_k ? j : j - CPTT;
+    const int row = min(t * BN + RPC * jt + lrow, N - 1);
+    const uint32_t m0v = lds0 + (t & 1) * STAGE + (is_k ? 0 : T::BYTES) + 1024 * jt;
+    dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
+  };
+
   copy_tile(0, 0);
   wait_vmem();  // also covers the Q/dO loads
   lds_barrier();
+  // Tile t+1 is copied during tile t (past the end: rows clamped, into the idle stage).
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) copy_tile(t + 1, (t + 1) & 1);
     const int t0 = t * BN;
     const char* ks = smem + (t & 1) * STAGE;
     const char* vs = ks + T::BYTES;
-    if (!CAUSAL || t0 <= qw0 + 31) {
+    if (CAUSAL && t0 > qw0 + 31) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) copy_piece(t + 1, i);
+    } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         f32x16 s, dp;
@@ -749,6 +767,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + off);
           s = mfma32(ak, qreg[c], s);
           dp = mfma32(av, doreg[c], dp);
+          if (kb == 0 && c < CPW) copy_piece(t + 1, c);
         }
         // Lane owns query qi; register r holds key t0 + kb*32 + 8(r/4) + 4*h32 + r%4.
         const int kb0 = t0 + kb * 32;
