@@ -135,6 +135,38 @@ __device__ __forceinline__ bf16x8 ld_tr_operand(const char* tile, int row0, int 
   return join_tr(ds_read_tr16(tile + swz_elem<D>(row, col)), ds_read_tr16(tile + swz_elem<D>(row + 8, col)));
 }
 
+// Lane-dependent LDS byte offsets of the MFMA operands inside a swizzled 64 x D tile: k[c] for
+// row-major operands (row lane%32, chunk 2c + lane/32: K or V rows as the A operand of a
+// 32x32x16 product), v[db][e] for the transposed reads of columns db*32 .. (rows rl, rl + 8
+// of ld_tr_operand's pattern).  The swizzle depends on the row modulo 16 only, so for row
+// blocks starting at multiples of 16 the block's row offset is a constant added to these.
+template <int D>
+struct TileOffsets {
+  uint32_t k[D / 16];
+  uint32_t v[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, h32 = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) k[c] = swz<D>(l32, 2 * c + h32);
+    const int G = lane >> 4, j = lane & 15;
+    const int rl = 4 * (G >> 1) + (j >> 2), cl = 16 * (G & 1) + 4 * (j & 3);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v[db][e] = swz_elem<D>(rl + 8 * e, db * 32 + cl);
+  }
+  // Switch between two LDS stages (stage size a power of two larger than every offset).
+  __device__ __forceinline__ void toggle(uint32_t stage_bytes) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) k[c] ^= stage_bytes;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      v[db][0] ^= stage_bytes;
+      v[db][1] ^= stage_bytes;
+    }
+  }
+};
+
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -322,35 +322,8 @@ struct PPShape {
 
 // One M phase: NPV MFMAs of O^T += V^T P^T (if PV) then NQK MFMAs of S^T = K Q^T (if QK), each
 // operand read from LDS LOOKAHEAD MFMAs ahead of its use, in a fixed issue order.
-// Lane-dependent LDS byte offsets of the M-phase operands inside a swizzled 64 x D tile.  The
-// swizzle depends on the row modulo 16 only, so for row blocks starting at multiples of 16
-// the block's row offset is a compile-time constant added to these.
 template <int D>
-struct PPOffsets {
-  uint32_t k[PPShape<D>::DC];      // K operand (A of S^T = K Q^T): row l32, chunk 2c + h32
-  uint32_t v[PPShape<D>::DB][2];   // V^T operand (transposing reads): rows rl and rl + 8
-  __device__ __forceinline__ void init(int lane) {
-    const int l32 = lane & 31, h32 = lane >> 5;
-#pragma unroll
-    for (int c = 0; c < PPShape<D>::DC; ++c) k[c] = swz<D>(l32, 2 * c + h32);
-    const int G = lane >> 4, j = lane & 15;
-    const int rl = 4 * (G >> 1) + (j >> 2), cl = 16 * (G & 1) + 4 * (j & 3);
-#pragma unroll
-    for (int db = 0; db < PPShape<D>::DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) v[db][e] = swz_elem<D>(rl + 8 * e, db * 32 + cl);
-  }
-  // Switch between the two LDS stages (stage size a power of two larger than every offset).
-  __device__ __forceinline__ void toggle(uint32_t stage_bytes) {
-#pragma unroll
-    for (int c = 0; c < PPShape<D>::DC; ++c) k[c] ^= stage_bytes;
-#pragma unroll
-    for (int db = 0; db < PPShape<D>::DB; ++db) {
-      v[db][0] ^= stage_bytes;
-      v[db][1] ^= stage_bytes;
-    }
-  }
-};
+using PPOffsets = TileOffsets<D>;
 
 // hook(k), k = 0 .. NHOOK-1, is called at evenly spaced points between the MFMAs.
 template <int D, bool PV, bool QK, int NHOOK, typename Hook>
