@@ -145,7 +145,6 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   if (dtype != ATTN_BF16) return fail(dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG,
                                       "backward supports bf16 only");
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
-  if (Hq != Hkv) return fail(ATTN_ERR_UNSUPPORTED, "grouped-query backward (Hq=%d, Hkv=%d) is not implemented", Hq, Hkv);
   const size_t need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);

@@ -311,7 +311,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_lag_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int Npad, float scale, float scale_log2, int BH) {
+    uint16_t* __restrict__ dv, int N, int Npad, float scale, float scale_log2, int BHkv, int Hq, int Hkv, int BHq) {
   constexpr int NW = 8, NG = 4, BK = NG * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32, NQB = BQ / 32;
   using T = BwdTile<D>;
   constexpr int STAGE = (2 * T::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // Q, dO, LSE2, D
@@ -325,34 +325,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
   const int grp = wave & (NG - 1), role = wave / NG;
-  const int bh = blockIdx.x % BH;
+  // One workgroup per (batch, KV head, 128 keys).  With grouped-query heads the g query heads
+  // sharing the KV head are visited one after the other ([OPT] §5.3 mapping kv = h / g), so
+  // dK and dV accumulate the whole group's gradient without atomics.
+  const int bkv = blockIdx.x % BHkv;
   // Causal: early key blocks see the most queries and are dispatched first.
-  const int k0 = (blockIdx.x / BH) * BK;
+  const int k0 = (blockIdx.x / BHkv) * BK;
   const int kw0 = k0 + grp * 32;
-  const uint16_t* qp = q + (size_t)bh * N * D;
-  const uint16_t* kp = k + (size_t)bh * N * D;
-  const uint16_t* vp = v + (size_t)bh * N * D;
-  const uint16_t* dop = dout + (size_t)bh * N * D;
-  // stats = [LSE2 | D], each [BH, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
-  const uint32_t lse_off = (uint32_t)((size_t)bh * Npad * 4);
-  const uint32_t dl_off = (uint32_t)(((size_t)BH + bh) * Npad * 4);
+  const int g = Hq / Hkv;
+  const int hq0 = (bkv / Hkv) * Hq + (bkv % Hkv) * g;  // first query head (b*Hq + h) of the group
+  const uint16_t* qp = q + (size_t)hq0 * N * D;         // head i of the group: + i*N*D
+  const uint16_t* kp = k + (size_t)bkv * N * D;
+  const uint16_t* vp = v + (size_t)bkv * N * D;
+  const uint16_t* dop = dout + (size_t)hq0 * N * D;
+  // stats = [LSE2 | D], each [B*Hq, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
+  auto lse_off = [&](int h) __attribute__((always_inline)) { return (uint32_t)((size_t)(hq0 + h) * Npad * 4); };
+  auto dl_off = [&](int h) __attribute__((always_inline)) { return (uint32_t)(((size_t)BHq + hq0 + h) * Npad * 4); };
   const int qt_begin = CAUSAL ? (k0 / BQ) : 0;
   const int qt_end = (N + BQ - 1) / BQ;
+  // Virtual tiles vt = 0 .. g*nt - 1: query head vt / nt of the group, tile qt_begin + vt % nt.
+  // The LDS ring slot and the P slot follow vt.
+  const int nt = qt_end - qt_begin, nvt = g * nt;
 
   // Tile copies, as in bwd_dkdv_kernel: wave w copies 1 KB pieces w, w + NW, ... of [Q | dO];
   // rows past N read row N-1 (their LSE2 is +inf); waves 0 and 1 copy the 64 LSE2 and D values.
   const int lrow = lane / (D / 8);
   const uint32_t loff0 =
       lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(RPC * wave + lrow, 0) >> 4) & (D / 8 - 1)));
-  auto copy_tile = [&](int t) __attribute__((always_inline)) {
-    char* dst = smem + (t % NS) * STAGE;
+  auto copy_tile = [&](int vt, int h, int t) __attribute__((always_inline)) {
+    char* dst = smem + (vt % NS) * STAGE;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int j = wave + NW * i;
       const bool is_q = j < CPTT;
       const int jt = is_q ? j : j - CPTT;
       const int row0 = t * BQ + RPC * jt;
-      const uint16_t* base = is_q ? qp : dop;
+      const uint16_t* base = (is_q ? qp : dop) + (size_t)h * N * D;
       char* d = dst + (is_q ? 0 : T::BYTES) + 1024 * jt;
       if (row0 + RPC <= N) {
         dma16(base, (uint32_t)row0 * (2 * D) + loff0, d);
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dma16(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), d);
       }
     }
-    if (wave < 2) dma4(stats, (wave == 0 ? lse_off : dl_off) + 4 * (t * BQ + lane), dst + 2 * T::BYTES + wave * BQ * 4);
+    if (wave < 2) dma4(stats, (wave == 0 ? lse_off(h) : dl_off(h)) + 4 * (t * BQ + lane), dst + 2 * T::BYTES + wave * BQ * 4);
   };
 
   // Branch-free single pieces, for issue between the MFMAs of the interleaved tiles: piece i
@@ -372,20 +380,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const void* sbase = wave_uniform(stats);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto copy_piece = [&](int t, int i) __attribute__((always_inline)) {
+  auto copy_piece = [&](int vt, int h, int t, int i) __attribute__((always_inline)) {
     const int j = wv + NW * i;
     const bool is_q = j < CPTT;
     const int jt = is_q ? j : j - CPTT;
     const int row = min(t * BQ + RPC * jt + lrow, N - 1);
-    const uint32_t m0v = lds0 + (t % NS) * STAGE + (is_q ? 0 : T::BYTES) + 1024 * jt;
-    dma16_m0(is_q ? qbase : dobase, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
+    const uint32_t m0v = lds0 + (vt % NS) * STAGE + (is_q ? 0 : T::BYTES) + 1024 * jt;
+    const char* base = reinterpret_cast<const char*>(is_q ? qbase : dobase) + (size_t)h * N * D * 2;
+    dma16_m0(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
   };
-  auto copy_stats = [&](int t) __attribute__((always_inline)) {
-    const uint32_t m0v = lds0 + (t % NS) * STAGE + 2 * T::BYTES + (wv & 1) * BQ * 4;
-    dma4_m0(sbase, ((wv & 1) ? dl_off : lse_off) + 4 * min(t * BQ + lane, Npad - 1), m0v);
+  auto copy_stats = [&](int vt, int h, int t) __attribute__((always_inline)) {
+    const uint32_t m0v = lds0 + (vt % NS) * STAGE + 2 * T::BYTES + (wv & 1) * BQ * 4;
+    dma4_m0(sbase, ((wv & 1) ? dl_off(h) : lse_off(h)) + 4 * min(t * BQ + lane, Npad - 1), m0v);
   };
 
-  copy_tile(qt_begin);
+  copy_tile(0, 0, qt_begin);
   // K^T (dV wave) or V^T (dK wave), the B operand of S = Q K^T or dP = dO V^T: lane owns key
   // kw0 + l32.
   const int kj = kw0 + l32;
@@ -406,13 +415,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lds_barrier();
 
   char* pbase = smem + NS * STAGE + grp * PGRP;
-  auto dv_tile_plain = [&](int t) __attribute__((always_inline)) {
-    // dV wave, tile t: S = Q K^T, P = 2^(S scale log2 e - LSE2) (masked), P to LDS,
-    // dV += P^T dO.
-    const char* qs = smem + (t % NS) * STAGE;
+  auto dv_tile_plain = [&](int vt, int t) __attribute__((always_inline)) {
+    // dV wave, virtual tile vt (query tile t): S = Q K^T, P = 2^(S scale log2 e - LSE2)
+    // (masked), P to LDS, dV += P^T dO.
+    const char* qs = smem + (vt % NS) * STAGE;
     const char* dos = qs + T::BYTES;
     const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
-    char* pw = pbase + (t & 1) * PBYTES;
+    char* pw = pbase + (vt & 1) * PBYTES;
     const int q0 = t * BQ;
     f32x16 sv[NQB];
 #pragma unroll
@@ -500,11 +509,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // MFMA operands read from LDS run XATTN_DKDV_LOOKAHEAD slots ahead.
   constexpr int LA = XATTN_DKDV_LOOKAHEAD;
   constexpr bool kIlv = XATTN_DKDV_ILV && D == 128;  // the slot plan assumes 8 chunks, 4 blocks
-  auto dv_tile_ilv = [&](int t, int ct) __attribute__((always_inline)) {
-    const char* qs = smem + (t % NS) * STAGE;
+  auto dv_tile_ilv = [&](int vt, int cvt, int ch, int ct) __attribute__((always_inline)) {
+    const char* qs = smem + (vt % NS) * STAGE;
     const char* dos = qs + T::BYTES;
     const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
-    char* pw = pbase + (t & 1) * PBYTES;
+    char* pw = pbase + (vt & 1) * PBYTES;
     // Operand j: j < 16: Q rows of block j/8, chunk j%8 (A of S); else dO^T of block
     // (j-16)/8, half ((j-16)/4)%2, features ((j-16)%4)*32 (B of dV).
     auto opnd = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
@@ -555,12 +564,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         pa[qb][r4 / 2] = as_bf16x8(u);
         if constexpr (r4 % 2 == 1) *reinterpret_cast<bf16x8*>(pw + (qb * 2 + r4 / 2) * 1024 + 16 * lane) = pa[qb][r4 / 2];
       }
-      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(ct, i / 3);
-      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(ct);
+      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(cvt, ch, ct, i / 3);
+      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
       sched_fence();
     });
   };
-  auto dk_tile_ilv = [&](int tt, int ct) __attribute__((always_inline)) {
+  auto dk_tile_ilv = [&](int tt, int cvt, int ch, int ct) __attribute__((always_inline)) {
     const char* qs = smem + (tt % NS) * STAGE;
     const char* dos = qs + T::BYTES;
     const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
@@ -615,36 +624,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         asm volatile("" : "+v"(u));  // keeps this slot's vector work in place
         dsa[qb][sh] = as_bf16x8(u);
       }
-      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(ct, i / 3);
-      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(ct);
+      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(cvt, ch, ct, i / 3);
+      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
       sched_fence();
     });
   };
 
-  // Tile t+1 is copied during iteration t: up front, or, with XATTN_DKDV_SPREAD, one piece
-  // every third MFMA of the first half of an interleaved tile.  A tile past the end is then
-  // copied too, its rows and statistics clamped to the last ones, into the stage nobody reads
-  // in this iteration.
-  for (int t = qt_begin; t <= qt_end; ++t) {
-    const int ct = t + 1;
-    const bool ilv_dv = kIlv && role == 0 && t < qt_end && !(CAUSAL && t * BQ < kw0 + 31);
-    const bool ilv_dk = kIlv && role == 1 && t > qt_begin;
-    if (!(XATTN_DKDV_SPREAD && (ilv_dv || ilv_dk)) && t + 1 < qt_end) copy_tile(t + 1);
+  // Virtual tile vt+1 is copied during iteration vt: up front, or, with XATTN_DKDV_SPREAD, one
+  // piece every third MFMA of the first half of an interleaved tile.  Past the end the last
+  // head's tile qt_end is copied, its rows and statistics clamped to the last ones, into the
+  // stage nobody reads in this iteration.
+  int h_cur = 0, t_cur = qt_begin;                                   // of vt
+  int h_nxt = nt == 1 ? 1 : 0, t_nxt = nt == 1 ? qt_begin : qt_begin + 1;  // of vt + 1
+  for (int vt = 0; vt <= nvt; ++vt) {
+    const bool more = vt + 1 < nvt;
+    const int ch = more ? h_nxt : g - 1, ct = more ? t_nxt : qt_end;
+    const bool ilv_dv = kIlv && role == 0 && vt < nvt && !(CAUSAL && t_cur * BQ < kw0 + 31);
+    const bool ilv_dk = kIlv && role == 1 && vt > 0;
+    if (!(XATTN_DKDV_SPREAD && (ilv_dv || ilv_dk)) && more) copy_tile(vt + 1, h_nxt, t_nxt);
     if (role == 0) {
-      if (t < qt_end) {
-        if (ilv_dv) dv_tile_ilv(t, ct);
-        else dv_tile_plain(t);
+      if (vt < nvt) {
+        if (ilv_dv) dv_tile_ilv(vt, vt + 1, ch, ct);
+        else dv_tile_plain(vt, t_cur);
       }
-    } else if (t > qt_begin) {
-      if (ilv_dk) dk_tile_ilv(t - 1, ct);
-      else dk_tile_plain(t - 1);
+    } else if (vt > 0) {
+      if (ilv_dk) dk_tile_ilv(vt - 1, vt + 1, ch, ct);
+      else dk_tile_plain(vt - 1);
     }
-    if (t + 1 < qt_end) wait_vmem();  // tile t+1 has landed
+    if (more) wait_vmem();  // virtual tile vt+1 has landed
     lds_barrier();
+    h_cur = h_nxt;
+    t_cur = t_nxt;
+    if (++t_nxt == qt_end) {
+      t_nxt = qt_begin;
+      ++h_nxt;
+    }
   }
 
   // C layout: lane holds feature db*32 + l32 of keys kw0 + 8(r/4) + 4*h32 + r%4.
-  uint16_t* outp = (role == 0 ? dv : dk) + (size_t)bh * N * D;
+  uint16_t* outp = (role == 0 ? dv : dk) + (size_t)bkv * N * D;
   const float oscale = role == 0 ? 1.f : scale;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -660,7 +678,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, int N,
-    int Npad, float scale, float scale_log2, int n_qtiles, int BH) {
+    int Npad, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv) {
   constexpr int NW = 4, BM = NW * 32, BN = kBwdBK, KB = BN / 32, DC = D / 16, DB = D / 32;
   using T = BwdTile<D>;
   constexpr int STAGE = 2 * T::BYTES;  // K, V
@@ -671,9 +689,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t_ = blockIdx.x / BH;
   const int qt = CAUSAL ? (n_qtiles - 1 - t_) : t_;
   const int q0 = qt * BM, qw0 = q0 + wave * 32, qi = qw0 + l32;
+  // K/V of the query head's KV head (grouped-query: kv = h / (Hq/Hkv)).
+  const int bkv = (bh / Hq) * Hkv + (bh % Hq) / (Hq / Hkv);
   const uint16_t* qp = q + (size_t)bh * N * D;
-  const uint16_t* kp = k + (size_t)bh * N * D;
-  const uint16_t* vp = v + (size_t)bh * N * D;
+  const uint16_t* kp = k + (size_t)bkv * N * D;
+  const uint16_t* vp = v + (size_t)bkv * N * D;
   const uint16_t* dop = dout + (size_t)bh * N * D;
 
   bf16x8 qreg[DC], doreg[DC];
@@ -820,10 +840,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_kt = (a.N + 127) / 128;
-  if (XATTN_DKDV_LAG)
-    hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(512), 0, a.stream,
+  const int BHkv = a.B * a.Hkv;
+  if (XATTN_DKDV_LAG || a.Hq != a.Hkv)
+    hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL>), dim3(n_kt * BHkv), dim3(512), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
-                       (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Npad, a.scale, sl2, BH);
+                       (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Npad, a.scale, sl2, BHkv,
+                       a.Hq, a.Hkv, BH);
   else
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
@@ -833,7 +855,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int n_qt = (a.N + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
-                     (const uint16_t*)a.dout, (uint16_t*)a.dq, a.N, a.Npad, a.scale, sl2, n_qt, BH);
+                     (const uint16_t*)a.dout, (uint16_t*)a.dq, a.N, a.Npad, a.scale, sl2, n_qt, BH, a.Hq, a.Hkv);
   return hipGetLastError();
 }
 

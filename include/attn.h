@@ -88,8 +88,9 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d] outputs (overwritten, same dtype as q)
  *   workspace                        >= attn_bwd_workspace_bytes(...) device bytes, 256-byte
  *                                    aligned; contents on entry are ignored
- * Supported: BF16, d in {64, 128}, Hq == Hkv (grouped-query backward returns
- * ATTN_ERR_UNSUPPORTED).  Deterministic (no atomics).
+ * Supported: BF16, d in {64, 128}.  Grouped-query heads ([OPT] §5.3, kv = h / (Hq/Hkv)): dk and
+ * dv of a KV head are the sums of the gradients of the Hq/Hkv query heads sharing it.
+ * Deterministic (no atomics).
  */
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,

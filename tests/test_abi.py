@@ -67,7 +67,7 @@ def test_bwd_validation():
     assert need == 1024                      # LSE2 and D rows, padded to 64 queries
     assert lib.attn_bwd_workspace_bytes(1, 2, 2, 65, 128) == 2 * 2 * 128 * 4
     assert bwd(dq=None) == 1
-    assert bwd(Hq=4, Hkv=2) == 2           # grouped-query backward not implemented
+    assert bwd(Hq=3, Hkv=2) == 1           # Hq must be a multiple of Hkv
     assert bwd(dt=0) == 2
     assert bwd(d=80) == 2
     assert bwd(ws=None) == 3

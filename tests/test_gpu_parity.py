@@ -254,6 +254,18 @@ def test_bwd_ragged(gpu_lib, N, d, causal):
     check_bwd(grads, inp, scale, causal, tag=f"N={N} d={d}")
 
 
+@pytest.mark.parametrize("heads", [(8, 2), (4, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_grouped_query(gpu_lib, heads, d, causal):
+    """Grouped-query backward: dK/dV of a KV head sum the gradients of its query heads."""
+    Hq, Hkv = heads
+    inp = make_prefill(2, Hq, Hkv, 333, d, "bf16", seed=Hq * 10 + Hkv + d, with_dout=True)
+    scale = default_scale(d)
+    grads = run_fwd_bwd(gpu_lib, inp, causal, scale)
+    check_bwd(grads, inp, scale, causal, tag=f"gqa {Hq}/{Hkv} d={d}")
+
+
 def test_bwd_from_oracle_forward(gpu_lib):
     """Feed the oracle's O (as bf16) and LSE into attn_bwd: isolates the backward kernels."""
     import torch
