@@ -165,6 +165,9 @@ def main():
     ws_d = torch.empty(attn.attn_decode_workspace_bytes(DB, DHq, DHkv, DL, d, 0), dtype=torch.uint8, device=dev)
     dec_o = torch.empty_like(dq_)
     dec_lse = torch.empty((DB, DHq), dtype=torch.float32, device=dev)
+    # Per-sequence cache lengths for the variable-length decode line: uniform in [L/2, L].
+    vlens = np.random.default_rng(1006).integers(DL // 2, DL + 1, DB).astype(np.int32)
+    vlens_dev = torch.from_numpy(vlens).to(dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -197,6 +200,19 @@ def main():
     t_step = [e[0].elapsed_time(e[3]) for e in evs]
     ms_fwd, ms_bwd, ms_dec = (float(np.mean(x)) for x in (t_fwd, t_bwd, t_dec))
     ms_step = float(np.mean(t_step))
+
+    # Variable-length decode, outside the timed step: same cache, lengths vlens.
+    for _ in range(3):
+        attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
+    vev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = 10
+    vev[0].record(stream)
+    for _ in range(reps):
+        attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
+    vev[1].record(stream)
+    torch.cuda.synchronize()
+    ms_vdec = vev[0].elapsed_time(vev[1]) / reps
+    vdec_bytes = int(vlens.sum()) * DHkv * d * 2 * 2 + 2 * DB * DHq * d * 2 + DB * DHq * 4
 
     f_fwd = flops_fwd(B, H, N, d, True)
     f_bwd = 2.5 * f_fwd
@@ -245,6 +261,8 @@ def main():
                                "B=64 Hq=32 Hkv=8 L=8192 d=128", "parallelism": "none (one GPU)"},
         "fwd_TFLOPs": f_fwd / (ms_fwd * 1e-3) / 1e12, "bwd_TFLOPs": f_bwd / (ms_bwd * 1e-3) / 1e12,
         "decode_GBps": dec_gbs,
+        "decode_varlen": {"GBps": vdec_bytes / (ms_vdec * 1e-3) / 1e9, "ms": ms_vdec,
+                          "lengths": "uniform in [L/2, L], seed 1006, mean %.0f" % float(vlens.mean())},
         "ms": {"fwd": ms_fwd, "bwd": ms_bwd, "decode": ms_dec, "fwd_min": min(t_fwd), "bwd_min": min(t_bwd),
                "decode_min": min(t_dec), "wall_per_step": wall / args.steps * 1e3},
         "roofline": roofline, "roofline_bwd": roofline_bwd, "roofline_decode": roofline_decode,

@@ -21,7 +21,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 EXPORTS = (
     "attn_abi_version", "attn_status_str", "attn_last_error", "attn_fwd",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_auto_splits",
-    "attn_decode_workspace_bytes", "attn_decode",
+    "attn_decode_workspace_bytes", "attn_decode", "attn_decode_varlen",
 )
 
 _lib = None
@@ -61,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_decode_varlen.restype = i
+    lib.attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -168,4 +170,29 @@ def attn_decode(q, k_cache, v_cache, scale: float, num_splits: int = 0, o=None, 
     _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d,
                            _dtype_code(q), float(scale), int(num_splits), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, lse
+
+
+def attn_decode_varlen(q, k_cache, v_cache, seqlens, scale: float, num_splits: int = 0, o=None, lse=None,
+                       want_lse=True, workspace=None, stream=None):
+    """attn_decode where sequence b attends to its first seqlens[b] cached keys (int32 [B], on
+    the device)."""
+    import torch
+    lib = load()
+    _require(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4, "q [B,Hq,d], caches [B,Hkv,L,d]")
+    for t in (q, k_cache, v_cache, seqlens):
+        _require(t.is_cuda and t.is_contiguous(), "inputs must be contiguous CUDA tensors")
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _require(tuple(k_cache.shape) == (B, Hkv, L, d) == tuple(v_cache.shape), "cache shape mismatch")
+    _require(tuple(seqlens.shape) == (B,) and seqlens.dtype == torch.int32, "seqlens must be int32 [B]")
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, L, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq,
+                                  Hkv, L, d, _dtype_code(q), float(scale), int(num_splits), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, lse

@@ -169,9 +169,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int num
   return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
 }
 
-attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B,
-                          int Hq, int Hkv, int L, int d, attn_dtype_t dtype, float scale, int num_splits,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+static attn_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                                 void* o, float* lse, int B, int Hq, int Hkv, int L, int d, attn_dtype_t dtype,
+                                 float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-null");
   RETURN_IF(check_heads(B, Hq, Hkv, L, d));
   RETURN_IF(check_scale(scale));
@@ -192,8 +192,25 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
   float* part_o = (float*)workspace;
   float* part_lse = (float*)((char*)workspace + align_up(rows * d * sizeof(float), 256));
   xattn::DecodeArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, L, d, scale, splits, kps, part_o, part_lse,
-                      (hipStream_t)stream};
+                      (hipStream_t)stream, seqlens};
   return from_hip(xattn::launch_decode(a), "attn_decode launch");
+}
+
+attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B,
+                          int Hq, int Hkv, int L, int d, attn_dtype_t dtype, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, nullptr, o, lse, B, Hq, Hkv, L, d, dtype, scale, num_splits, workspace,
+                     workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                                 void* o, float* lse, int B, int Hq, int Hkv, int L, int d, attn_dtype_t dtype,
+                                 float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!seqlens) return fail(ATTN_ERR_INVALID_ARG, "seqlens must be non-null");
+  if (!aligned16(seqlens)) return fail(ATTN_ERR_INVALID_ARG, "seqlens must be 16-byte aligned");
+  return decode_impl(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, L, d, dtype, scale, num_splits, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

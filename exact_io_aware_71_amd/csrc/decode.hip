@@ -38,7 +38,7 @@ template <int D, int GP>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq, int Hkv, int L,
-    int splits, int keys_per_split, float scale_log2) {
+    int splits, int keys_per_split, float scale_log2, const int* __restrict__ seqlens) {
   constexpr int EPL = D / 16;  // features per lane in the P V product
   constexpr int DC = D / 32;   // 32-wide feature chunks of the score MFMA
   __shared__ float s_m[kDecWaves][GP];
@@ -51,8 +51,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
   const int split = blockIdx.x % splits;
   const int bk = blockIdx.x / splits;  // b * Hkv + kv head
   const int b = bk / Hkv, kvh = bk - b * Hkv;
+  // Sequence b attends to the first len keys of its cache (all L without seqlens).
+  const int len = seqlens != nullptr ? min(max(seqlens[b], 0), L) : L;
   const int kbeg = split * keys_per_split;
-  const int kend = min(L, kbeg + keys_per_split);
+  const int kend = max(kbeg, min(len, kbeg + keys_per_split));
   const uint16_t* kp = kc + (size_t)bk * L * D;
   const uint16_t* vp = vc + (size_t)bk * L * D;
 
@@ -194,8 +196,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
       }
     }
     const size_t row = (size_t)(split * B + b) * Hq + kvh * g + h;
-    part_o[row * D + d] = num / den;
-    if (d == 0) part_lse[row] = M + fast_log2(den);
+    // A chunk past the sequence's end holds no key: partial O = 0, lse = -inf (weight 0).
+    const bool empty = M == -INFINITY;
+    part_o[row * D + d] = empty ? 0.f : num / den;
+    if (d == 0) part_lse[row] = empty ? -INFINITY : M + fast_log2(den);
   }
 }
 
@@ -208,14 +212,17 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
   for (int s = 0; s < splits; ++s) M = fmaxf(M, part_lse[(size_t)s * BHq + row]);
   float num = 0.f, den = 0.f;
   for (int s = 0; s < splits; ++s) {
-    const float w = fast_exp2(part_lse[(size_t)s * BHq + row] - M);
+    const float ls = part_lse[(size_t)s * BHq + row];
+    const float w = ls == -INFINITY ? 0.f : fast_exp2(ls - M);
     num = fmaf(w, part_o[((size_t)s * BHq + row) * D + d], num);
     den += w;
   }
-  const float val = num / den;
+  // No key at all (a zero-length sequence): O = 0 and LSE = -inf, the empty sum's log.
+  const bool empty = M == -INFINITY;
+  const float val = empty ? 0.f : num / den;
   const uint32_t packed = pack_bf16x2(val, 0.f);
   o[(size_t)row * D + d] = (uint16_t)(packed & 0xffffu);
-  if (lse != nullptr && d == 0) lse[row] = (M + fast_log2(den)) * kLn2;
+  if (lse != nullptr && d == 0) lse[row] = empty ? -INFINITY : (M + fast_log2(den)) * kLn2;
 }
 
 template <int D, int GP>
@@ -223,7 +230,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const float sl2 = a.scale * kLog2e;
   hipLaunchKernelGGL((decode_split_kernel<D, GP>), dim3(a.B * a.Hkv * a.splits), dim3(kDecWaves * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.part_o,
-                     a.part_lse, a.B, a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2);
+                     a.part_lse, a.B, a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2, a.seqlens);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, a.stream, a.part_o, a.part_lse,

@@ -33,6 +33,7 @@ struct DecodeArgs {
   float* part_o;        // [splits, B, Hq, d] fp32
   float* part_lse;      // [splits, B, Hq] fp32 (base-2 log-sum-exp of the scaled scores)
   hipStream_t stream;
+  const int* seqlens;   // [B] keys per sequence (device), clamped to [0, L]; null = L for all
 };
 
 hipError_t launch_fwd(const FwdArgs& a);

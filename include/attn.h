@@ -126,6 +126,21 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
                           float scale, int num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * attn_decode for a batch whose sequences hold different numbers of cached keys (caches of
+ * one capacity L, each sequence b filled to its own length).  Sequence b attends to keys
+ * [0, seqlens[b]) of its cache rows; everything else is as in attn_decode (same workspace
+ * size for the same L and num_splits).
+ *   seqlens [B] int32          device array, 16-byte aligned, read by the kernels; values are
+ *                              clamped to [0, L]; a sequence of length 0 gets o = 0 and
+ *                              lse = -inf (the log of an empty sum)
+ * Errors: as attn_decode, plus ATTN_ERR_INVALID_ARG for a null or misaligned seqlens.
+ */
+attn_status_t attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv,
+                                 int L, int d, attn_dtype_t dtype, float scale, int num_splits,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -149,23 +149,31 @@ def backward(q, k, v, dout, scale: float, causal: bool):
     return dq, dk, dv
 
 
-def decode(q, k_cache, v_cache, scale: float):
+def decode(q, k_cache, v_cache, scale: float, seqlens=None):
     """Single-token decode: q [B,Hq,d] against caches [B,Hkv,L,d]; no mask.
 
+    With seqlens, sequence b attends to the first seqlens[b] keys of its cache (clamped to
+    [0, L]); a sequence with no key gets O = 0 and LSE = -inf, the log of an empty sum.
     Returns O [B,Hq,d] and LSE [B,Hq] (float64).  Works one (b, KV head) at a time so
     a large bf16 cache is widened to fp64 slice by slice.
     """
     B, Hq, d = np.asarray(q).shape
-    Hkv = np.asarray(k_cache).shape[1]
+    Hkv, L = np.asarray(k_cache).shape[1], np.asarray(k_cache).shape[2]
     g = Hq // Hkv
     o = np.empty((B, Hq, np.asarray(v_cache).shape[3]))
     lse = np.empty((B, Hq))
     for b in range(B):
+        n = L if seqlens is None else min(max(int(seqlens[b]), 0), L)
         for kv in range(Hkv):
-            qg = upcast(q[b, kv * g:(kv + 1) * g])
-            kk, vv = upcast(k_cache[b, kv]), upcast(v_cache[b, kv])
-            p, lse[b, kv * g:(kv + 1) * g] = _softmax_rows(_scores(qg, kk, scale, False))
-            o[b, kv * g:(kv + 1) * g] = p @ vv
+            rows = slice(kv * g, (kv + 1) * g)
+            if n == 0:
+                o[b, rows] = 0.0
+                lse[b, rows] = -np.inf
+                continue
+            qg = upcast(q[b, rows])
+            kk, vv = upcast(k_cache[b, kv, :n]), upcast(v_cache[b, kv, :n])
+            p, lse[b, rows] = _softmax_rows(_scores(qg, kk, scale, False))
+            o[b, rows] = p @ vv
     return o, lse
 
 

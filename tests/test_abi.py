@@ -95,6 +95,13 @@ def test_decode_plan_and_validation():
     assert dec(ws_bytes=need - 4) == 3
     assert dec(scale=float("inf")) == 1
 
+    def decv(seqlens=P, d=128):
+        return lib.attn_decode_varlen(P, P, P, seqlens, P, P, 64, 32, 8, 8192, d, 1, ctypes.c_float(0.1), 0, P,
+                                      need, None)
+    assert decv(seqlens=None) == 1
+    assert decv(seqlens=P + 4) == 1  # misaligned
+    assert decv(d=32) == 2
+
 
 def test_binding_raises_typed_error():
     with pytest.raises(binding.AttnError) as ei:

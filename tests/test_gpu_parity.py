@@ -208,6 +208,26 @@ def test_decode_matches_forward_single_row(gpu_lib):
     assert_fwd_ok(fwd_errors(to_host64(o), of[:, :, 0], lse.cpu().numpy(), lf[:, :, 0]))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+def test_decode_per_sequence_lengths(gpu_lib, d, splits):
+    """attn_decode_varlen: sequence b attends to its first seqlens[b] cached keys; lengths
+    cover empty, single-key, block-boundary, ragged and full caches."""
+    import torch
+    L = 1000
+    lens = np.array([0, 1, 31, 32, 33, 500, 999, 1000], dtype=np.int32)
+    inp = make_decode(len(lens), 8, 2, L, d, seed=5 + d)
+    scale = default_scale(d)
+    sl = torch.from_numpy(lens).cuda()
+    o, lse = gpu_lib.attn_decode_varlen(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), sl, scale,
+                                        num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(inp["q"], inp["k"], inp["v"], scale, seqlens=lens)
+    o_h, lse_h = to_host64(o), lse.cpu().numpy().astype(np.float64)
+    assert np.all(o_h[0] == 0.0) and np.all(lse_h[0] == -np.inf)
+    assert_fwd_ok(fwd_errors(o_h[1:], o_ref[1:], lse_h[1:], lse_ref[1:]), f"varlen d={d} splits={splits}")
+
+
 # ----------------------------------------------------------------------------- backward
 def run_fwd_bwd(lib, inp, causal, scale):
     import torch

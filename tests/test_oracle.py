@@ -373,3 +373,28 @@ def test_planted_mistakes_are_caught(monkeypatch, slip):
         monkeypatch.setattr(oracle, "forward", bad_forward)
         with pytest.raises(AssertionError):
             test_hand_derived_2x2_fixture()
+
+
+def test_decode_per_sequence_lengths():
+    """Per-sequence cache lengths: each row equals the (independently pinned) forward over its
+    first n keys, splitting a row's keys and merging by LSE gives the same, full lengths give
+    plain decode, and a zero-length sequence gives O = 0, LSE = -inf."""
+    B, Hq, Hkv, L, d = 4, 6, 2, 40, 8
+    q, kc, vc = rnd(61, B, Hq, d), rnd(62, B, Hkv, L, d), rnd(63, B, Hkv, L, d)
+    lens = np.array([0, 1, 17, 40])
+    o, lse = oracle.decode(q, kc, vc, 0.4, seqlens=lens)
+    for b in range(1, B):
+        n = lens[b]
+        of, lf = oracle.forward(q[b:b + 1, :, None, :], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], 0.4, False)
+        np.testing.assert_allclose(o[b], of[0, :, 0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[b], lf[0, :, 0], rtol=1e-13)
+    assert np.all(o[0] == 0.0) and np.all(lse[0] == -np.inf)
+    o1, l1 = oracle.decode(q[2:3], kc[2:3], vc[2:3], 0.4, seqlens=[7])
+    o2, l2 = oracle.decode(q[2:3], kc[2:3, :, 7:], vc[2:3, :, 7:], 0.4, seqlens=[10])
+    om, lm = oracle.lse_merge([o1, o2], [l1, l2])
+    np.testing.assert_allclose(om[0], o[2], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lm[0], lse[2], rtol=1e-13)
+    of, lf = oracle.decode(q, kc, vc, 0.4)
+    ov, lv = oracle.decode(q, kc, vc, 0.4, seqlens=[L] * B)
+    np.testing.assert_array_equal(of, ov)
+    np.testing.assert_array_equal(lf, lv)
