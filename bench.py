@@ -138,7 +138,7 @@ def main():
     import numpy as np
     import torch
     from exact_io_aware_71_amd import binding as attn
-    from synth import default_scale, make_decode, make_prefill
+    from synth import default_scale, make_decode, make_prefill, make_varlen
 
     attn.load()
     dev = torch.device("cuda:0")
@@ -214,6 +214,45 @@ def main():
     ms_vdec = vev[0].elapsed_time(vev[1]) / reps
     vdec_bytes = int(vlens.sum()) * DHkv * d * 2 * 2 + 2 * DB * DHq * d * 2 + DB * DHq * 4
 
+    # Secondary forward lines, outside the timed step, FLOPs = 4 d per (query, key) pair the
+    # mask keeps.  Chunked prefill: a 1024-token chunk appended to 7168 cached tokens
+    # (Nk = 8192, causal aligned at the bottom right), B=4, Hq=32, Hkv=8, d=128.
+    def time_call(fn, reps=10):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    log("chunked prefill and packed variable-length forward")
+    CB, CHq, CHkv, CNq, CNk = 4, 32, 8, 1024, 8192
+    ch = make_prefill(CB, CHq, CHkv, CNq, d, "bf16", seed=1007, L=CNk)
+    cq, ck, cv = (to_dev(ch[x]) for x in ("q", "k", "v"))
+    del ch
+    co = torch.empty_like(cq)
+    clse = torch.empty((CB, CHq, CNq), dtype=torch.float32, device=dev)
+    ms_chunk = time_call(lambda: attn.attn_fwd_kv(cq, ck, cv, True, scale, o=co, lse=clse))
+    chunk_pairs = CNq * (CNk - CNq) + CNq * (CNq + 1) // 2
+    f_chunk = 4.0 * d * CB * CHq * chunk_pairs
+    del cq, ck, cv, co, clse
+    # Packed batch: 12 sequences, lengths uniform in [256, 4096] (seed 1008), H=16, d=128, causal.
+    vl = np.random.default_rng(1008).integers(256, 4097, 12)
+    VH = 16
+    px = make_varlen(vl, vl, VH, VH, d, "bf16", seed=1009)
+    pq, pk, pv = (to_dev(px[x]) for x in ("q", "k", "v"))
+    pcu = torch.from_numpy(px["cu_q"]).to(dev)
+    del px
+    po = torch.empty_like(pq)
+    plse = torch.empty((VH, int(vl.sum())), dtype=torch.float32, device=dev)
+    ms_varlen = time_call(lambda: attn.attn_fwd_varlen(pq, pk, pv, pcu, pcu, int(vl.max()), True, scale, o=po,
+                                                      lse=plse))
+    f_varlen = 4.0 * d * VH * float(sum(int(n) * (int(n) + 1) // 2 for n in vl))
+    del pq, pk, pv, po, plse
+
     f_fwd = flops_fwd(B, H, N, d, True)
     f_bwd = 2.5 * f_fwd
     tflops = (f_fwd + f_bwd) / ((ms_fwd + ms_bwd) * 1e-3) / 1e12
@@ -263,6 +302,11 @@ def main():
         "decode_GBps": dec_gbs,
         "decode_varlen": {"GBps": vdec_bytes / (ms_vdec * 1e-3) / 1e9, "ms": ms_vdec,
                           "lengths": "uniform in [L/2, L], seed 1006, mean %.0f" % float(vlens.mean())},
+        "fwd_chunk": {"TFLOPs": f_chunk / (ms_chunk * 1e-3) / 1e12, "ms": ms_chunk,
+                      "workload": "attn_fwd_kv B=4 Hq=32 Hkv=8 Nq=1024 Nk=8192 d=128 causal (bottom right)"},
+        "fwd_varlen": {"TFLOPs": f_varlen / (ms_varlen * 1e-3) / 1e12, "ms": ms_varlen,
+                       "workload": "attn_fwd_varlen 12 packed sequences, lengths uniform in [256, 4096] "
+                                   "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},
         "ms": {"fwd": ms_fwd, "bwd": ms_bwd, "decode": ms_dec, "fwd_min": min(t_fwd), "bwd_min": min(t_bwd),
                "decode_min": min(t_dec), "wall_per_step": wall / args.steps * 1e3},
         "roofline": roofline, "roofline_bwd": roofline_bwd, "roofline_decode": roofline_decode,

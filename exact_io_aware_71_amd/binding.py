@@ -19,7 +19,7 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ER
 ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTS = (
-    "attn_abi_version", "attn_status_str", "attn_last_error", "attn_fwd",
+    "attn_abi_version", "attn_status_str", "attn_last_error", "attn_fwd", "attn_fwd_kv", "attn_fwd_varlen",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_auto_splits",
     "attn_decode_workspace_bytes", "attn_decode", "attn_decode_varlen",
 )
@@ -51,6 +51,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_fwd.restype = i
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_kv.restype = i
+    lib.attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_varlen.restype = i
+    lib.attn_fwd_varlen.argtypes = [vp] * 7 + [i, i, i, i, i, i, i, i, i, f, vp]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd.restype = i
@@ -112,6 +116,53 @@ def attn_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, want_lse: bo
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, _dtype_code(q),
                         int(bool(causal)), float(scale), _stream(stream)))
+    return o, lse
+
+
+def attn_fwd_kv(q, k, v, causal: bool, scale: float, o=None, lse=None, want_lse: bool = True, stream=None):
+    """q [B,Hq,Nq,d] against k/v [B,Hkv,Nk,d]; causal masks are aligned at the bottom right
+    (query i sees keys j <= i + Nk - Nq)."""
+    import torch
+    lib = load()
+    _require(q.is_cuda and q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D CUDA tensors")
+    _require(all(t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _require(tuple(k.shape) == (B, Hkv, Nk, d) and tuple(v.shape) == (B, Hkv, Nk, d), "k/v shape mismatch")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, _dtype_code(q),
+                           int(bool(causal)), float(scale), _stream(stream)))
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool, scale: float, o=None,
+                    lse=None, want_lse: bool = True, stream=None):
+    """Packed variable-length forward: q [Hq,total_q,d], k/v [Hkv,total_k,d]; sequence b owns rows
+    cu_seqlens_q[b]..cu_seqlens_q[b+1]-1 of q (likewise for k/v); int32 offsets on the device."""
+    import torch
+    lib = load()
+    _require(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q [Hq,total_q,d], k/v [Hkv,total_k,d]")
+    for t in (q, k, v, cu_seqlens_q, cu_seqlens_k):
+        _require(t.is_cuda and t.is_contiguous(), "inputs must be contiguous CUDA tensors")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    _require(tuple(v.shape) == tuple(k.shape) and k.shape[2] == d, "k/v shape mismatch")
+    _require(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    _require(cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape == cu_seqlens_k.shape and cu_seqlens_q.numel() >= 2,
+             "cu_seqlens must be [B+1]")
+    B = cu_seqlens_q.numel() - 1
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                               _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d,
+                               _dtype_code(q), int(bool(causal)), float(scale), _stream(stream)))
     return o, lse
 
 

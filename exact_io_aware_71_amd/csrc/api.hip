@@ -39,14 +39,21 @@ attn_status_t check_scale(float scale) {
   return ATTN_OK;
 }
 
+// Element offsets of a head are formed in 64-bit, row indices and byte offsets within a head
+// in 32-bit: keep B*H*N in int range and a head's bytes (N*d elements of up to 4 bytes) below
+// 2^31.
+attn_status_t check_rows(int B, int Hq, int Hkv, int N, int d) {
+  if ((long long)B * Hq * N > 0x7fffffffLL || (long long)B * Hkv * N > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "B*H*N exceeds 2^31-1");
+  if ((long long)N * d > (1LL << 29)) return fail(ATTN_ERR_UNSUPPORTED, "N*d exceeds 2^29 per head");
+  return ATTN_OK;
+}
+
 attn_status_t check_heads(int B, int Hq, int Hkv, int N, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
     return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d N=%d d=%d)", B, Hq, Hkv, N, d);
   if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  // Element offsets are formed in 64-bit, row indices in 32-bit: keep B*H*N in int range.
-  if ((long long)B * Hq * N > 0x7fffffffLL || (long long)B * Hkv * N > 0x7fffffffLL)
-    return fail(ATTN_ERR_UNSUPPORTED, "B*H*N exceeds 2^31-1");
-  return ATTN_OK;
+  return check_rows(B, Hq, Hkv, N, d);
 }
 
 #define RETURN_IF(expr)                 \
@@ -102,10 +109,22 @@ const char* attn_status_str(attn_status_t s) {
 
 const char* attn_last_error(void) { return g_err; }
 
-attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                       int Hkv, int N, int d, attn_dtype_t dtype, int causal, float scale, void* stream) {
-  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
-  RETURN_IF(check_heads(B, Hq, Hkv, N, d));
+// Shared by the three forward entry points: dense (cu_q == nullptr) with Nq query and Nk key
+// rows per head, or packed variable-length with totals Nq, Nk and longest query run max_q.
+static attn_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q,
+                              const int* cu_k, int B, int Hq, int Hkv, int Nq, int Nk, int max_q, int d,
+                              attn_dtype_t dtype, int causal, float scale, void* stream) {
+  if ((Nq > 0 && (!q || !o)) || (Nk > 0 && (!k || !v)))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null (k and v may be null when there are no keys)");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d d=%d)", B, Hq, Hkv, d);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (Nq < 0 || Nk < 0 || max_q < 0 || max_q > Nq)
+    return fail(ATTN_ERR_INVALID_ARG, "bad row counts (Nq=%d Nk=%d max_q=%d)", Nq, Nk, max_q);
+  const int Bd = cu_q ? 1 : B;  // packed tensors hold the batch inside the row count
+  RETURN_IF(check_rows(Bd, Hq, Hq, Nq, d));
+  RETURN_IF(check_rows(Bd, Hkv, Hkv, Nk, d));
+  if ((long long)B * Hq * ((max_q + 31) / 32) > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
   RETURN_IF(check_scale(scale));
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
@@ -116,9 +135,33 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   } else {
     return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   }
-  xattn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, dtype == ATTN_BF16 ? 1 : 0, causal ? 1 : 0, scale,
-                   (hipStream_t)stream};
+  xattn::FwdArgs a{q, k, v, o, lse, cu_q, cu_k, B, Hq, Hkv, Nq, Nk, max_q, d, dtype == ATTN_BF16 ? 1 : 0,
+                   causal ? 1 : 0, scale, (hipStream_t)stream};
   return from_hip(xattn::launch_fwd(a), "attn_fwd launch");
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                       int Hkv, int N, int d, attn_dtype_t dtype, int causal, float scale, void* stream) {
+  if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N must be positive (got %d)", N);
+  return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, N, N, N, d, dtype, causal, scale, stream);
+}
+
+attn_status_t attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                          int Hkv, int Nq, int Nk, int d, attn_dtype_t dtype, int causal, float scale,
+                          void* stream) {
+  if (Nq <= 0 || Nk < 0) return fail(ATTN_ERR_INVALID_ARG, "need Nq > 0 and Nk >= 0 (got Nq=%d Nk=%d)", Nq, Nk);
+  return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, Nq, d, dtype, causal, scale, stream);
+}
+
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                              int total_q, int total_k, int max_seqlen_q, int d, attn_dtype_t dtype, int causal,
+                              float scale, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be non-null");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens arrays must be 4-byte aligned");
+  return fwd_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q, d,
+                  dtype, causal, scale, stream);
 }
 
 // Rows of the backward's per-row statistics are padded to whole 64-query tiles.

@@ -230,6 +230,44 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Rows of one (batch, head) slice of the forward's tensors.  Dense tensors are [B, H, N, d]
+// (cu == nullptr): slice (b, h) starts at row (b*H + h)*N and holds N rows.  Packed
+// variable-length tensors are [H, total, d], the batch folded into the sequence axis:
+// sequence b of head h starts at row h*total + cu[b] and holds cu[b+1] - cu[b] rows.  The
+// offsets are clamped into [0, total] and made non-decreasing, so a malformed offset array
+// yields wrong rows but never an access outside the tensors.
+struct SeqGeo {
+  const int* cu_q;  // [B+1] query offsets, or nullptr (dense)
+  const int* cu_k;  // [B+1] key offsets (used when cu_q is not null)
+  int nq, nk;       // dense: rows per head; packed: total rows
+};
+struct SeqRows {
+  size_t q, k;      // first row of the slice in Q/O/LSE and in K/V
+  int lq, lk;       // query and key rows of the slice
+};
+__device__ __forceinline__ SeqRows seq_rows(const SeqGeo& g, int b, int hq, int Hq, int hk, int Hkv) {
+  SeqRows r;
+  if (g.cu_q == nullptr) {
+    r.lq = g.nq;
+    r.lk = g.nk;
+    r.q = ((size_t)b * Hq + hq) * g.nq;
+    r.k = ((size_t)b * Hkv + hk) * g.nk;
+  } else {
+    const int q0 = min(max(g.cu_q[b], 0), g.nq), q1 = min(max(g.cu_q[b + 1], q0), g.nq);
+    const int k0 = min(max(g.cu_k[b], 0), g.nk), k1 = min(max(g.cu_k[b + 1], k0), g.nk);
+    r.lq = q1 - q0;
+    r.lk = k1 - k0;
+    r.q = (size_t)hq * g.nq + q0;
+    r.k = (size_t)hk * g.nk + k0;
+  }
+  return r;
+}
+
+// Initial running max of the forward kernels: the most negative finite float rather than
+// -inf, so that 2^(s - m) of a masked score (s = -inf) is 0 even for a row that has seen
+// no key yet, and a row without any key ends with l = 0 (O = 0, LSE = -inf).
+constexpr float kMaxInit = -3.402823466e38f;
+
 // Pins the instruction order: the scheduler moves nothing across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 

@@ -44,9 +44,6 @@
 #ifndef XATTN_FWD128_WPE
 #define XATTN_FWD128_WPE 2
 #endif
-#ifndef XATTN_FWD_PP
-#define XATTN_FWD_PP 1
-#endif
 #ifndef XATTN_FWD64_NQ
 #define XATTN_FWD64_NQ 1
 #endif
@@ -80,7 +77,7 @@ __device__ __forceinline__ void fwd_tile_of(int id, int BH, int n_qtiles, bool c
 template <int D, int NQ, int NW, int WPE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, float scale_log2,
     int n_qtiles, int BH) {
   constexpr int BM = NW * NQ * 32;
   constexpr int BN = kFwdBN;
@@ -104,12 +101,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int b = bh / Hq;
   const int hq = bh - b * Hq;
   const int hk = hq / (Hq / Hkv);
-  const uint16_t* qp = q + (size_t)bh * N * D;
-  const uint16_t* kp = k + (size_t)(b * Hkv + hk) * N * D;
-  const uint16_t* vp = v + (size_t)(b * Hkv + hk) * N * D;
-
+  const SeqRows sr = seq_rows(geo, b, hq, Hq, hk, Hkv);
+  const int Nq = sr.lq, Nk = sr.lk;
   const int q0 = qt * BM;
+  if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
+  const uint16_t* qp = q + sr.q * D;
+  const uint16_t* kp = k + sr.k * D;
+  const uint16_t* vp = v + sr.k * D;
   const int qw0 = q0 + wave * NQ * 32;
+  // Causal masks align the last query with the last key: query i sees keys j <= i + Nk - Nq.
+  const int qd0 = qw0 + (Nk - Nq);
 
   // Q^T operand: lane holds query qw0 + qb*32 + l32, features 16c + 8*h32 .. +7.
   bf16x8 qreg[NQ][DC];
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       u32x4 u = {0u, 0u, 0u, 0u};
-      if (qi < N) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
+      if (qi < Nq) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
       qreg[qb][c] = as_bf16x8(u);
     }
   }
@@ -133,10 +134,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.f;
   float m_run[NQ], l_run[NQ];
 #pragma unroll
-  for (int qb = 0; qb < NQ; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
+  for (int qb = 0; qb < NQ; ++qb) { m_run[qb] = kMaxInit; l_run[qb] = 0.f; }
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int kv_end = CAUSAL ? min(Nk, q0 + BM + (Nk - Nq)) : Nk;
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
   u32x4 pk[CPT], pv[CPT];
   auto load_tile = [&](int t) {
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       const int col = c % (D / 8);
       const int key = t0 + row;
       u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (key < N) {
+      if (key < Nk) {
         zk = ld_global16(kp + (size_t)key * D + col * 8);
         zv = ld_global16(vp + (size_t)key * D + col * 8);
       }
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const char* ks = smem + (t & 1) * Lds::STAGE;
     const char* vs = ks + Lds::KBYTES;
     // A wave whose queries all precede this tile has nothing to add (causal skip).
-    const bool active = !CAUSAL || (t0 <= qw0 + NQ * 32 - 1);
+    const bool active = !CAUSAL || (t0 <= qd0 + NQ * 32 - 1);
     if (active) {
       f32x16 s[KB][NQ];
 #pragma unroll
@@ -198,17 +199,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         }
       }
       // Mask keys past the end and, on diagonal tiles, keys after the query.
-      const bool need_mask = (t0 + BN > N) || (CAUSAL && t0 + BN - 1 > qw0);
+      const bool need_mask = (t0 + BN > Nk) || (CAUSAL && t0 + BN - 1 > qd0);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int qb = 0; qb < NQ; ++qb) {
-            const int qi = qw0 + qb * 32 + l32;
+            const int kmax = qd0 + qb * 32 + l32;  // last key of this lane's row
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-              if (kj >= N || (CAUSAL && kj > qi)) s[kb][qb][r] = -INFINITY;
+              if (kj >= Nk || (CAUSAL && kj > kmax)) s[kb][qb][r] = -INFINITY;
             }
           }
       }
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         mx = max_xor32(mx) * scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kLazy) != 0) {  // wave-uniform branch
           const float m_new = fmaxf(m_run[qb], mx);
-          const float alpha = fast_exp2(m_run[qb] - m_new);  // m_new finite: key 0 is never masked
+          const float alpha = fast_exp2(m_run[qb] - m_new);  // both finite (m starts at kMaxInit)
           m_run[qb] = m_new;
           l_run[qb] *= alpha;
 #pragma unroll
@@ -272,14 +273,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     __syncthreads();
   }
 
-  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
-  uint16_t* op = o + (size_t)bh * N * D;
+  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l); a row without keys (l = 0) gets O = 0
+  // and LSE = -inf.
+  uint16_t* op = o + sr.q * D;
 #pragma unroll
   for (int qb = 0; qb < NQ; ++qb) {
     const float lt = sum_xor32(l_run[qb]);
-    const float inv = 1.f / lt;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int qi = qw0 + qb * 32 + l32;
-    if (qi < N) {
+    if (qi < Nq) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -290,345 +292,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           w[1] = pack_bf16x2(acc[db][qb][4 * jj + 2] * inv, acc[db][qb][4 * jj + 3] * inv);
           *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
         }
-      if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run[qb] + fast_log2(lt)) * kLn2;
+      if (lse != nullptr && h32 == 0) lse[sr.q + qi] = (m_run[qb] + fast_log2(lt)) * kLn2;
     }
   }
 }
 
-// Ping-pong forward (bf16).  Eight waves, two per SIMD; each wave owns 32 query rows of a
-// 256-row block.  Every key tile is processed by each wave in two phases:
-//   M(t): O^T += V_{t-1}^T P_{t-1}^T and S_t^T = K_t Q^T   (MFMA + LDS reads),
-//   V(t): online softmax of S_t into P_t                   (vector ALU only).
-// Waves 0-3 (group 0) and 4-7 (group 1) run the same sequence one phase apart, so on every
-// SIMD one wave issues MFMAs while its partner does the softmax, and the matrix core and the
-// vector ALU work at the same time.  Phases are separated by workgroup barriers ("slots").
-// The LDS holds two stages; stage t&1 holds the pair {K_t, V_{t-1}} that the M(t) phases of
-// both groups read in slots 2t and 2t+1.  The pair t+1 is copied global -> LDS directly
-// (no registers) starting in slot 2t and must have landed by the end of slot 2t+1.
-#ifndef XATTN_PP_LOOKAHEAD
-#define XATTN_PP_LOOKAHEAD 8
-#endif
-#ifndef XATTN_PP_PRIO
-#define XATTN_PP_PRIO 1
-#endif
-
-template <int D>
-struct PPShape {
-  static constexpr int BN = kFwdBN, KB = BN / 32, DC = D / 16, DB = D / 32;
-  static constexpr int TILE = BN * D * 2;          // bytes of one K or V tile
-  static constexpr int NPV = KB * 2 * DB;          // P V MFMAs per tile
-  static constexpr int NQK = DC * KB;              // Q K^T MFMAs per tile
-};
-
-// One M phase: NPV MFMAs of O^T += V^T P^T (if PV) then NQK MFMAs of S^T = K Q^T (if QK), each
-// operand read from LDS LOOKAHEAD MFMAs ahead of its use, in a fixed issue order.
-template <int D>
-using PPOffsets = TileOffsets<D>;
-
-// hook(k), k = 0 .. NHOOK-1, is called at evenly spaced points between the MFMAs.
-template <int D, bool PV, bool QK, int NHOOK, typename Hook>
-__device__ __forceinline__ void pp_mphase(const char* ks, const char* vs, const bf16x8 (&pb)[PPShape<D>::KB][2],
-                                          const bf16x8 (&qreg)[PPShape<D>::DC], f32x16 (&acc)[PPShape<D>::DB],
-                                          f32x16 (&s)[PPShape<D>::KB], const PPOffsets<D>& ofs, Hook&& hook) {
-  using S = PPShape<D>;
-  constexpr int L = XATTN_PP_LOOKAHEAD;
-  constexpr int N0 = PV ? S::NPV : 0;
-  constexpr int NOPS = N0 + (QK ? S::NQK : 0);
-  auto operand = [&](auto ic) -> bf16x8 {
-    constexpr int i = decltype(ic)::value;
-    if constexpr (i < N0) {  // (kb, sh, db) with db fastest; rows kb*32 + 16*sh + {rl, rl+8}
-      constexpr int db = i % S::DB, sh = (i / S::DB) % 2, kb = i / (2 * S::DB);
-      const char* base = vs + (kb * 32 + 16 * sh) * (2 * D);
-      return join_tr(ds_read_tr16(base + ofs.v[db][0]), ds_read_tr16(base + ofs.v[db][1]));
-    } else {                 // (c, kb) with kb fastest; rows kb*32 + l32
-      constexpr int j = i - N0, kb = j % S::KB, c = j / S::KB;
-      return *reinterpret_cast<const bf16x8*>(ks + kb * 32 * (2 * D) + ofs.k[c]);
-    }
-  };
-  if constexpr (QK) {
-#pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-  }
-  bf16x8 buf[L];
-  static_for<(L < NOPS ? L : NOPS)>([&](auto ic) { buf[decltype(ic)::value] = operand(ic); });
-  sched_fence();
-  static_for<NOPS>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    if constexpr (i < N0) {
-      constexpr int db = i % S::DB, sh = (i / S::DB) % 2, kb = i / (2 * S::DB);
-      acc[db] = mfma32(buf[i % L], pb[kb][sh], acc[db]);
-    } else {
-      constexpr int j = i - N0, kb = j % S::KB, c = j / S::KB;
-      s[kb] = mfma32(buf[i % L], qreg[c], s[kb]);
-    }
-    if constexpr (i + L < NOPS) buf[i % L] = operand(std::integral_constant<int, i + L>{});
-    static_for<NHOOK>([&](auto kc) {
-      constexpr int kk = decltype(kc)::value;
-      if constexpr (i == (2 * kk + 1) * NOPS / (2 * NHOOK)) hook(kk);
-    });
-    sched_fence();
-  });
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
-    int n_qtiles, int BH) {
-  using S = PPShape<D>;
-  constexpr int NW = 8, BM = 256, BN = S::BN, KB = S::KB, DC = S::DC, DB = S::DB, TILE = S::TILE;
-  constexpr int STAGE = 2 * TILE;                // one pair {K_t, V_{t-1}}
-  constexpr int NSTAGE = 4;
-  constexpr int RPC = 1024 / (2 * D);            // tile rows covered by one 1 KB wave copy
-  constexpr int CPT = TILE / 1024;               // wave copies per tile
-  constexpr int CPW = CPT / NW;                  // copies per wave and tile
-  static_assert(CPW >= 1 && CPT % NW == 0, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];  // [stage][K | V]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h32 = lane >> 5;
-  const int grp = wave >> 2;                     // wave w runs on SIMD w % 4
-  const int rb = 2 * (wave & 3) + grp;           // the two waves of a SIMD own adjacent rows
-
-  int bh, qt;
-  fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
-  const uint16_t* qp = q + (size_t)bh * N * D;
-  const uint16_t* kp = k + (size_t)(b * Hkv + hk) * N * D;
-  const uint16_t* vp = v + (size_t)(b * Hkv + hk) * N * D;
-  const int q0 = qt * BM;
-  const int qw0 = q0 + rb * 32;
-
-  // Q^T operand: lane holds query qw0 + l32, features 16c + 8*h32 .. +7.
-  bf16x8 qreg[DC];
-  {
-    const int qi = qw0 + l32;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (qi < N) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
-      qreg[c] = as_bf16x8(u);
-    }
-  }
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  f32x16 s[KB];
-  bf16x8 pb[KB][2];
-  float m_run = -INFINITY, l_run = 0.f;
-  PPOffsets<D> ofs;
-  ofs.init(lane);
-
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int T = (kv_end + BN - 1) / BN;
-
-  // Pair t lives in LDS stage gray(t mod 4), so consecutive pairs differ in one stage bit and
-  // the M phase moves its operand offsets on with one XOR.  Every wave copies CPW of the 1 KB
-  // blocks of each tile: wave copy j covers tile bytes [1024 j, 1024 j + 1024), i.e. rows
-  // RPC*j .. RPC*j + RPC-1.  Lane l fills physical chunk l of the block: row RPC*j + l/(D/8),
-  // swizzled chunk l%(D/8), so it reads logical chunk (l%(D/8)) ^ swizzle(row); that offset
-  // is fixed per wave and copy.  Rows past N read row N-1 (finite data whose probabilities
-  // are zero).
-  auto stage_of = [](int t) { const int m = t & 3; return m ^ (m >> 1); };
-  const int lrow = lane / (D / 8);
-  uint32_t loff[CPW];
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int r = RPC * (wave * CPW + i) + lrow;
-    loff[i] = lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(r, 0) >> 4) & (D / 8 - 1)));
-  }
-  // This wave's copy i of tile `tile` of K (is_k) or V into the stage of pair p.
-  auto copy = [&](int tile, bool is_k, int p, int i) __attribute__((always_inline)) {
-    const int j = wave * CPW + i;
-    const int row0 = tile * BN + RPC * j;
-    const char* base = reinterpret_cast<const char*>(is_k ? kp : vp);
-    const char* dst = smem + stage_of(p) * STAGE + (is_k ? 0 : TILE) + 1024 * j;
-    // Byte offsets stay below 2^31: the API bounds N*d*2 per head well under that.
-    if (row0 + RPC <= N) {
-      dma16(base, (uint32_t)row0 * (2 * D) + loff[i], dst);
-    } else {
-      const int row = min(row0 + lrow, N - 1);
-      dma16(base, (uint32_t)row * (2 * D) + (loff[i] - lrow * (2 * D)), dst);
-    }
-  };
-  // A wave whose queries all precede tile t has nothing to add for it (causal skip).
-  auto active = [&](int t) __attribute__((always_inline)) { return !CAUSAL || t * BN <= qw0 + 31; };
-
-  // V(t): online softmax of S_t ([OPT] §3.2.1) in base 2 with a lazy reference max; hook(k)
-  // is called at four points spread over the phase (to issue tile copies evenly).
-  auto vphase = [&](int t, auto&& hook) __attribute__((always_inline)) {
-    const int t0 = t * BN;
-    if ((t0 + BN > N) || (CAUSAL && t0 + BN - 1 > qw0)) {
-      const int qi = qw0 + l32;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          if (kj >= N || (CAUSAL && kj > qi)) s[kb][r] = -INFINITY;
-        }
-    }
-    // Independent chains throughout, so that one wave keeps the ALU busy on its own.
-    float mx4[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx4[j] = fmaxf(s[0][4 * j], s[0][4 * j + 1]);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = (kb == 0 ? 2 : 0); r < 4; r += 2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx4[j] = fmaxf(fmaxf(mx4[j], s[kb][4 * j + r]), s[kb][4 * j + r + 1]);
-    hook(0);
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = max_xor32(mx) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {  // wave-uniform branch
-      const float m_new = fmaxf(m_run, mx);  // finite: key 0 is never masked
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    }
-    // p = 2^(s * scale * log2 e - m), in place.
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], scale_log2, -m_run);
-    hook(1);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(s[kb][r]);
-    hook(2);
-    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rs4[r & 3] += s[kb][r];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        u32x4 u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(s[kb][8 * sh + 2 * e], s[kb][8 * sh + 2 * e + 1]);
-        pb[kb][sh] = as_bf16x8(u);
-      }
-    hook(3);
-    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
-  };
-
-  // Prologue: pairs 0 and 1, a zero V half in stage 0 and zero P (so M(0)'s P V part adds
-  // nothing).
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    copy(0, true, 0, i);
-    if (1 < T) copy(1, true, 1, i);
-    copy(0, false, 1, i);
-  }
-  for (int i = tid; i < TILE / 16; i += NW * 64)
-    *reinterpret_cast<u32x4*>(smem + TILE + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh) pb[kb][sh] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-  wait_vmem();  // also covers the Q loads
-  lds_barrier();
-
-  // Slot schedule (2T + 2 slots, one barrier each).  Group 0: slot 2t = M(t), slot 2t+1 =
-  // V(t); group 1 runs one slot later.  Copies run two pairs ahead: every wave copies its
-  // blocks of K_{t+2} in slot 2t and of V_{t+1} in slot 2t+1, spread over whatever phase it
-  // is in, into stage gray((t+2) mod 4), last read in slot 2t-3.  Pair t+1 is waited for at
-  // the end of slot 2t+1.  M(T) computes an S that is never used.  A wave whose rows all
-  // precede tile t-1 (causal) has no M(t) or later work.
-  const int slots = 2 * T + 2;
-  for (int sl = 0; sl < slots; ++sl) {
-    const int cpair = (sl >> 1) + 2;
-    const bool cis_k = !(sl & 1);
-    const int ctile = cis_k ? cpair : cpair - 1;
-    const bool has_copy = ctile < T;
-    auto hook = [&](int kq) __attribute__((always_inline)) {
-      if (has_copy) copy(ctile, cis_k, cpair, kq);
-    };
-    const int ls = sl - grp;
-    if (ls >= 0 && ls <= 2 * T) {
-      const int t = ls >> 1;
-      if (!(ls & 1)) {
-        if (t == 0 || active(t - 1)) {
-          if (XATTN_PP_PRIO) __builtin_amdgcn_s_setprio(1);
-          pp_mphase<D, true, true, CPW>(smem, smem + TILE, pb, qreg, acc, s, ofs, hook);
-          if (XATTN_PP_PRIO) __builtin_amdgcn_s_setprio(0);
-          ofs.toggle(((t & 1) ? 2 : 1) * STAGE);
-        } else {
-#pragma unroll
-          for (int i = 0; i < CPW; ++i) hook(i);
-        }
-      } else if (t < T) {
-        // Also run for a causally finished wave: its tile is fully masked, so P = 0 and the
-        // statistics do not move.
-        vphase(t, [&](int kq) __attribute__((always_inline)) {
-#pragma unroll
-          for (int i = 0; i < CPW; ++i)
-            if (i * 4 / CPW == kq) hook(i);
-        });
-      } else {
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) hook(i);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) hook(i);
-    }
-    if (sl & 1) {
-      // Pair t+1 (t = sl/2) must have landed; this wave's newer copies (K_{t+2}, V_{t+1})
-      // may stay in flight.
-      const int t = sl >> 1;
-      if (t + 2 < T) wait_vmem_n<2 * CPW>();
-      else if (t + 1 < T) wait_vmem_n<CPW>();
-      else wait_vmem();
-    }
-    lds_barrier();
-  }
-
-  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
-  uint16_t* op = o + (size_t)bh * N * D;
-  const float lt = sum_xor32(l_run);
-  const float inv = 1.f / lt;
-  const int qi = qw0 + l32;
-  if (qi < N) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = db * 32 + 8 * jj + 4 * h32;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
-      }
-    if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run + fast_log2(lt)) * kLn2;
-  }
-}
-
-// Interleaved forward (bf16, d = 128).  Four waves, one per SIMD, each owning 64 query rows
-// (two 32-row blocks) of a 256-row block, so every K or V operand read from LDS feeds two
-// MFMAs.  Each wave software-pipelines its own work over 32-key blocks u: in step u it issues
-//   O^T += V_{u-1}^T P_{u-1}^T  and  S_{u+1}^T = K_{u+1} Q^T        (32 MFMAs)
+// Interleaved forward (bf16, d = 128).  Eight waves, two per SIMD, each owning 32 query rows
+// of a 256-row block (XATTN_ILV_RB = 2: four waves of 64 rows, one per SIMD).  Each wave
+// software-pipelines its own work over 32-key blocks u: in step u it issues
+//   O^T += V_{u-1}^T P_{u-1}^T  and  S_{u+1}^T = K_{u+1} Q^T        (MFMAs)
 // and, between those MFMAs, the online softmax of S_u into P_u       (vector ALU),
 // which are independent of each other, so the matrix core and the vector ALU of the SIMD
-// work at the same time without a second wave.  The S and P register sets alternate roles
-// between even and odd steps.  K and V arrive in 64-key tiles through direct global -> LDS
-// copies into two rings of four stages (128 KB); the two steps of tile t read K_t, K_{t+1},
-// V_{t-1}, V_t, copy K_{t+3} and V_{t+2}, and end with one barrier.  A rescale of O forced
-// by a moved running max is applied after the step's MFMAs, before P_u is added.
+// work at the same time within one wave.  The S and P register sets alternate roles between
+// even and odd steps.  K and V arrive in 64-key tiles through direct global -> LDS copies
+// into two rings of four stages (128 KB); the two steps of tile t read K_t, K_{t+1}, V_{t-1},
+// V_t, copy K_{t+3} and V_{t+2}, and end with one barrier.  A rescale of O forced by a moved
+// running max is applied after the step's MFMAs, before P_u is added.
 #ifndef XATTN_FWD_ILV
 #define XATTN_FWD_ILV 1
 #endif
@@ -700,7 +379,7 @@ struct IlvShape {
 template <int D, int RB_, bool CAUSAL>
 __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 / RB_, 2 / RB_))) void fwd_ilv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, float scale_log2,
     int n_qtiles, int BH) {
   using S = IlvShape<D, RB_>;
   constexpr int BN = S::BN, DC = S::DC, DB = S::DB, RB = S::RB, NS = S::NS, NW = S::NW;
@@ -717,11 +396,16 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
   const int b = bh / Hq;
   const int hq = bh - b * Hq;
   const int hk = hq / (Hq / Hkv);
-  const uint16_t* qp = q + (size_t)bh * N * D;
-  const uint16_t* kp = k + (size_t)(b * Hkv + hk) * N * D;
-  const uint16_t* vp = v + (size_t)(b * Hkv + hk) * N * D;
+  const SeqRows sr = seq_rows(geo, b, hq, Hq, hk, Hkv);
+  const int Nq = sr.lq, Nk = sr.lk;
   const int q0 = qt * S::BM;
+  if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
+  const uint16_t* qp = q + sr.q * D;
+  const uint16_t* kp = k + sr.k * D;
+  const uint16_t* vp = v + sr.k * D;
   const int qw0 = q0 + wave * (RB * 32);  // rows qw0 + 32 rb + l32
+  // Causal masks align the last query with the last key: query i sees keys j <= i + Nk - Nq.
+  const int qd0 = qw0 + (Nk - Nq);        // last key visible to the wave's first row
 
   // Q^T operands: lane holds query qw0 + 32 rb + l32, features 16c + 8*h32 .. +7.
   bf16x8 qreg[RB][DC];
@@ -731,7 +415,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       u32x4 u = {0u, 0u, 0u, 0u};
-      if (qi < N) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
+      if (qi < Nq) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
       qreg[rb][c] = as_bf16x8(u);
     }
   }
@@ -744,17 +428,46 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
       for (int r = 0; r < 16; ++r) acc[rb][db][r] = 0.f;
   float m_run[RB], l_run[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) { m_run[rb] = -INFINITY; l_run[rb] = 0.f; }
-  PPOffsets<D> ofs;
-  ofs.init(lane);
+  for (int rb = 0; rb < RB; ++rb) { m_run[rb] = kMaxInit; l_run[rb] = 0.f; }
 
-  const int kv_end = CAUSAL ? min(N, q0 + S::BM) : N;
-  const int T = (kv_end + BN - 1) / BN;
+  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l); a row without keys (l = 0) gets O = 0
+  // and LSE = -inf.
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    uint16_t* op = o + sr.q * D;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float lt = sum_xor32(l_run[rb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int qi = qw0 + 32 * rb + l32;
+      if (qi < Nq) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d = db * 32 + 8 * jj + 4 * h32;
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[rb][db][4 * jj + 0] * inv, acc[rb][db][4 * jj + 1] * inv);
+            w[1] = pack_bf16x2(acc[rb][db][4 * jj + 2] * inv, acc[rb][db][4 * jj + 3] * inv);
+            *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
+          }
+        if (lse != nullptr && h32 == 0) lse[sr.q + qi] = (m_run[rb] + fast_log2(lt)) * kLn2;
+      }
+    }
+  };
+
+  const int kv_end = CAUSAL ? min(Nk, q0 + S::BM + (Nk - Nq)) : Nk;
+  const int T = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  if (T == 0) {  // no key for any row of the tile (empty key sequence, or causal with Nk < Nq)
+    epilogue();
+    return;
+  }
+  TileOffsets<D> ofs;
+  ofs.init(lane);
 
   // Copies: tile i of K (V) lives in stage i % 4 of the K (V) ring.  Wave copy j covers tile
   // rows RPC*j .. RPC*j + RPC-1; lane l fills physical chunk l of that 1 KB block (row
   // RPC*j + l/(D/8), chunk l%(D/8)), so it reads logical chunk (l%(D/8)) ^ swizzle(row).
-  // Rows past N read row N-1 (finite data whose probabilities are zero).
+  // Rows past the last key read the last key (finite data whose probabilities are zero).
   const int lrow = lane / (D / 8);
   uint32_t loff[CPW];
 #pragma unroll
@@ -763,14 +476,14 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
     loff[i] = lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(r, 0) >> 4) & (D / 8 - 1)));
   }
   // Branch-free (it sits inside the interleaved MFMA sequence): rows are clamped per lane.
-  // Byte offsets stay below 2^31: the API bounds N*d*2 per head well under that.  The LDS
+  // Byte offsets stay below 2^31: the API bounds the key rows times 2d under that.  The LDS
   // destination is computed in scalar registers from a wave index made uniform once.
   const void* kbase = wave_uniform(kp);
   const void* vbase = wave_uniform(vp);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const uint32_t wdst = lds0 + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (CPW * 1024);
   auto copy = [&](int tile, bool is_k, int i) __attribute__((always_inline)) {
-    const int row = min(tile * BN + RPC * (wave * CPW + i) + lrow, N - 1);
+    const int row = min(tile * BN + RPC * (wave * CPW + i) + lrow, Nk - 1);
     const uint32_t m0v = wdst + (is_k ? 0 : NS * TILE) + (tile & (NS - 1)) * TILE + 1024 * i;
     dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff[i] - lrow * (2 * D)), m0v);
   };
@@ -793,7 +506,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
     }
   };
   // A wave has work in step u while key block u-1 still holds keys at or before its last row.
-  auto active = [&](int u) __attribute__((always_inline)) { return !CAUSAL || (u - 1) * 32 <= qw0 + RB * 32 - 1; };
+  auto active = [&](int u) __attribute__((always_inline)) { return !CAUSAL || (u - 1) * 32 <= qd0 + RB * 32 - 1; };
 
   // Prologue: K_0, K_1, K_2, V_0, V_1; V stage 3 (read as block -1, with P_{-1} = 0) is zeroed.
 #pragma unroll
@@ -842,21 +555,21 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
 
   // Step u: sc = S_u (complete), sn <- S_{u+1}, pp = P_{u-1}, pc <- P_u; copies of the
   // step's half of the tile's copy list (K_{t+3} on even steps, V_{t+2} on odd ones).  Tiles
-  // past the end are copied too, clamped to row N-1, into stages nobody reads any more, so
+  // past the end are copied too, clamped to the last key, into stages nobody reads any more, so
   // every step issues the same copies and the wait counts stay fixed.
   auto step = [&](int u, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2], u32x4(&pc)[RB][2],
                   int ctile, bool cis_k) __attribute__((always_inline)) {
     if (active(u)) {
       if constexpr (RB > 1 && XATTN_ILV_QKASM != 0) qk_result_fence();  // S_u came from asm MFMAs
       const int u0 = u * 32;
-      if ((u0 + 32 > N) || (CAUSAL && u0 + 31 > qw0)) {
+      if ((u0 + 32 > Nk) || (CAUSAL && u0 + 31 > qd0)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const int qi = qw0 + 32 * rb + l32;
+          const int kmax = qd0 + 32 * rb + l32;  // last key of this lane's row
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = u0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            if (kj >= N || (CAUSAL && kj > qi)) sc[rb][r] = -INFINITY;
+            if (kj >= Nk || (CAUSAL && kj > kmax)) sc[rb][r] = -INFINITY;
           }
         }
       }
@@ -912,7 +625,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
           float mx = fmaxf(m4[vrb][0], m4[vrb][1]);
           mx = max_xor32(mx) * scale_log2;
           // Lazy reference max ([OPT] §3.2.1 with a deferred rescale): it moves only when a
-          // row's block max exceeds it by more than 2^kLazy; finite, as key 0 is never masked.
+          // row's block max exceeds it by more than 2^kLazy; it starts at kMaxInit (finite).
           const bool up = __builtin_amdgcn_ballot_w64(mx > m_run[vrb] + kLazy) != 0;
           const float m_new = up ? fmaxf(m_run[vrb], mx) : m_run[vrb];
           alpha[vrb] = fast_exp2(m_run[vrb] - m_new);
@@ -945,10 +658,11 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
 #if XATTN_ILV_SUMCHECK
       // Reference max check ([OPT] §3.2.1, lazily): the step's probabilities were formed
       // against the current reference m.  If every lane-partial row sum stays at or below
-      // kSumMax (so does every probability; NaN, from the first step's m = -inf, fails the
-      // test) they are kept.  Otherwise the wave redoes the step with m moved to the true
-      // running max (finite: key 0 is never masked) and rescales O and l by 2^(m_old - m_new);
-      // the P V products already issued this step used the old m, as O did.
+      // kSumMax (so does every probability; the first visible key of a row overflows against
+      // the initial m = kMaxInit, and +inf fails the test) they are kept.  Otherwise the wave
+      // redoes the step with m moved to the running max (at least kMaxInit, so finite) and
+      // rescales O and l by 2^(m_old - m_new); the P V products already issued this step used
+      // the old m, as O did.  Masked scores (-inf) give probability 0 against any finite m.
       {
         bool bad = false;
 #pragma unroll
@@ -1031,27 +745,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
     });
   }
 
-  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
-  uint16_t* op = o + (size_t)bh * N * D;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float lt = sum_xor32(l_run[rb]);
-    const float inv = 1.f / lt;
-    const int qi = qw0 + 32 * rb + l32;
-    if (qi < N) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d = db * 32 + 8 * jj + 4 * h32;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[rb][db][4 * jj + 0] * inv, acc[rb][db][4 * jj + 1] * inv);
-          w[1] = pack_bf16x2(acc[rb][db][4 * jj + 2] * inv, acc[rb][db][4 * jj + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
-        }
-      if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run[rb] + fast_log2(lt)) * kLn2;
-    }
-  }
+  epilogue();
 }
 
 // fp32 inputs (d = 64): the same tiled online softmax with v_mfma_f32_32x32x2_f32, one
@@ -1059,7 +753,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float scale_log2,
+    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, float scale_log2,
     int n_qtiles, int BH) {
   constexpr int D = 64, BM = 128, BN = 32, P = D + 1;  // P: padded pitch in floats
   __shared__ float ks[BN * P];
@@ -1068,29 +762,33 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   int bh, qt;
   fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
   const int b = bh / Hq, hq = bh - b * Hq, hk = hq / (Hq / Hkv);
-  const float* qp = q + (size_t)bh * N * D;
-  const float* kp = k + (size_t)(b * Hkv + hk) * N * D;
-  const float* vp = v + (size_t)(b * Hkv + hk) * N * D;
+  const SeqRows sr = seq_rows(geo, b, hq, Hq, hk, Hkv);
+  const int Nq = sr.lq, Nk = sr.lk;
   const int q0 = qt * BM, qw0 = q0 + wave * 32, qi = qw0 + l32;
+  if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
+  const float* qp = q + sr.q * D;
+  const float* kp = k + sr.k * D;
+  const float* vp = v + sr.k * D;
+  const int qd0 = qw0 + (Nk - Nq), kmax = qi + (Nk - Nq);  // causal: query i sees keys <= i + Nk - Nq
 
   float qr[D / 2];
 #pragma unroll
-  for (int c = 0; c < D / 2; ++c) qr[c] = (qi < N) ? qp[(size_t)qi * D + 2 * c + h32] : 0.f;
+  for (int c = 0; c < D / 2; ++c) qr[c] = (qi < Nq) ? qp[(size_t)qi * D + 2 * c + h32] : 0.f;
   f32x16 acc[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) { acc[0][r] = 0.f; acc[1][r] = 0.f; }
   float m_run = -INFINITY, l_run = 0.f;
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int kv_end = CAUSAL ? min(Nk, q0 + BM + (Nk - Nq)) : Nk;
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = t * BN;
     for (int i = tid; i < BN * D; i += 256) {
       const int row = i / D, col = i % D, key = t0 + row;
-      ks[row * P + col] = key < N ? kp[(size_t)key * D + col] : 0.f;
-      vs[row * P + col] = key < N ? vp[(size_t)key * D + col] : 0.f;
+      ks[row * P + col] = key < Nk ? kp[(size_t)key * D + col] : 0.f;
+      vs[row * P + col] = key < Nk ? vp[(size_t)key * D + col] : 0.f;
     }
     __syncthreads();
-    if (!CAUSAL || t0 <= qw0 + 31) {
+    if (!CAUSAL || t0 <= qd0 + 31) {
       f32x16 s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -1100,7 +798,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kj = t0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        if (kj >= N || (CAUSAL && kj > qi)) s[r] = -INFINITY;
+        if (kj >= Nk || (CAUSAL && kj > kmax)) s[r] = -INFINITY;
         mx = fmaxf(mx, s[r]);
       }
       mx = max_xor32(mx);
@@ -1123,96 +821,54 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     }
     __syncthreads();
   }
+  // A row without keys (l = 0, m = -inf) gets O = 0 and LSE = -inf.
   const float lt = sum_xor32(l_run);
-  if (qi < N) {
-    float* op = o + (size_t)bh * N * D + (size_t)qi * D;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qi < Nq) {
+    float* op = o + (sr.q + qi) * D;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) op[db * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)] = acc[db][r] / lt;
-    if (lse != nullptr && h32 == 0) lse[(size_t)bh * N + qi] = (m_run + fast_log2(lt)) * kLn2;
+      for (int r = 0; r < 16; ++r) op[db * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)] = acc[db][r] * inv;
+    if (lse != nullptr && h32 == 0) lse[sr.q + qi] = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -INFINITY;
   }
 }
 
 // ------------------------------------------------------------------------- host launchers
-template <int D>
-static hipError_t launch_fwd_ilv_t(const FwdArgs& a) {
-  constexpr int RB = XATTN_ILV_RB;
-  constexpr int BM = IlvShape<D, RB>::BM;
-  const int n_qtiles = (a.N + BM - 1) / BM;
-  const int BH = a.B * a.Hq;
-  const dim3 grid(n_qtiles * BH), block(IlvShape<D, RB>::NW * 64);
-  const float sl2 = a.scale * kLog2e;
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_ilv_kernel<D, RB, true>), grid, block, 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
-                       n_qtiles, BH);
-  else
-    hipLaunchKernelGGL((fwd_ilv_kernel<D, RB, false>), grid, block, 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
-                       n_qtiles, BH);
-  return hipGetLastError();
-}
+// Grid: one workgroup per (query tile, batch, head); query tiles cover the longest query
+// sequence and those past a shorter sequence's end exit at once.
+template <typename T>
+using FwdKernel = void (*)(const T*, const T*, const T*, T*, float*, int, int, SeqGeo, float, int, int);
 
-template <int D>
-static hipError_t launch_fwd_pp_t(const FwdArgs& a) {
-  constexpr int BM = 256;
-  const int n_qtiles = (a.N + BM - 1) / BM;
+template <typename T>
+static hipError_t launch_fwd_grid(FwdKernel<T> kern, int BM, int threads, const FwdArgs& a) {
+  const int n_qtiles = (a.max_q + BM - 1) / BM;
   const int BH = a.B * a.Hq;
-  const dim3 grid(n_qtiles * BH), block(512);
-  const float sl2 = a.scale * kLog2e;
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_pp_kernel<D, true>), grid, block, 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
-                       n_qtiles, BH);
-  else
-    hipLaunchKernelGGL((fwd_pp_kernel<D, false>), grid, block, 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.N, sl2,
-                       n_qtiles, BH);
-  return hipGetLastError();
-}
-
-template <int D, int NQ, int NW, int WPE>
-static hipError_t launch_fwd_bf16_t(const FwdArgs& a) {
-  constexpr int BM = NW * NQ * 32;
-  const int n_qtiles = (a.N + BM - 1) / BM;
-  const int BH = a.B * a.Hq;
-  const dim3 grid(n_qtiles * BH), block(NW * 64);
-  const float sl2 = a.scale * kLog2e;
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, WPE, true>), grid, block, 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                       a.lse, a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NQ, NW, WPE, false>), grid, block, 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                       a.lse, a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
+  if (n_qtiles == 0) return hipSuccess;  // every query sequence is empty
+  const SeqGeo geo{a.cu_q, a.cu_k, a.Nq, a.Nk};
+  hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(threads), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, geo, a.scale * kLog2e, n_qtiles, BH);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.dtype == 0) {  // fp32, d = 64
-    const int n_qtiles = (a.N + 127) / 128;
-    const int BH = a.B * a.Hq;
-    const float sl2 = a.scale * kLog2e;
-    if (a.causal)
-      hipLaunchKernelGGL(fwd_f32_kernel<true>, dim3(n_qtiles * BH), dim3(256), 0, a.stream,
-                         (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                         a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
-    else
-      hipLaunchKernelGGL(fwd_f32_kernel<false>, dim3(n_qtiles * BH), dim3(256), 0, a.stream,
-                         (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                         a.Hq, a.Hkv, a.N, sl2, n_qtiles, BH);
-    return hipGetLastError();
-  }
+  if (a.dtype == 0)  // fp32, d = 64
+    return launch_fwd_grid<float>(a.causal ? fwd_f32_kernel<true> : fwd_f32_kernel<false>, 128, 256, a);
 #if XATTN_FWD_ILV
-  if (a.d == 128) return launch_fwd_ilv_t<128>(a);
+  if (a.d == 128) {
+    using S = IlvShape<128, XATTN_ILV_RB>;
+    return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, XATTN_ILV_RB, true> : fwd_ilv_kernel<128, XATTN_ILV_RB, false>,
+                           S::BM, S::NW * 64, a);
+  }
 #endif
-#if XATTN_FWD_PP
-  if (a.d == 128) return launch_fwd_pp_t<128>(a);
-#endif
-  if (a.d == 128) return launch_fwd_bf16_t<128, XATTN_FWD128_NQ, XATTN_FWD128_NW, XATTN_FWD128_WPE>(a);
-  return launch_fwd_bf16_t<64, XATTN_FWD64_NQ, XATTN_FWD64_NW, XATTN_FWD64_WPE>(a);
+  if (a.d == 128) {
+    constexpr int NQ = XATTN_FWD128_NQ, NW = XATTN_FWD128_NW, WPE = XATTN_FWD128_WPE;
+    return launch_fwd_grid<uint16_t>(a.causal ? fwd_bf16_kernel<128, NQ, NW, WPE, true> : fwd_bf16_kernel<128, NQ, NW, WPE, false>,
+                           NW * NQ * 32, NW * 64, a);
+  }
+  constexpr int NQ = XATTN_FWD64_NQ, NW = XATTN_FWD64_NW, WPE = XATTN_FWD64_WPE;
+  return launch_fwd_grid<uint16_t>(a.causal ? fwd_bf16_kernel<64, NQ, NW, WPE, true> : fwd_bf16_kernel<64, NQ, NW, WPE, false>,
+                         NW * NQ * 32, NW * 64, a);
 }
 
 }  // namespace xattn

@@ -7,9 +7,14 @@
 
 namespace xattn {
 
+// Forward: dense Q/O [B,Hq,Nq,d], K/V [B,Hkv,Nk,d] (cu_q == nullptr), or packed
+// variable-length Q/O [Hq,Nq,d], K/V [Hkv,Nk,d] with per-sequence offsets cu_q/cu_k [B+1]
+// (Nq, Nk are then the totals and max_q the longest query sequence).  Causal masks are
+// aligned at the bottom right of each (query, key) block.
 struct FwdArgs {
   const void* q; const void* k; const void* v; void* o; float* lse;
-  int B, Hq, Hkv, N, d, dtype, causal;
+  const int* cu_q; const int* cu_k;
+  int B, Hq, Hkv, Nq, Nk, max_q, d, dtype, causal;
   float scale;
   hipStream_t stream;
 };

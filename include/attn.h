@@ -26,6 +26,8 @@
  *     LSE and D are fp32 [B, Hq, N]; decode Q/O are [B, Hq, d] (one token each), the KV
  *     cache [B, Hkv, L, d].  Element type is given by `dtype` for Q/K/V/O/dO/dQ/dK/dV.
  *   - Pointers must be 16-byte aligned.  `scale` must be finite and > 0.
+ *   - Sizes: B*H*N below 2^31 and N*d at most 2^29 per head (offsets within a head are 32-bit);
+ *     larger requests return ATTN_ERR_UNSUPPORTED.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only
  *     enqueue work and return; kernel faults surface at the caller's synchronisation.
  *   - Arguments are validated before any HIP call.  On a non-OK return nothing has been
@@ -74,6 +76,42 @@ const char* attn_last_error(void);
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int Hq, int Hkv, int N, int d, attn_dtype_t dtype, int causal,
                        float scale, void* stream);
+
+/*
+ * Forward attention of Nq queries against Nk keys per (batch, head): chunked prefill of Nq new
+ * tokens onto a cache of Nk keys, or multi-token decode, the cases between the full prefill
+ * and the single-token decode of [OPT] §4.2.1-§4.2.2.  Reading: the queries are the last Nq
+ * positions of a sequence whose keys are the Nk cached ones (the new tokens included).
+ *   q/o [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], lse [B,Hq,Nq] (optional)
+ *   causal != 0        query i sees keys j <= i + (Nk - Nq): the mask is aligned at the bottom
+ *                      right, so the last query sees every key and Nq == Nk is attn_fwd's mask
+ * A query row that sees no key (Nk == 0, or causal with i + Nk - Nq < 0) gets o = 0 and
+ * lse = -inf (the log of an empty sum).  Nq >= 1, Nk >= 0.  Supported d and dtype as attn_fwd;
+ * no workspace; bitwise deterministic.
+ */
+attn_status_t attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, attn_dtype_t dtype,
+                          int causal, float scale, void* stream);
+
+/*
+ * Forward attention over a batch of sequences of different lengths with no padding ([NOTE]
+ * Method, implementation details: each sequence is processed at its true length).  The tensors are packed: the batch
+ * is folded into the row axis of each head.
+ *   q/o [Hq,total_q,d], k/v [Hkv,total_k,d], lse [Hq,total_q] fp32 (optional)
+ *   cu_seqlens_q/k [B+1] int32 device arrays, 4-byte aligned, non-decreasing from 0 to
+ *                  total_q/total_k: sequence b owns query rows cu_seqlens_q[b] ..
+ *                  cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *   max_seqlen_q   the longest query sequence (sizes the grid; rows of a sequence at positions
+ *                  >= max_seqlen_q are not computed), 0 <= max_seqlen_q <= total_q
+ *   causal         per sequence as in attn_fwd_kv (bottom-right aligned with its own lengths)
+ * Sequences may be empty; a query row that sees no key gets o = 0 and lse = -inf.  The
+ * kernels clamp the offsets into [0, total] and make them non-decreasing, so malformed arrays
+ * give wrong rows but no out-of-bounds access.  Supported d and dtype as attn_fwd.
+ */
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                              int Hkv, int total_q, int total_k, int max_seqlen_q, int d,
+                              attn_dtype_t dtype, int causal, float scale, void* stream);
 
 /* Bytes of device workspace attn_bwd needs: fp32 per-row statistics (LSE * log2(e) and
  * D = rowsum(dO * O)) for every query row padded to a multiple of 64, i.e.

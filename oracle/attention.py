@@ -21,15 +21,16 @@ The backward is the textbook softmax gradient (the pages only say that it recomp
   dK = scale dS^T Q, with dK/dV summed over the query heads that share a KV head.
 Grouped-query attention maps query head h to KV head h // (Hq / Hkv) ([OPT] §5.3).
 Decode is the same definition with a single query row against a KV cache ([OPT] §4.2.2,
-[FUND] §2.3.1).  Every function is pinned by tests against closed forms, invariants,
+[FUND] §2.3.1); forward_kv takes Nq query rows against Nk keys (the causal mask aligned at
+the bottom right) and forward_varlen a packed batch of sequences of different lengths.  Every function is pinned by tests against closed forms, invariants,
 brute-force scalar loops and hand-derived fixtures; none is "parity unpinned".
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["upcast", "probabilities", "forward", "forward_rows", "backward", "decode",
-           "split_kv_decode", "lse_merge", "attention_flops"]
+__all__ = ["upcast", "probabilities", "forward", "forward_kv", "forward_varlen", "forward_rows", "backward",
+           "decode", "split_kv_decode", "lse_merge", "attention_flops"]
 
 
 def upcast(x: np.ndarray) -> np.ndarray:
@@ -99,6 +100,54 @@ def forward(q, k, v, scale: float, causal: bool):
             kv = _kv_head(h, Hq, Hkv)
             p, lse[b, h] = _softmax_rows(_scores(q[b, h], k[b, kv], scale, causal))
             o[b, h] = p @ v[b, kv]
+    return o, lse
+
+
+def forward_kv(q, k, v, scale: float, causal: bool):
+    """Nq queries against Nk keys: q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> O [B,Hq,Nq,d], LSE [B,Hq,Nq].
+
+    Chunked prefill onto a KV cache and multi-token decode sit between the full prefill and
+    the single-token decode of [OPT] §4.2.  Reading for the causal mask: the queries are the
+    last Nq positions of a sequence whose Nk keys include them, so query i sits at absolute
+    position i + Nk - Nq and the square mask of [FUND] §2.1 on absolute positions keeps keys
+    j <= i + Nk - Nq (aligned at the bottom right).  A row that keeps no key (Nk = 0, or
+    causal with i + Nk - Nq < 0) gets O = 0 and LSE = -inf, the log of an empty sum.
+    """
+    q, k, v = upcast(q), upcast(k), upcast(v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    o = np.zeros((B, Hq, Nq, dv))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    if Nk == 0:
+        return o, lse
+    pos = np.arange(Nq) + (Nk - Nq)
+    for b in range(B):
+        for h in range(Hq):
+            kv = _kv_head(h, Hq, Hkv)
+            p, lse[b, h] = _softmax_rows(_scores(q[b, h], k[b, kv], scale, causal, row_ids=pos))
+            o[b, h] = p @ v[b, kv]
+    return o, lse
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool):
+    """A batch of sequences of different lengths, packed without padding ([NOTE] Method,
+    implementation details: each sequence at its true length).
+
+    Reading of the packed layout: the batch is folded into the row axis of every head, so
+    q [Hq, total_q, d], k/v [Hkv, total_k, d]; sequence b owns query rows cu_q[b]..cu_q[b+1]-1
+    and key rows cu_k[b]..cu_k[b+1]-1.  Each sequence is forward_kv on its own rows (causal
+    masks aligned with its own lengths).  Returns O [Hq, total_q, d], LSE [Hq, total_q].
+    """
+    q, k, v = upcast(q), upcast(k), upcast(v)
+    Hq, total_q, _ = q.shape
+    o = np.zeros((Hq, total_q, v.shape[2]))
+    lse = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        ob, lb = forward_kv(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], scale, causal)
+        o[:, q0:q1], lse[:, q0:q1] = ob[0], lb[0]
     return o, lse
 
 

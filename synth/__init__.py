@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "normal_f32", "Workload", "WORKLOADS",
-    "make_prefill", "make_decode", "default_scale",
+    "make_prefill", "make_decode", "make_varlen", "default_scale",
 ]
 
 
@@ -116,3 +116,21 @@ def make_decode(B, Hq, Hkv, L, d, seed=0, dtype="bf16"):
             c[b] = _as_io(normal_f32(rng, (Hkv, L, d)), dtype)
         caches.append(c)
     return {"q": q, "k": caches[0], "v": caches[1]}
+
+
+def make_varlen(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", seed=0, qk_mult=1.0):
+    """Packed variable-length inputs: Q [Hq,total_q,d], K/V [Hkv,total_k,d] with sequence b
+    at rows cu_q[b]..cu_q[b+1]-1 (cu_k likewise); cu_q, cu_k are int32 [B+1] running sums of
+    the lengths.  Drawn Q, K, V from one PCG64 stream, rounded as in make_prefill.
+    """
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q = normal_f32(rng, (Hq, int(cu_q[-1]), d))
+    k = normal_f32(rng, (Hkv, int(cu_k[-1]), d))
+    v = normal_f32(rng, (Hkv, int(cu_k[-1]), d))
+    if qk_mult != 1.0:
+        assert math.log2(qk_mult).is_integer()
+        q *= np.float32(qk_mult)
+        k *= np.float32(qk_mult)
+    return {"q": _as_io(q, dtype), "k": _as_io(k, dtype), "v": _as_io(v, dtype), "cu_q": cu_q, "cu_k": cu_k}

@@ -57,6 +57,28 @@ def test_fwd_validation(kwargs, status):
     assert lib.attn_last_error() != b""
 
 
+def test_fwd_kv_and_varlen_validation():
+    def kv(Nq=64, Nk=128, k=P, d=128, dt=1):
+        return lib.attn_fwd_kv(P, k, P, P, P, 1, 2, 2, Nq, Nk, d, dt, 1, ctypes.c_float(0.1), None)
+    assert kv(Nq=0) == 1
+    assert kv(Nk=-1) == 1
+    assert kv(d=96) == 2
+    assert kv(Nk=1 << 23) == 2          # a head's N*d above 2^29
+    assert kv(k=None) == 1              # keys present but no pointer
+
+    def vl(cu_q=P, cu_k=P, B=4, total_q=100, total_k=300, max_q=40, q=P, k=P, dt=1):
+        return lib.attn_fwd_varlen(q, k, P, P, P, cu_q, cu_k, B, 2, 1, total_q, total_k, max_q, 64, dt, 1,
+                                   ctypes.c_float(0.1), None)
+    assert vl(cu_q=None) == 1
+    assert vl(cu_k=P + 2) == 1          # int32 offsets must be 4-byte aligned
+    assert vl(max_q=101) == 1           # longer than the packed total
+    assert vl(max_q=-1) == 1
+    assert vl(total_k=-5) == 1
+    assert vl(B=0) == 1
+    assert vl(q=None) == 1
+    assert lib.attn_last_error() != b""
+
+
 def bwd(ws=P, ws_bytes=1 << 30, Hq=2, Hkv=2, d=128, dt=1, scale=0.1, dq=P):
     return lib.attn_bwd(P, P, P, P, P, P, dq, P, P, 1, Hq, Hkv, 64, d, dt, 1, ctypes.c_float(scale),
                         ws, ws_bytes, None)

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from oracle import attention as A
-from synth import bf16_bits_to_f32, f32_to_bf16_bits, make_prefill, default_scale
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, make_prefill, make_varlen, default_scale
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -335,7 +335,8 @@ def test_inputs_are_deterministic_and_upcast_exact():
 
 
 # ----------------------------------------------------------------------------- planted slips
-@pytest.mark.parametrize("slip", ["no_max_shift_in_lse", "mask_includes_diagonal", "transpose_v"])
+@pytest.mark.parametrize("slip", ["no_max_shift_in_lse", "mask_includes_diagonal", "transpose_v",
+                                  "mask_aligned_top_left"])
 def test_planted_mistakes_are_caught(monkeypatch, slip):
     """Plant a plausible mistake in the oracle (CPU only) and check that a pin fails."""
     if slip == "no_max_shift_in_lse":
@@ -360,6 +361,14 @@ def test_planted_mistakes_are_caught(monkeypatch, slip):
         monkeypatch.setattr(A, "_scores", bad)
         with pytest.raises(AssertionError):
             test_zero_query_gives_prefix_mean(True)
+    elif slip == "mask_aligned_top_left":
+        orig = A._scores
+
+        def bad(q, k, scale, causal, row_ids=None):
+            return orig(q, k, scale, causal, None)   # ignores the query positions
+        monkeypatch.setattr(A, "_scores", bad)
+        with pytest.raises(AssertionError):
+            test_chunked_prefill_equals_rows_of_full_prefill(True)
     else:
         def bad_forward(q, k, v, scale, causal):
             q, k, v = A.upcast(q), A.upcast(k), A.upcast(v)
@@ -398,3 +407,106 @@ def test_decode_per_sequence_lengths():
     ov, lv = oracle.decode(q, kc, vc, 0.4, seqlens=[L] * B)
     np.testing.assert_array_equal(of, ov)
     np.testing.assert_array_equal(lf, lv)
+
+
+# ----------------------------------------------------------------------------- Nq != Nk, packed
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunked_prefill_equals_rows_of_full_prefill(causal):
+    """Prefill in chunks: chunk [a, b) of the queries against keys [0, b) gives rows a..b-1 of the
+    (independently pinned) full forward; the last chunk against all keys likewise."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 37, 8
+    q, k, v = rnd(80, B, Hq, N, d), rnd(81, B, Hkv, N, d), rnd(82, B, Hkv, N, d)
+    of, lf = oracle.forward(q, k, v, 0.35, causal)
+    for a, b in [(0, 1), (0, 16), (16, 17), (17, 30), (30, 37), (36, 37), (0, 37)]:
+        kb = b if causal else N      # non-causal queries see every key
+        oc, lc = oracle.forward_kv(q[:, :, a:b], k[:, :, :kb], v[:, :, :kb], 0.35, causal)
+        np.testing.assert_allclose(oc, of[:, :, a:b], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lc, lf[:, :, a:b], rtol=1e-13)
+
+
+def test_single_query_forward_kv_is_decode():
+    """The last query sees every key, so one query row is decode (pinned on its own)."""
+    B, Hq, Hkv, L, d = 2, 4, 1, 29, 8
+    q, kc, vc = rnd(83, B, Hq, d), rnd(84, B, Hkv, L, d), rnd(85, B, Hkv, L, d)
+    od, ld = oracle.decode(q, kc, vc, 0.5)
+    for causal in (False, True):
+        o, lse = oracle.forward_kv(q[:, :, None, :], kc, vc, 0.5, causal)
+        np.testing.assert_allclose(o[:, :, 0], od, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, 0], ld, rtol=1e-13)
+
+
+def test_more_queries_than_keys_and_no_keys():
+    """Causal with Nk < Nq: rows i < Nq - Nk see no key (O = 0, LSE = -inf); row i >= Nq - Nk
+    sees keys 0..i-(Nq-Nk), which is the square causal forward of the last Nk queries.
+    Non-causal rows see all Nk keys.  Nk = 0 gives O = 0, LSE = -inf everywhere."""
+    B, H, Nq, Nk, d = 1, 2, 12, 5, 4
+    q, k, v = rnd(86, B, H, Nq, d), rnd(87, B, H, Nk, d), rnd(88, B, H, Nk, d)
+    o, lse = oracle.forward_kv(q, k, v, 0.7, True)
+    assert np.all(o[:, :, :Nq - Nk] == 0.0) and np.all(lse[:, :, :Nq - Nk] == -np.inf)
+    os_, ls_ = oracle.forward(q[:, :, Nq - Nk:], k, v, 0.7, True)
+    np.testing.assert_allclose(o[:, :, Nq - Nk:], os_, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[:, :, Nq - Nk:], ls_, rtol=1e-13)
+    on, ln = oracle.forward_kv(q, k, v, 0.7, False)
+    for i in range(Nq):
+        od, ld = oracle.decode(q[:, :, i], k, v, 0.7)
+        np.testing.assert_allclose(on[:, :, i], od, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ln[:, :, i], ld, rtol=1e-13)
+    for causal in (False, True):
+        oz, lz = oracle.forward_kv(q, k[:, :, :0], v[:, :, :0], 0.7, causal)
+        assert np.all(oz == 0.0) and np.all(lz == -np.inf)
+
+
+def _brute_forward_kv(q, k, v, scale, causal):
+    """Scalar loops over absolute positions: query i is token Nk - Nq + i of the sequence."""
+    Nq, d = q.shape
+    Nk = k.shape[0]
+    o = np.zeros((Nq, v.shape[1]))
+    lse = np.full(Nq, -np.inf)
+    for i in range(Nq):
+        pos = Nk - Nq + i
+        keys = [j for j in range(Nk) if not (causal and j > pos)]
+        if not keys:
+            continue
+        s = [scale * math.fsum(q[i, c] * k[j, c] for c in range(d)) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = math.fsum(e)
+        lse[i] = m + math.log(z)
+        for c in range(v.shape[1]):
+            o[i, c] = math.fsum(e[t] / z * v[j, c] for t, j in enumerate(keys))
+    return o, lse
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 6), (3, 7), (6, 6), (7, 3), (4, 0)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_kv_brute_force_tiny(Nq, Nk, causal):
+    q, k, v = rnd(90 + Nq, Nq, 3), rnd(91 + Nk, Nk, 3), rnd(92 + Nk, Nk, 3)
+    o, lse = oracle.forward_kv(q[None, None], k[None, None], v[None, None], 0.9, causal)
+    ob, lb = _brute_forward_kv(q, k, v, 0.9, causal)
+    np.testing.assert_allclose(o[0, 0], ob, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], lb, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_varlen_equals_per_sequence_and_dense(causal):
+    """Packed sequences: each one equals forward_kv on its own rows (empty ones included), and
+    a batch of equal lengths equals the dense forward with the batch folded into the rows."""
+    Hq, Hkv, d = 4, 2, 8
+    lens_q, lens_k = [5, 0, 9, 1, 3], [7, 4, 9, 0, 2]
+    x = make_varlen(lens_q, lens_k, Hq, Hkv, d, "f32", seed=93)
+    o, lse = oracle.forward_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], 0.4, causal)
+    cq, ck = x["cu_q"], x["cu_k"]
+    for b in range(len(lens_q)):
+        sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        ob, lb = oracle.forward_kv(x["q"][None, :, sq], x["k"][None, :, sk], x["v"][None, :, sk], 0.4, causal)
+        np.testing.assert_array_equal(o[:, sq], ob[0])
+        np.testing.assert_array_equal(lse[:, sq], lb[0])
+    assert np.all(lse[:, cq[3]:cq[4]] == -np.inf)  # sequence 3 has no keys
+    B, N = 3, 11
+    y = make_prefill(B, Hq, Hkv, N, d, "f32", seed=94)
+    od, ld = oracle.forward(y["q"], y["k"], y["v"], 0.4, causal)
+    fold = lambda t: np.ascontiguousarray(t.transpose(1, 0, 2, 3).reshape(t.shape[1], B * N, d))
+    cu = np.arange(0, B * N + 1, N, dtype=np.int32)
+    op, lp = oracle.forward_varlen(fold(y["q"]), fold(y["k"]), fold(y["v"]), cu, cu, 0.4, causal)
+    np.testing.assert_allclose(op, fold(od), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lp, ld.transpose(1, 0, 2).reshape(Hq, B * N), rtol=1e-13)
