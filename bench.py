@@ -252,6 +252,25 @@ def main():
                                                       lse=plse))
     f_varlen = 4.0 * d * VH * float(sum(int(n) * (int(n) + 1) // 2 for n in vl))
     del pq, pk, pv, po, plse
+    # Block-sparse: B=1, H=32, N=16384, d=128, causal; query block i keeps key blocks i-7 .. i
+    # and block 0 (128x128 blocks), i.e. a 1024-key window plus the first block.
+    SH, SN = 32, 16384
+    sp = make_prefill(1, SH, SH, SN, d, "bf16", seed=1010)
+    sq_, sk_, sv_ = (to_dev(sp[x]) for x in ("q", "k", "v"))
+    del sp
+    nbk = SN // 128
+    bi, bj = np.meshgrid(np.arange(nbk), np.arange(nbk), indexing="ij")
+    smask = ((((bi - bj) >= 0) & ((bi - bj) < 8)) | (bj == 0)).astype(np.uint8)
+    smask_dev = torch.from_numpy(smask).to(dev)
+    so = torch.empty_like(sq_)
+    slse = torch.empty((1, SH, SN), dtype=torch.float32, device=dev)
+    ms_sparse = time_call(lambda: attn.attn_fwd_blocksparse(sq_, sk_, sv_, smask_dev, True, scale, o=so, lse=slse))
+    # Kept (query, key) pairs: whole kept blocks below the diagonal, plus the causal half (with
+    # the diagonal) of each diagonal block.
+    off = int(np.sum(smask * (bi > bj)))
+    sparse_pairs = off * 128 * 128 + nbk * 128 * 129 // 2
+    f_sparse = 4.0 * d * SH * sparse_pairs
+    del sq_, sk_, sv_, so, slse
 
     f_fwd = flops_fwd(B, H, N, d, True)
     f_bwd = 2.5 * f_fwd
@@ -304,6 +323,10 @@ def main():
                           "lengths": "uniform in [L/2, L], seed 1006, mean %.0f" % float(vlens.mean())},
         "fwd_chunk": {"TFLOPs": f_chunk / (ms_chunk * 1e-3) / 1e12, "ms": ms_chunk,
                       "workload": "attn_fwd_kv B=4 Hq=32 Hkv=8 Nq=1024 Nk=8192 d=128 causal (bottom right)"},
+        "fwd_blocksparse": {"TFLOPs": f_sparse / (ms_sparse * 1e-3) / 1e12, "ms": ms_sparse,
+                            "workload": "attn_fwd_blocksparse B=1 H=32 N=16384 d=128 causal, 128x128 blocks: "
+                                        "8-block band + first block (%.1f%% of causal pairs kept)"
+                                        % (100.0 * sparse_pairs / (SN * (SN + 1) / 2))},
         "fwd_varlen": {"TFLOPs": f_varlen / (ms_varlen * 1e-3) / 1e12, "ms": ms_varlen,
                        "workload": "attn_fwd_varlen 12 packed sequences, lengths uniform in [256, 4096] "
                                    "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},

@@ -20,6 +20,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTS = (
     "attn_abi_version", "attn_status_str", "attn_last_error", "attn_fwd", "attn_fwd_kv", "attn_fwd_varlen",
+    "attn_fwd_blocksparse",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_auto_splits",
     "attn_decode_workspace_bytes", "attn_decode", "attn_decode_varlen",
 )
@@ -53,6 +54,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.attn_fwd_kv.restype = i
     lib.attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_blocksparse.restype = i
+    lib.attn_fwd_blocksparse.argtypes = [vp] * 6 + [ctypes.c_longlong, ctypes.c_longlong] + [i] * 8 + [f, vp]
     lib.attn_fwd_varlen.restype = i
     lib.attn_fwd_varlen.argtypes = [vp] * 7 + [i, i, i, i, i, i, i, i, i, f, vp]
     lib.attn_bwd_workspace_bytes.restype = sz
@@ -136,6 +139,43 @@ def attn_fwd_kv(q, k, v, causal: bool, scale: float, o=None, lse=None, want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     _check(lib.attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, _dtype_code(q),
                            int(bool(causal)), float(scale), _stream(stream)))
+    return o, lse
+
+
+SPARSE_BLOCK = 128
+
+
+def attn_fwd_blocksparse(q, k, v, block_mask, causal: bool, scale: float, o=None, lse=None, want_lse: bool = True,
+                         stream=None):
+    """attn_fwd_kv restricted to the 128x128 (query block, key block) pairs block_mask keeps.
+    block_mask: uint8 CUDA tensor [B, Hq, nqb, nkb], [Hq, nqb, nkb] or [nqb, nkb] (shared over
+    the missing leading dims), nqb = ceil(Nq/128), nkb = ceil(Nk/128); the last two dims dense."""
+    import torch
+    lib = load()
+    _require(q.is_cuda and q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D CUDA tensors")
+    _require(all(t.is_contiguous() for t in (q, k, v)), "q, k, v must be contiguous")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _require(tuple(k.shape) == (B, Hkv, Nk, d) and tuple(v.shape) == (B, Hkv, Nk, d), "k/v shape mismatch")
+    nqb, nkb = -(-Nq // SPARSE_BLOCK), -(-Nk // SPARSE_BLOCK)
+    m = block_mask
+    _require(m.is_cuda and m.dtype == torch.uint8 and 2 <= m.dim() <= 4, "block_mask must be a uint8 CUDA tensor")
+    _require(tuple(m.shape[-2:]) == (nqb, nkb), f"block_mask must end in [{nqb}, {nkb}]")
+    _require(m.stride(-1) == 1 and m.stride(-2) == nkb, "block_mask rows must be dense")
+    sb = m.stride(0) if m.dim() == 4 else 0
+    sh = m.stride(-3) if m.dim() >= 3 else 0
+    if m.dim() == 4:
+        _require(m.shape[0] in (1, B), "block_mask batch dim must be 1 or B")
+        sb = 0 if m.shape[0] == 1 else sb
+    if m.dim() >= 3:
+        _require(m.shape[-3] in (1, Hq), "block_mask head dim must be 1 or Hq")
+        sh = 0 if m.shape[-3] == 1 else sh
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(m), sb, sh, B, Hq, Hkv, Nq,
+                                    Nk, d, _dtype_code(q), int(bool(causal)), float(scale), _stream(stream)))
     return o, lse
 
 

@@ -113,7 +113,9 @@ const char* attn_last_error(void) { return g_err; }
 // rows per head, or packed variable-length with totals Nq, Nk and longest query run max_q.
 static attn_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q,
                               const int* cu_k, int B, int Hq, int Hkv, int Nq, int Nk, int max_q, int d,
-                              attn_dtype_t dtype, int causal, float scale, void* stream) {
+                              attn_dtype_t dtype, int causal, float scale, void* stream,
+                              const unsigned char* block_mask = nullptr, long long mask_sb = 0,
+                              long long mask_sh = 0) {
   if ((Nq > 0 && (!q || !o)) || (Nk > 0 && (!k || !v)))
     return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null (k and v may be null when there are no keys)");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
@@ -136,7 +138,7 @@ static attn_status_t fwd_impl(const void* q, const void* k, const void* v, void*
     return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   }
   xattn::FwdArgs a{q, k, v, o, lse, cu_q, cu_k, B, Hq, Hkv, Nq, Nk, max_q, d, dtype == ATTN_BF16 ? 1 : 0,
-                   causal ? 1 : 0, scale, (hipStream_t)stream};
+                   causal ? 1 : 0, scale, (hipStream_t)stream, block_mask, mask_sb, mask_sh};
   return from_hip(xattn::launch_fwd(a), "attn_fwd launch");
 }
 
@@ -151,6 +153,21 @@ attn_status_t attn_fwd_kv(const void* q, const void* k, const void* v, void* o, 
                           void* stream) {
   if (Nq <= 0 || Nk < 0) return fail(ATTN_ERR_INVALID_ARG, "need Nq > 0 and Nk >= 0 (got Nq=%d Nk=%d)", Nq, Nk);
   return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, Nq, d, dtype, causal, scale, stream);
+}
+
+attn_status_t attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const unsigned char* block_mask, long long mask_stride_b,
+                                   long long mask_stride_h, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                   attn_dtype_t dtype, int causal, float scale, void* stream) {
+  if (!block_mask) return fail(ATTN_ERR_INVALID_ARG, "block_mask must be non-null");
+  if (mask_stride_b < 0 || mask_stride_h < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "mask strides must be >= 0 (got %lld, %lld)", mask_stride_b, mask_stride_h);
+  if (Nq <= 0 || Nk < 0) return fail(ATTN_ERR_INVALID_ARG, "need Nq > 0 and Nk >= 0 (got Nq=%d Nk=%d)", Nq, Nk);
+  if (dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "block-sparse forward supports bf16 only");
+  if (Nk > xattn::kMaxSparseKeys)
+    return fail(ATTN_ERR_UNSUPPORTED, "block-sparse forward supports Nk <= %d (got %d)", xattn::kMaxSparseKeys, Nk);
+  return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, Nq, d, dtype, causal, scale, stream,
+                  block_mask, mask_stride_b, mask_stride_h);
 }
 
 attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -263,6 +263,47 @@ __device__ __forceinline__ SeqRows seq_rows(const SeqGeo& g, int b, int hq, int 
   return r;
 }
 
+// Block-sparse mask: byte (b, h, i, j) at mask[b*sb + h*sh + i*nkb + j] keeps (non-zero) or
+// drops (zero) every score of query block i (rows 128i .. 128i+127) against key block j
+// (keys 128j .. 128j+127).  Strides of 0 share one mask across batches or heads.
+constexpr int kSparseBlock = 128;
+constexpr int kMaxSparseTiles = 8192;  // 64-key tiles a workgroup can list (kMaxSparseKeys / 64)
+struct BlockMask {
+  const unsigned char* mask;  // nullptr: dense
+  long long sb, sh;
+  int nqb, nkb;
+};
+
+// Lists, in key order, the 64-key tiles t < T that some query block of a workgroup's QB
+// blocks (starting at block qb0) keeps: entry = t | (keep bits of the QB blocks) << 14.
+// Wave 0 compacts 64 tiles per ballot; returns the count to every thread (one barrier).
+template <int QB>
+__device__ __forceinline__ int build_tile_list(const BlockMask& bm, int b, int h, int qb0, int T, uint16_t* list,
+                                               int* count) {
+  static_assert(QB >= 1 && QB <= 2, "two keep bits per entry");
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    const unsigned char* rows = bm.mask + b * bm.sb + h * bm.sh;
+    int n = 0;
+    for (int t0 = 0; t0 < T; t0 += 64) {
+      const int t = t0 + lane;
+      uint32_t keep = 0;
+      if (t < T) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+          if (qb0 + i < bm.nqb && rows[(size_t)(qb0 + i) * bm.nkb + (t >> 1)] != 0) keep |= 1u << i;
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep != 0);
+      const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (keep != 0) list[pos] = (uint16_t)(t | (keep << 14));
+      n += __builtin_popcountll(bal);
+    }
+    if (lane == 0) *count = n;
+  }
+  __syncthreads();
+  return *count;
+}
+
 // Initial running max of the forward kernels: the most negative finite float rather than
 // -inf, so that 2^(s - m) of a masked score (s = -inf) is 0 even for a row that has seen
 // no key yet, and a row without any key ends with l = 0 (O = 0, LSE = -inf).

@@ -57,6 +57,7 @@
 namespace xattn {
 
 constexpr int kFwdBN = 64;  // keys per tile
+static_assert(kMaxSparseTiles * kFwdBN == kMaxSparseKeys, "block-sparse tile list size");
 constexpr float kLazy = 8.f; // log2 of the largest un-normalised probability allowed
 
 template <int D>
@@ -74,11 +75,11 @@ __device__ __forceinline__ void fwd_tile_of(int id, int BH, int n_qtiles, bool c
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
-template <int D, int NQ, int NW, int WPE, bool CAUSAL>
+template <int D, int NQ, int NW, int WPE, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, float scale_log2,
-    int n_qtiles, int BH) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask bm,
+    float scale_log2, int n_qtiles, int BH) {
   constexpr int BM = NW * NQ * 32;
   constexpr int BN = kFwdBN;
   constexpr int KB = BN / 32;             // 32-key blocks per tile
@@ -89,6 +90,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split evenly over the workgroup");
   using Lds = FwdLds<D>;
   __shared__ __attribute__((aligned(16))) char smem[Lds::TOTAL];
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];  // kept key tiles (block-sparse)
+  __shared__ int tcount;
+  static_assert(!SPARSE || BM % kSparseBlock == 0, "query tile must cover whole mask blocks");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,7 +141,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   for (int qb = 0; qb < NQ; ++qb) { m_run[qb] = kMaxInit; l_run[qb] = 0.f; }
 
   const int kv_end = CAUSAL ? min(Nk, q0 + BM + (Nk - Nq)) : Nk;
-  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // Block-sparse: walk only the tiles one of the workgroup's query blocks keeps; walk position
+  // t holds key tile kt(t) and the wave skips tiles its own block drops.  Dense: kt(t) = t.
+  if constexpr (SPARSE)
+    ntiles = build_tile_list<SPARSE ? BM / kSparseBlock : 1>(bm, b, hq, q0 / kSparseBlock, ntiles, tlist, &tcount);
+  auto entry = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tlist[t]);
+    else return t;
+  };
+  auto ktile = [&](int e) __attribute__((always_inline)) -> int { return SPARSE ? (e & 0x3fff) : e; };
 
   u32x4 pk[CPT], pv[CPT];
   auto load_tile = [&](int t) {
@@ -170,17 +183,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
   };
 
-  load_tile(0);
+  load_tile(ntiles > 0 ? ktile(entry(0)) : 0);
   store_tile(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const int t0 = t * BN;
+    if (t + 1 < ntiles) load_tile(ktile(entry(t + 1)));
+    const int e = entry(t);
+    const int t0 = ktile(e) * BN;
     const char* ks = smem + (t & 1) * Lds::STAGE;
     const char* vs = ks + Lds::KBYTES;
-    // A wave whose queries all precede this tile has nothing to add (causal skip).
-    const bool active = !CAUSAL || (t0 <= qd0 + NQ * 32 - 1);
+    // A wave whose queries all precede this tile has nothing to add (causal skip), nor one whose
+    // query block drops it.
+    const bool keep = !SPARSE || ((e >> (14 + (qw0 - q0) / kSparseBlock)) & 1) != 0;
+    const bool active = keep && (!CAUSAL || (t0 <= qd0 + NQ * 32 - 1));
     if (active) {
       f32x16 s[KB][NQ];
 #pragma unroll
@@ -376,17 +392,19 @@ struct IlvShape {
   static constexpr int NQK = DC;                   // K operands per 32-key block
 };
 
-template <int D, int RB_, bool CAUSAL>
+template <int D, int RB_, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 / RB_, 2 / RB_))) void fwd_ilv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, float scale_log2,
-    int n_qtiles, int BH) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask bm,
+    float scale_log2, int n_qtiles, int BH) {
   using S = IlvShape<D, RB_>;
   constexpr int BN = S::BN, DC = S::DC, DB = S::DB, RB = S::RB, NS = S::NS, NW = S::NW;
   constexpr int TILE = S::TILE, CPW = S::CPW, RPC = S::RPC, NPV = S::NPV, NQK = S::NQK;
   constexpr int NOPS = NPV + NQK, NMF = RB * NOPS, L = XATTN_ILV_LOOKAHEAD;
   static_assert(NS == 4 && CPW <= 4, "copy schedule");
   __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];  // [K ring | V ring]
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];             // kept key tiles
+  __shared__ int tcount;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
@@ -456,11 +474,18 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
   };
 
   const int kv_end = CAUSAL ? min(Nk, q0 + S::BM + (Nk - Nq)) : Nk;
-  const int T = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-  if (T == 0) {  // no key for any row of the tile (empty key sequence, or causal with Nk < Nq)
-    epilogue();
+  int T = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // Block-sparse: the workgroup walks only the tiles that one of its query blocks keeps; tile
+  // position i of the walk holds key tile kt(i).  Dense: kt(i) = i.
+  if constexpr (SPARSE) T = build_tile_list<S::BM / kSparseBlock>(bm, b, hq, q0 / kSparseBlock, T, tlist, &tcount);
+  if (T == 0) {  // no key for any row of the tile (empty key sequence, causal with Nk < Nq, or
+    epilogue();  // every block dropped)
     return;
   }
+  auto entry = [&](int i) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_readfirstlane((int)tlist[min(i, T - 1)]);
+  };
+  const int wblk = (qw0 - q0) / kSparseBlock;  // the wave's query block within the workgroup
   TileOffsets<D> ofs;
   ofs.init(lane);
 
@@ -482,8 +507,8 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
   const void* vbase = wave_uniform(vp);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const uint32_t wdst = lds0 + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (CPW * 1024);
-  auto copy = [&](int tile, bool is_k, int i) __attribute__((always_inline)) {
-    const int row = min(tile * BN + RPC * (wave * CPW + i) + lrow, Nk - 1);
+  auto copy = [&](int tile, int ktile, bool is_k, int i) __attribute__((always_inline)) {
+    const int row = min(ktile * BN + RPC * (wave * CPW + i) + lrow, Nk - 1);
     const uint32_t m0v = wdst + (is_k ? 0 : NS * TILE) + (tile & (NS - 1)) * TILE + 1024 * i;
     dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff[i] - lrow * (2 * D)), m0v);
   };
@@ -506,16 +531,23 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
     }
   };
   // A wave has work in step u while key block u-1 still holds keys at or before its last row.
-  auto active = [&](int u) __attribute__((always_inline)) { return !CAUSAL || (u - 1) * 32 <= qd0 + RB * 32 - 1; };
+  // (Block-sparse: always; dropped and masked blocks give probability 0.)
+  auto active = [&](int u) __attribute__((always_inline)) {
+    return SPARSE || !CAUSAL || (u - 1) * 32 <= qd0 + RB * 32 - 1;
+  };
+  auto kt = [&](int i) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return entry(i) & 0x3fff;
+    else return i;
+  };
 
   // Prologue: K_0, K_1, K_2, V_0, V_1; V stage 3 (read as block -1, with P_{-1} = 0) is zeroed.
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    copy(0, true, i);
-    if (1 < T) copy(1, true, i);
-    if (2 < T) copy(2, true, i);
-    copy(0, false, i);
-    if (1 < T) copy(1, false, i);
+    copy(0, kt(0), true, i);
+    if (1 < T) copy(1, kt(1), true, i);
+    if (2 < T) copy(2, kt(2), true, i);
+    copy(0, kt(0), false, i);
+    if (1 < T) copy(1, kt(1), false, i);
   }
   for (int i = tid; i < TILE / 16; i += NW * 64)
     *reinterpret_cast<u32x4*>(smem + NS * TILE + (NS - 1) * TILE + 16 * i) = u32x4{0u, 0u, 0u, 0u};
@@ -556,20 +588,23 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
   // Step u: sc = S_u (complete), sn <- S_{u+1}, pp = P_{u-1}, pc <- P_u; copies of the
   // step's half of the tile's copy list (K_{t+3} on even steps, V_{t+2} on odd ones).  Tiles
   // past the end are copied too, clamped to the last key, into stages nobody reads any more, so
-  // every step issues the same copies and the wait counts stay fixed.
+  // every step issues the same copies and the wait counts stay fixed.  ctile is the walk
+  // position of the copied tile (its ring stage), ckt its key tile; kcur is the key tile of
+  // S_u and keep whether the wave's query block keeps it (block-sparse).
   auto step = [&](int u, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2], u32x4(&pc)[RB][2],
-                  int ctile, bool cis_k) __attribute__((always_inline)) {
+                  int ctile, int ckt, bool cis_k, int kcur, bool keep) __attribute__((always_inline)) {
     if (active(u)) {
       if constexpr (RB > 1 && XATTN_ILV_QKASM != 0) qk_result_fence();  // S_u came from asm MFMAs
-      const int u0 = u * 32;
-      if ((u0 + 32 > Nk) || (CAUSAL && u0 + 31 > qd0)) {
+      const int u0 = kcur * BN + (u & 1) * 32;  // first key of S_u
+      const bool drop = SPARSE && !keep;
+      if (drop || (u0 + 32 > Nk) || (CAUSAL && u0 + 31 > qd0)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int kmax = qd0 + 32 * rb + l32;  // last key of this lane's row
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = u0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            if (kj >= Nk || (CAUSAL && kj > kmax)) sc[rb][r] = -INFINITY;
+            if (drop || kj >= Nk || (CAUSAL && kj > kmax)) sc[rb][r] = -INFINITY;
           }
         }
       }
@@ -651,7 +686,7 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
             pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
           }
         });
-        if constexpr (i % 8 == XATTN_ILV_COPY_SLOT && i / 8 < CPW) copy(ctile, cis_k, i / 8);
+        if constexpr (i % 8 == XATTN_ILV_COPY_SLOT && i / 8 < CPW) copy(ctile, ckt, cis_k, i / 8);
         sched_fence();
       });
       if (XATTN_ILV_PRIO) __builtin_amdgcn_s_setprio(0);
@@ -720,13 +755,19 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
       for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
     } else {
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) copy(ctile, cis_k, i);
+      for (int i = 0; i < CPW; ++i) copy(ctile, ckt, cis_k, i);
     }
   };
 
   for (int t = 0; t < T; ++t) {
-    step(2 * t, sA, sB, pA, pB, t + 3, true);
-    step(2 * t + 1, sB, sA, pB, pA, t + 2, false);
+    int kc = t, keep = 1;
+    if constexpr (SPARSE) {
+      const int e = entry(t);
+      kc = e & 0x3fff;
+      keep = (e >> (14 + wblk)) & 1;
+    }
+    step(2 * t, sA, sB, pA, pB, t + 3, kt(t + 3), true, kc, keep != 0);
+    step(2 * t + 1, sB, sA, pB, pA, t + 2, kt(t + 2), false, kc, keep != 0);
     // K_{t+2} and V_{t+1} (copied in tile t-1) must have landed; this tile's copies may stay
     // in flight.
     wait_vmem_n<2 * CPW>();
@@ -753,8 +794,8 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, float scale_log2,
-    int n_qtiles, int BH) {
+    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask /*dense only*/,
+    float scale_log2, int n_qtiles, int BH) {
   constexpr int D = 64, BM = 128, BN = 32, P = D + 1;  // P: padded pitch in floats
   __shared__ float ks[BN * P];
   __shared__ float vs[BN * P];
@@ -838,7 +879,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // Grid: one workgroup per (query tile, batch, head); query tiles cover the longest query
 // sequence and those past a shorter sequence's end exit at once.
 template <typename T>
-using FwdKernel = void (*)(const T*, const T*, const T*, T*, float*, int, int, SeqGeo, float, int, int);
+using FwdKernel = void (*)(const T*, const T*, const T*, T*, float*, int, int, SeqGeo, BlockMask, float, int, int);
 
 template <typename T>
 static hipError_t launch_fwd_grid(FwdKernel<T> kern, int BM, int threads, const FwdArgs& a) {
@@ -846,29 +887,34 @@ static hipError_t launch_fwd_grid(FwdKernel<T> kern, int BM, int threads, const 
   const int BH = a.B * a.Hq;
   if (n_qtiles == 0) return hipSuccess;  // every query sequence is empty
   const SeqGeo geo{a.cu_q, a.cu_k, a.Nq, a.Nk};
+  const BlockMask bm{a.block_mask, a.mask_sb, a.mask_sh, (a.Nq + kSparseBlock - 1) / kSparseBlock,
+                     (a.Nk + kSparseBlock - 1) / kSparseBlock};
   hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(threads), 0, a.stream, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, geo, a.scale * kLog2e, n_qtiles, BH);
+                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, geo, bm, a.scale * kLog2e, n_qtiles, BH);
   return hipGetLastError();
 }
 
+// Picks the <causal, sparse> instantiation of a kernel template.
+#define XATTN_PICK(K, ...)                                                                           \
+  (a.block_mask ? (a.causal ? K<__VA_ARGS__, true, true> : K<__VA_ARGS__, false, true>)              \
+                : (a.causal ? K<__VA_ARGS__, true, false> : K<__VA_ARGS__, false, false>))
+
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.dtype == 0)  // fp32, d = 64
+  if (a.dtype == 0)  // fp32, d = 64 (dense only)
     return launch_fwd_grid<float>(a.causal ? fwd_f32_kernel<true> : fwd_f32_kernel<false>, 128, 256, a);
 #if XATTN_FWD_ILV
   if (a.d == 128) {
     using S = IlvShape<128, XATTN_ILV_RB>;
-    return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, XATTN_ILV_RB, true> : fwd_ilv_kernel<128, XATTN_ILV_RB, false>,
-                           S::BM, S::NW * 64, a);
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, XATTN_ILV_RB), S::BM, S::NW * 64, a);
   }
 #endif
   if (a.d == 128) {
     constexpr int NQ = XATTN_FWD128_NQ, NW = XATTN_FWD128_NW, WPE = XATTN_FWD128_WPE;
-    return launch_fwd_grid<uint16_t>(a.causal ? fwd_bf16_kernel<128, NQ, NW, WPE, true> : fwd_bf16_kernel<128, NQ, NW, WPE, false>,
-                           NW * NQ * 32, NW * 64, a);
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_bf16_kernel, 128, NQ, NW, WPE), NW * NQ * 32, NW * 64, a);
   }
   constexpr int NQ = XATTN_FWD64_NQ, NW = XATTN_FWD64_NW, WPE = XATTN_FWD64_WPE;
-  return launch_fwd_grid<uint16_t>(a.causal ? fwd_bf16_kernel<64, NQ, NW, WPE, true> : fwd_bf16_kernel<64, NQ, NW, WPE, false>,
-                         NW * NQ * 32, NW * 64, a);
+  return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_bf16_kernel, 64, NQ, NW, WPE), NW * NQ * 32, NW * 64, a);
 }
+#undef XATTN_PICK
 
 }  // namespace xattn

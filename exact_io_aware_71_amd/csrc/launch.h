@@ -17,6 +17,8 @@ struct FwdArgs {
   int B, Hq, Hkv, Nq, Nk, max_q, d, dtype, causal;
   float scale;
   hipStream_t stream;
+  const unsigned char* block_mask;  // optional [B, Hq, ceil(Nq/128), ceil(Nk/128)] keep bytes (dense layout only)
+  long long mask_sb, mask_sh;       // batch and head strides of block_mask in bytes
 };
 
 struct BwdArgs {
@@ -40,6 +42,9 @@ struct DecodeArgs {
   hipStream_t stream;
   const int* seqlens;   // [B] keys per sequence (device), clamped to [0, L]; null = L for all
 };
+
+// Longest key sequence the block-sparse forward walks (its tile list holds 8192 tiles of 64).
+constexpr int kMaxSparseKeys = 8192 * 64;
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);

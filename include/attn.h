@@ -94,6 +94,26 @@ attn_status_t attn_fwd_kv(const void* q, const void* k, const void* v, void* o, 
                           int causal, float scale, void* stream);
 
 /*
+ * Block-sparse forward: attn_fwd_kv restricted to the (query block, key block) pairs a mask
+ * keeps, exact for that pattern ([OPT] §7.2 names block sparsity; here no weight is dropped
+ * that the mask keeps).  Blocks are 128 query rows by 128 keys:
+ *   block_mask  uint8 device array; byte (b, h, i, j) at
+ *               block_mask[b*mask_stride_b + h*mask_stride_h + i*ceil(Nk/128) + j]
+ *               keeps (non-zero) or drops (zero) the scores of query rows 128i .. 128i+127
+ *               against keys 128j .. 128j+127, for i < ceil(Nq/128), j < ceil(Nk/128);
+ *               strides in bytes, >= 0 (0 shares one [ceil(Nq/128), ceil(Nk/128)] mask)
+ *   causal      applied on top of the mask, aligned at the bottom right as in attn_fwd_kv
+ * Score (i, j) enters the softmax iff its block is kept (and j <= i + Nk - Nq when causal); a
+ * row that keeps no key gets o = 0 and lse = -inf.  Dropped blocks are neither loaded nor
+ * multiplied where a whole workgroup (256 query rows at d = 128, 128 at d = 64) drops them.
+ * Supported: BF16, d in {64, 128}, Nk <= 524288.  Other arguments as attn_fwd_kv.
+ */
+attn_status_t attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const unsigned char* block_mask, long long mask_stride_b,
+                                   long long mask_stride_h, int B, int Hq, int Hkv, int Nq, int Nk,
+                                   int d, attn_dtype_t dtype, int causal, float scale, void* stream);
+
+/*
  * Forward attention over a batch of sequences of different lengths with no padding ([NOTE]
  * Method, implementation details: each sequence is processed at its true length).  The tensors are packed: the batch
  * is folded into the row axis of each head.

@@ -22,14 +22,16 @@ The backward is the textbook softmax gradient (the pages only say that it recomp
 Grouped-query attention maps query head h to KV head h // (Hq / Hkv) ([OPT] §5.3).
 Decode is the same definition with a single query row against a KV cache ([OPT] §4.2.2,
 [FUND] §2.3.1); forward_kv takes Nq query rows against Nk keys (the causal mask aligned at
-the bottom right) and forward_varlen a packed batch of sequences of different lengths.  Every function is pinned by tests against closed forms, invariants,
+the bottom right), forward_blocksparse the same under a block keep-mask, and forward_varlen
+a packed batch of sequences of different lengths.  Every function is pinned by tests against closed forms, invariants,
 brute-force scalar loops and hand-derived fixtures; none is "parity unpinned".
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["upcast", "probabilities", "forward", "forward_kv", "forward_varlen", "forward_rows", "backward",
+__all__ = ["upcast", "probabilities", "forward", "forward_kv", "forward_blocksparse", "forward_varlen", "forward_rows",
+           "backward",
            "decode", "split_kv_decode", "lse_merge", "attention_flops"]
 
 
@@ -125,6 +127,36 @@ def forward_kv(q, k, v, scale: float, causal: bool):
         for h in range(Hq):
             kv = _kv_head(h, Hq, Hkv)
             p, lse[b, h] = _softmax_rows(_scores(q[b, h], k[b, kv], scale, causal, row_ids=pos))
+            o[b, h] = p @ v[b, kv]
+    return o, lse
+
+
+def forward_blocksparse(q, k, v, block_mask, scale: float, causal: bool, block: int = 128):
+    """forward_kv restricted to the (query block, key block) pairs a mask keeps.
+
+    [OPT] §7.2 names block sparsity.  Reading: with a given block pattern the result is exact
+    attention under the element mask that pattern expands to; score (i, j) takes part iff
+    block_mask[.., i // block, j // block] is non-zero (and j <= i + Nk - Nq when causal).
+    block_mask broadcasts against [B, Hq, ceil(Nq/block), ceil(Nk/block)].  Rows that keep no
+    key get O = 0 and LSE = -inf.
+    """
+    q, k, v = upcast(q), upcast(k), upcast(v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    nqb, nkb = -(-Nq // block), -(-Nk // block)
+    mask = np.broadcast_to(np.asarray(block_mask) != 0, (B, Hq, nqb, nkb))
+    o = np.zeros((B, Hq, Nq, dv))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    if Nk == 0:
+        return o, lse
+    pos = np.arange(Nq) + (Nk - Nq)
+    qi, kj = np.arange(Nq) // block, np.arange(Nk) // block
+    for b in range(B):
+        for h in range(Hq):
+            kv = _kv_head(h, Hq, Hkv)
+            s = _scores(q[b, h], k[b, kv], scale, causal, row_ids=pos)
+            s = np.where(mask[b, h][qi[:, None], kj[None, :]], s, -np.inf)
+            p, lse[b, h] = _softmax_rows(s)
             o[b, h] = p @ v[b, kv]
     return o, lse
 

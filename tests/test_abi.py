@@ -79,6 +79,19 @@ def test_fwd_kv_and_varlen_validation():
     assert lib.attn_last_error() != b""
 
 
+def test_fwd_blocksparse_validation():
+    def bs(mask=P, sb=0, sh=0, Nq=256, Nk=256, dt=1, d=128):
+        return lib.attn_fwd_blocksparse(P, P, P, P, P, mask, sb, sh, 1, 2, 2, Nq, Nk, d, dt, 1, ctypes.c_float(0.1),
+                                        None)
+    assert bs(mask=None) == 1
+    assert bs(sb=-1) == 1
+    assert bs(sh=-4) == 1
+    assert bs(Nq=0) == 1
+    assert bs(dt=0, d=64) == 2           # fp32 is dense only
+    assert bs(Nk=524288 + 64) == 2       # beyond the tile list
+    assert bs(d=96) == 2
+
+
 def bwd(ws=P, ws_bytes=1 << 30, Hq=2, Hkv=2, d=128, dt=1, scale=0.1, dq=P):
     return lib.attn_bwd(P, P, P, P, P, P, dq, P, P, 1, Hq, Hkv, 64, d, dt, 1, ctypes.c_float(scale),
                         ws, ws_bytes, None)

@@ -336,7 +336,7 @@ def test_inputs_are_deterministic_and_upcast_exact():
 
 # ----------------------------------------------------------------------------- planted slips
 @pytest.mark.parametrize("slip", ["no_max_shift_in_lse", "mask_includes_diagonal", "transpose_v",
-                                  "mask_aligned_top_left"])
+                                  "mask_aligned_top_left", "block_index_off_by_one"])
 def test_planted_mistakes_are_caught(monkeypatch, slip):
     """Plant a plausible mistake in the oracle (CPU only) and check that a pin fails."""
     if slip == "no_max_shift_in_lse":
@@ -361,6 +361,14 @@ def test_planted_mistakes_are_caught(monkeypatch, slip):
         monkeypatch.setattr(A, "_scores", bad)
         with pytest.raises(AssertionError):
             test_zero_query_gives_prefix_mean(True)
+    elif slip == "block_index_off_by_one":
+        orig = A.forward_blocksparse
+
+        def bad(q, k, v, block_mask, scale, causal, block=128):   # key j read from block j//block - 1
+            return orig(q, k, v, np.roll(np.asarray(block_mask), 1, axis=-1), scale, causal, block)
+        monkeypatch.setattr(oracle, "forward_blocksparse", bad)
+        with pytest.raises(AssertionError):
+            test_blocksparse_equals_gathered_keys()
     elif slip == "mask_aligned_top_left":
         orig = A._scores
 
@@ -510,3 +518,81 @@ def test_packed_varlen_equals_per_sequence_and_dense(causal):
     op, lp = oracle.forward_varlen(fold(y["q"]), fold(y["k"]), fold(y["v"]), cu, cu, 0.4, causal)
     np.testing.assert_allclose(op, fold(od), rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(lp, ld.transpose(1, 0, 2).reshape(Hq, B * N), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- block-sparse
+def test_blocksparse_full_mask_is_forward_kv():
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 1, 11, 19, 4
+    q, k, v = rnd(100, B, Hq, Nq, d), rnd(101, B, Hkv, Nk, d), rnd(102, B, Hkv, Nk, d)
+    for causal in (False, True):
+        o, lse = oracle.forward_blocksparse(q, k, v, np.ones((3, 5)), 0.6, causal, block=4)
+        ok, lk = oracle.forward_kv(q, k, v, 0.6, causal)
+        np.testing.assert_array_equal(o, ok)
+        np.testing.assert_array_equal(lse, lk)
+
+
+def test_blocksparse_block_diagonal_is_separate_sequences():
+    """A block-diagonal mask makes every block an independent sequence: the packed forward
+    (independently pinned) over sequences of one block each."""
+    Hq, Hkv, blk, nb, d = 2, 2, 5, 4, 6
+    lens = [blk] * (nb - 1) + [3]                      # ragged last block
+    x = make_varlen(lens, lens, Hq, Hkv, d, "f32", seed=103)
+    n = sum(lens)
+    for causal in (False, True):
+        o, lse = oracle.forward_blocksparse(x["q"][None], x["k"][None], x["v"][None], np.eye(nb), 0.5, causal,
+                                            block=blk)
+        ov, lv = oracle.forward_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], 0.5, causal)
+        np.testing.assert_allclose(o[0], ov, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[0], lv, rtol=1e-13)
+        assert o.shape[2] == n
+
+
+def test_blocksparse_lower_blocks_with_causal_is_causal_forward():
+    B, H, N, d, blk = 1, 2, 23, 4, 4
+    q, k, v = rnd(104, B, H, N, d), rnd(105, B, H, N, d), rnd(106, B, H, N, d)
+    nb = -(-N // blk)
+    lower = np.tril(np.ones((nb, nb)))
+    o, lse = oracle.forward_blocksparse(q, k, v, lower, 0.5, True, block=blk)
+    of, lf = oracle.forward(q, k, v, 0.5, True)
+    np.testing.assert_allclose(o, of, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lf, rtol=1e-13)
+
+
+def test_blocksparse_equals_gathered_keys():
+    """Without causal, query block i attends to exactly the keys of its kept blocks: the same as
+    decode (pinned on its own) of each row against those keys gathered; an empty row of blocks
+    gives O = 0, LSE = -inf."""
+    B, Hq, Hkv, Nq, Nk, d, blk = 1, 2, 2, 10, 14, 3, 4
+    q, k, v = rnd(107, B, Hq, Nq, d), rnd(108, B, Hkv, Nk, d), rnd(109, B, Hkv, Nk, d)
+    mask = np.array([[1, 0, 0, 1], [0, 1, 1, 0], [0, 0, 0, 0]])   # [ceil(10/4), ceil(14/4)]
+    o, lse = oracle.forward_blocksparse(q, k, v, mask, 0.7, False, block=blk)
+    for i in range(Nq):
+        keys = np.concatenate([np.arange(j * blk, min((j + 1) * blk, Nk)) for j in range(4) if mask[i // blk, j]]
+                              + [np.zeros(0, dtype=int)]).astype(int)
+        if keys.size == 0:
+            assert np.all(o[:, :, i] == 0.0) and np.all(lse[:, :, i] == -np.inf)
+            continue
+        od, ld = oracle.decode(q[:, :, i], k[:, :, keys], v[:, :, keys], 0.7)
+        np.testing.assert_allclose(o[:, :, i], od, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, i], ld, rtol=1e-13)
+
+
+def test_blocksparse_brute_force_tiny():
+    """Scalar loops over the element mask the blocks expand to, causal aligned at the bottom right."""
+    Nq, Nk, d, blk = 5, 7, 2, 2
+    q, k, v = rnd(110, Nq, d), rnd(111, Nk, d), rnd(112, Nk, d)
+    mask = np.array([[1, 0, 1, 1], [0, 0, 1, 0], [1, 1, 0, 1]])
+    for causal in (False, True):
+        o, lse = oracle.forward_blocksparse(q[None, None], k[None, None], v[None, None], mask, 0.8, causal, block=blk)
+        for i in range(Nq):
+            keys = [j for j in range(Nk) if mask[i // blk, j // blk] and not (causal and j > i + Nk - Nq)]
+            if not keys:
+                assert o[0, 0, i].tolist() == [0.0, 0.0] and lse[0, 0, i] == -np.inf
+                continue
+            s = [0.8 * math.fsum(q[i, c] * k[j, c] for c in range(d)) for j in keys]
+            m = max(s)
+            z = math.fsum(math.exp(x - m) for x in s)
+            assert abs(lse[0, 0, i] - (m + math.log(z))) <= 1e-13
+            for c in range(d):
+                ref = math.fsum(math.exp(s[t] - m) / z * v[j, c] for t, j in enumerate(keys))
+                assert abs(o[0, 0, i, c] - ref) <= 1e-13
