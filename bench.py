@@ -242,8 +242,8 @@ def main():
     # Packed batch: 12 sequences, lengths uniform in [256, 4096] (seed 1008), H=16, d=128, causal.
     vl = np.random.default_rng(1008).integers(256, 4097, 12)
     VH = 16
-    px = make_varlen(vl, vl, VH, VH, d, "bf16", seed=1009)
-    pq, pk, pv = (to_dev(px[x]) for x in ("q", "k", "v"))
+    px = make_varlen(vl, vl, VH, VH, d, "bf16", seed=1009, with_dout=True)
+    pq, pk, pv, pdo = (to_dev(px[x]) for x in ("q", "k", "v", "dout"))
     pcu = torch.from_numpy(px["cu_q"]).to(dev)
     del px
     po = torch.empty_like(pq)
@@ -251,7 +251,12 @@ def main():
     ms_varlen = time_call(lambda: attn.attn_fwd_varlen(pq, pk, pv, pcu, pcu, int(vl.max()), True, scale, o=po,
                                                       lse=plse))
     f_varlen = 4.0 * d * VH * float(sum(int(n) * (int(n) + 1) // 2 for n in vl))
-    del pq, pk, pv, po, plse
+    pg = [torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)]
+    pws = torch.empty(attn.attn_bwd_varlen_workspace_bytes(len(vl), VH, int(vl.sum())), dtype=torch.uint8, device=dev)
+    ms_varlen_bwd = time_call(lambda: attn.attn_bwd_varlen(pq, pk, pv, po, plse, pdo, pcu, pcu, int(vl.max()),
+                                                          int(vl.max()), True, scale, dq=pg[0], dk=pg[1], dv=pg[2],
+                                                          workspace=pws))
+    del pq, pk, pv, po, plse, pdo, pg, pws
     # Block-sparse: B=1, H=32, N=16384, d=128, causal; query block i keeps key blocks i-7 .. i
     # and block 0 (128x128 blocks), i.e. a 1024-key window plus the first block.
     SH, SN = 32, 16384
@@ -328,6 +333,7 @@ def main():
                                         "8-block band + first block (%.1f%% of causal pairs kept)"
                                         % (100.0 * sparse_pairs / (SN * (SN + 1) / 2))},
         "fwd_varlen": {"TFLOPs": f_varlen / (ms_varlen * 1e-3) / 1e12, "ms": ms_varlen,
+                       "bwd_TFLOPs": 2.5 * f_varlen / (ms_varlen_bwd * 1e-3) / 1e12, "bwd_ms": ms_varlen_bwd,
                        "workload": "attn_fwd_varlen 12 packed sequences, lengths uniform in [256, 4096] "
                                    "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},
         "ms": {"fwd": ms_fwd, "bwd": ms_bwd, "decode": ms_dec, "fwd_min": min(t_fwd), "bwd_min": min(t_bwd),

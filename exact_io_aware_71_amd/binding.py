@@ -21,7 +21,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 EXPORTS = (
     "attn_abi_version", "attn_status_str", "attn_last_error", "attn_fwd", "attn_fwd_kv", "attn_fwd_varlen",
     "attn_fwd_blocksparse",
-    "attn_bwd_workspace_bytes", "attn_bwd", "attn_decode_auto_splits",
+    "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen", "attn_decode_auto_splits",
     "attn_decode_workspace_bytes", "attn_decode", "attn_decode_varlen",
 )
 
@@ -62,6 +62,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd.restype = i
     lib.attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_bwd_varlen_workspace_bytes.restype = sz
+    lib.attn_bwd_varlen_workspace_bytes.argtypes = [i, i, i]
+    lib.attn_bwd_varlen.restype = i
+    lib.attn_bwd_varlen.argtypes = [vp] * 11 + [i] * 10 + [f, vp, sz, vp]
     lib.attn_decode_auto_splits.restype = i
     lib.attn_decode_auto_splits.argtypes = [i, i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = sz
@@ -230,6 +234,41 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None
     _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                         B, Hq, Hkv, N, d, _dtype_code(q), int(bool(causal)), float(scale), _ptr(workspace),
                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_varlen_workspace_bytes(B, Hq, total_q) -> int:
+    return int(load().attn_bwd_varlen_workspace_bytes(B, Hq, total_q))
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    causal: bool, scale: float, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Packed variable-length backward: q/o/dout [Hq,total_q,d], k/v [Hkv,total_k,d],
+    lse [Hq,total_q] fp32, int32 offsets [B+1] on the device."""
+    import torch
+    lib = load()
+    for t in (q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k):
+        _require(t.is_cuda and t.is_contiguous(), "all inputs must be contiguous CUDA tensors")
+    _require(q.dim() == 3 and k.dim() == 3 and tuple(v.shape) == tuple(k.shape), "q [Hq,total_q,d], k/v [Hkv,total_k,d]")
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    _require(tuple(o.shape) == tuple(q.shape) == tuple(dout.shape), "o/dout shape mismatch")
+    _require(tuple(lse.shape) == (Hq, total_q) and lse.dtype == torch.float32, "lse must be fp32 [Hq,total_q]")
+    _require(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    _require(cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape == cu_seqlens_k.shape and cu_seqlens_q.numel() >= 2,
+             "cu_seqlens must be [B+1]")
+    B = cu_seqlens_q.numel() - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_varlen_workspace_bytes(B, Hq, total_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k,
+                               int(max_seqlen_q), int(max_seqlen_k), d, _dtype_code(q), int(bool(causal)),
+                               float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream)))
     return dq, dk, dv
 
 

@@ -181,7 +181,8 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void*
                   dtype, causal, scale, stream);
 }
 
-// Rows of the backward's per-row statistics are padded to whole 64-query tiles.
+// Rows of the backward's per-row statistics are padded to whole 64-query tiles: per head in the
+// dense layout, per sequence (64 spare rows each) in the packed one.
 int bwd_npad(int N) { return (N + 63) / 64 * 64; }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
@@ -191,13 +192,28 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   return align_up(2 * (size_t)B * Hq * bwd_npad(N) * sizeof(float), 256);
 }
 
-attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                       const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
-                       attn_dtype_t dtype, int causal, float scale, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+size_t attn_bwd_varlen_workspace_bytes(int B, int Hq, int total_q) {
+  if (B <= 0 || Hq <= 0 || total_q < 0) return 0;
+  return align_up(2 * (size_t)Hq * ((size_t)total_q + 64 * (size_t)B) * sizeof(float), 256);
+}
+
+// Shared by attn_bwd (dense, cu_q == nullptr) and attn_bwd_varlen (packed).
+static attn_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, const int* cu_q, const int* cu_k, int B,
+                              int Hq, int Hkv, int Nq, int Nk, int max_q, int max_k, int d, attn_dtype_t dtype,
+                              int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if ((Nq > 0 && (!q || !o || !lse || !dout || !dq)) || (Nk > 0 && (!k || !v || !dk || !dv)))
     return fail(ATTN_ERR_INVALID_ARG, "all tensor pointers of attn_bwd must be non-null");
-  RETURN_IF(check_heads(B, Hq, Hkv, N, d));
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d d=%d)", B, Hq, Hkv, d);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (Nq < 0 || Nk < 0 || max_q < 0 || max_q > Nq || max_k < 0 || max_k > Nk)
+    return fail(ATTN_ERR_INVALID_ARG, "bad row counts (Nq=%d Nk=%d max_q=%d max_k=%d)", Nq, Nk, max_q, max_k);
+  const int Bd = cu_q ? 1 : B;
+  RETURN_IF(check_rows(Bd, Hq, Hq, Nq, d));
+  RETURN_IF(check_rows(Bd, Hkv, Hkv, Nk, d));
+  if ((long long)B * Hq * ((max_q + 63) / 64) > 0x7fffffffLL || (long long)B * Hkv * ((max_k + 127) / 128) > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
   RETURN_IF(check_scale(scale));
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   for (const void* p : ptrs)
@@ -205,13 +221,36 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   if (dtype != ATTN_BF16) return fail(dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG,
                                       "backward supports bf16 only");
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "backward supports d in {64, 128} (got %d)", d);
-  const size_t need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d);
+  const size_t need = cu_q ? attn_bwd_varlen_workspace_bytes(B, Hq, Nq) : attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, d);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  xattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal ? 1 : 0, scale,
-                   (float*)workspace, bwd_npad(N), (hipStream_t)stream};
+  const long long stride = cu_q ? (long long)Nq + 64LL * B : bwd_npad(Nq);
+  const long long half = cu_q ? (long long)Hq * stride : (long long)B * Hq * stride;
+  xattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, B, Hq, Hkv, Nq, Nk, max_q, max_k, d,
+                   causal ? 1 : 0, scale, (float*)workspace, stride, half, (hipStream_t)stream};
   return from_hip(xattn::launch_bwd(a), "attn_bwd launch");
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                       attn_dtype_t dtype, int causal, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N must be positive (got %d)", N);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, B, Hq, Hkv, N, N, N, N, d, dtype, causal,
+                  scale, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                              const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k,
+                              int max_seqlen_q, int max_seqlen_k, int d, attn_dtype_t dtype, int causal, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be non-null");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens arrays must be 4-byte aligned");
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, d, dtype, causal, scale, workspace, workspace_bytes, stream);
 }
 
 int attn_decode_auto_splits(int B, int Hq, int Hkv, int L, int d) {

@@ -15,25 +15,22 @@
 // Three launches, deterministic (no atomics):
 //   1. bwd_prep_kernel: D = rowsum(dO * O) and LSE * log2(e), into row-padded arrays of the
 //      caller's workspace (padding rows get LSE = +inf, so their probabilities vanish).
-//   2. bwd_dkdv_kernel: one workgroup per 128 keys; each wave keeps its 32 keys' K and V
-//      rows in registers (B operands of S = Q K^T and dP = dO V^T) and the dK, dV
-//      accumulators in registers while Q/dO tiles of 64 queries stream through a double-
-//      buffered LDS.  In the C layout of S each lane owns one key, so P and dS are already
-//      the A operand of dV = P^T dO and dK = dS^T Q; dO and Q enter those products through
-//      the transposing ds_read_b64_tr_b16.  Causal: query tiles before the diagonal are
-//      never visited.
+//   2. bwd_dkdv_lag_kernel: one workgroup per 128 keys of a KV head; each wave keeps its 32
+//      keys' K (or V) rows in registers as the B operand of S = Q K^T (or dP = dO V^T) and
+//      its dV (or dK) accumulator in registers, while [Q | dO | LSE | D] tiles of 64 queries
+//      stream through a three-stage LDS ring.  In the C layout of S each lane owns one key,
+//      so P and dS are already the A operand of dV = P^T dO and dK = dS^T Q; dO and Q enter
+//      those products through the transposing ds_read_b64_tr_b16.  Causal: query tiles
+//      before the diagonal are never visited.
 //   3. bwd_dq_kernel: one workgroup per 128 queries; S^T = K Q^T and dP^T = V dO^T with
 //      Q and dO resident in registers, K/V tiles streamed through LDS; dS^T in the C layout
 //      is the A operand of dQ = dS K, K entering through the transposing read.
+// Every kernel takes the per-sequence row map of the forward (dense [B,H,N,d], or packed
+// variable-length [H,total,d] with offsets), and causal masks aligned at the bottom right:
+// query i of Nq sees keys j <= i + Nk - Nq.
 #include "common.h"
 #include "launch.h"
 
-#ifndef XATTN_DKDV_NS
-#define XATTN_DKDV_NS 2
-#endif
-#ifndef XATTN_DKDV_LAG
-#define XATTN_DKDV_LAG 1
-#endif
 #ifndef XATTN_DKDV_ILV
 #define XATTN_DKDV_ILV 1
 #endif
@@ -47,33 +44,44 @@
 namespace xattn {
 
 // ------------------------------------------------------------------ D = rowsum(dO * O), LSE2
-// Row r of the padded [BH, Npad] arrays: r % Npad < N holds real statistics, the rest padding.
+// First statistics row of (b, h) in each half of the workspace (see BwdArgs).
+__device__ __forceinline__ size_t stat_row(const SeqGeo& g, long long stride, int b, int h, int Hq) {
+  if (g.cu_q == nullptr) return ((size_t)b * Hq + h) * stride;
+  return (size_t)h * stride + min(max(g.cu_q[b], 0), g.nq) + 64 * (size_t)b;
+}
+
+// One block per (batch, head, RPB rows): rows below the sequence's length get its statistics,
+// rows up to the next multiple of 64 the padding (LSE2 = +inf, D = 0).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse,
-                                                       float* __restrict__ lse2, float* __restrict__ delta,
-                                                       int N, int Npad, int rows_pad) {
+                                                       const float* __restrict__ lse, float* __restrict__ lse2,
+                                                       float* __restrict__ delta, SeqGeo geo, long long stat_stride,
+                                                       int Hq, int BH) {
   constexpr int LPR = D / 8;             // lanes per row, 8 features each
   constexpr int RPB = 256 / LPR;         // rows per block
   const int tid = threadIdx.x;
-  const int row = blockIdx.x * RPB + tid / LPR;
+  const int bh = blockIdx.x % BH, b = bh / Hq, h = bh - b * Hq;
+  const SeqRows sr = seq_rows(geo, b, h, Hq, 0, 1);
+  const int i = (blockIdx.x / BH) * RPB + tid / LPR;
   const int c = tid % LPR;
-  const int bh = row / Npad, i = row - bh * Npad;
-  const bool real = row < rows_pad && i < N;
+  const int npad = (sr.lq + 63) / 64 * 64;
+  if (i >= npad) return;                 // whole rows only: the reduction below stays in-row
+  const bool real = i < sr.lq;
   float s = 0.f;
   if (real) {
-    const size_t off = ((size_t)bh * N + i) * D + 8 * c;
+    const size_t off = (sr.q + i) * D + 8 * c;
     const u32x4 a = ld_global16(o + off);
     const u32x4 g = ld_global16(dout + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) s += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
   }
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows_pad && c == 0) {
-    delta[row] = s;
-    lse2[row] = real ? lse[(size_t)bh * N + i] * kLog2e : INFINITY;
+  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, LPR);
+  if (c == 0) {
+    const size_t r = stat_row(geo, stat_stride, b, h, Hq) + i;
+    delta[r] = s;
+    lse2[r] = real ? lse[sr.q + i] * kLog2e : INFINITY;
   }
 }
 
@@ -93,215 +101,9 @@ struct BwdTile {
   static constexpr int BYTES = 64 * D * 2;   // one swizzled 64-row tile
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int Npad, float scale, float scale_log2, int BH) {
-  constexpr int NW = 8, NG = 4, BK = NG * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32;
-  using T = BwdTile<D>;
-  constexpr int STAGE = 2 * T::BYTES + 2 * BQ * 4;  // Q, dO, LSE2, D
-  constexpr int NS = XATTN_DKDV_NS;                 // LDS ring: tile t+NS-1 loads during tile t
-  static_assert(NS == 2 || NS == 3, "ring depth");
-  constexpr int RPC = 1024 / (2 * D), CPTT = T::BYTES / 1024, CPW = 2 * CPTT / NW;
-  static_assert(CPTT % NW == 0 || (2 * CPTT) % NW == 0, "tile pieces split over the waves");
-  static_assert(NW % (16 / RPC) == 0, "pieces of a wave share their swizzle");
-  // Tile ring, then the P hand-over buffers: [key group][32-query block][register][lane] fp32.
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + NG * (BQ / 32) * 16 * 64 * 4];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
-  // Waves g and g + NG run on the same SIMD and own the same 32 keys: the first accumulates
-  // dV, the second dK (see the tile loop below).
-  const int grp = wave & (NG - 1), role = wave / NG;
-  const int bh = blockIdx.x % BH;
-  // Causal: early key tiles see the most queries and are dispatched first.
-  const int k0 = (blockIdx.x / BH) * BK;
-  const int kw0 = k0 + grp * 32;
-  const uint16_t* qp = q + (size_t)bh * N * D;
-  const uint16_t* kp = k + (size_t)bh * N * D;
-  const uint16_t* vp = v + (size_t)bh * N * D;
-  const uint16_t* dop = dout + (size_t)bh * N * D;
-  // stats = [LSE2 | D], each [BH, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
-  const uint32_t lse_off = (uint32_t)((size_t)bh * Npad * 4);
-  const uint32_t dl_off = (uint32_t)(((size_t)BH + bh) * Npad * 4);
-
-  const int qt_begin = CAUSAL ? (k0 / BQ) : 0;
-  const int qt_end = (N + BQ - 1) / BQ;
-
-  // Tile copies: wave w copies 1 KB pieces j = w, w + NW, ... of [Q tile | dO tile]; piece j
-  // covers tile rows RPC*(j % CPTT) ...; lane l fills physical chunk l, i.e. logical chunk
-  // (l%(D/8)) ^ swizzle(row), the same swizzle for all pieces of a wave.  Rows past N read
-  // row N-1 (their LSE2 is +inf, so they contribute nothing).  Waves 0 and 1 also copy the
-  // tile's 64 LSE2 and 64 D values (the padded rows hold +inf and 0).
-  const int lrow = lane / (D / 8);
-  const uint32_t loff0 =
-      lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(RPC * wave + lrow, 0) >> 4) & (D / 8 - 1)));
-  auto copy_tile = [&](int t, int st) __attribute__((always_inline)) {
-    char* dst = smem + st * STAGE;
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int j = wave + NW * i;
-      const bool is_q = j < CPTT;
-      const int jt = is_q ? j : j - CPTT;
-      const int row0 = t * BQ + RPC * jt;
-      const uint16_t* base = is_q ? qp : dop;
-      char* d = dst + (is_q ? 0 : T::BYTES) + 1024 * jt;
-      if (row0 + RPC <= N) {
-        dma16(base, (uint32_t)row0 * (2 * D) + loff0, d);
-      } else {
-        const int row = min(row0 + lrow, N - 1);
-        dma16(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), d);
-      }
-    }
-    if (wave < 2) dma4(stats, (wave == 0 ? lse_off : dl_off) + 4 * (t * BQ + lane), dst + 2 * T::BYTES + wave * BQ * 4);
-  };
-  constexpr int CPW0 = CPW + 1;  // copies per tile issued by waves 0 and 1
-
-  // Ring prologue: tiles qt_begin .. qt_begin + NS - 2.
-#pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (qt_begin + j < qt_end) copy_tile(qt_begin + j, j);
-
-  // K^T (dV wave) or V^T (dK wave), the B operand of S = Q K^T or dP = dO V^T: lane owns key
-  // kw0 + l32.
-  const int kj = kw0 + l32;
-  const uint16_t* kvp = role == 0 ? kp : vp;
-  bf16x8 kreg[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c) {
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (kj < N) a = ld_global16(kvp + (size_t)kj * D + 16 * c + 8 * h32);
-    kreg[c] = as_bf16x8(a);
-  }
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  wait_vmem();
-  lds_barrier();
-
-  // End of tile t: tile t+1 must have landed; with three stages this wave's copies of tile
-  // t+2 may stay in flight.
-  auto end_tile = [&](int t) __attribute__((always_inline)) {
-    if (NS > 2 && t + 2 < qt_end) {
-      if (wave < 2) wait_vmem_n<CPW0>();
-      else wait_vmem_n<CPW>();
-    } else {
-      wait_vmem();
-    }
-    lds_barrier();
-  };
-
-  // Per tile, two phases separated by a barrier.  Phase A: the dV wave computes S = Q K^T,
-  // P = 2^(S scale log2 e - LSE2) (masked) and hands P (fp32) to its partner through LDS;
-  // the dK wave computes dP = dO V^T meanwhile.  Phase B: the dV wave adds P^T dO to dV; the
-  // dK wave reads P, forms dS = P (dP - D) and adds dS^T Q to dK.  Every product is computed
-  // once, 16 MFMAs per 32-query block on each wave of the pair.
-  constexpr int NQB = BQ / 32;
-  float* pbuf = reinterpret_cast<float*>(smem + NS * STAGE) + grp * (NQB * 16 * 64);  // [qb][r][lane]
-  if (role == 0) {
-    for (int t = qt_begin; t < qt_end; ++t) {
-      const int it = t - qt_begin;
-      if (t + NS - 1 < qt_end) copy_tile(t + NS - 1, (it + NS - 1) % NS);
-      const char* qs = smem + (it % NS) * STAGE;
-      const char* dos = qs + T::BYTES;
-      const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
-      const int q0 = t * BQ;
-      bf16x8 pa[NQB][2];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qb0 = q0 + qb * 32;
-        f32x16 sv;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < DC; ++c)
-          sv = mfma32(*reinterpret_cast<const bf16x8*>(qs + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], sv);
-        // Lane owns key kj; register r holds query qb0 + 8(r/4) + 4*h32 + r%4.  Queries before
-        // the key (causal) get P = 0, which also covers blocks wholly before this wave's keys.
-        const bool need_mask = CAUSAL && (qb0 < kw0 + 31);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * r4 + 4 * h32);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * r4 + i;
-            float p = fast_exp2(fmaf(sv[r], scale_log2, -l4[i]));
-            if (need_mask && kj > qb0 + 8 * r4 + 4 * h32 + i) p = 0.f;
-            sv[r] = p;
-          }
-        }
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<f32x4*>(pbuf + (qb * 4 + r4) * 256 + 4 * lane) =
-              f32x4{sv[4 * r4], sv[4 * r4 + 1], sv[4 * r4 + 2], sv[4 * r4 + 3]};
-        pa[qb][0] = pack8(sv, 0);
-        pa[qb][1] = pack8(sv, 1);
-      }
-      lds_barrier();  // P visible to the dK wave
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            acc[db] = mfma32(pa[qb][sh], ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
-      end_tile(t);
-    }
-  } else {
-    for (int t = qt_begin; t < qt_end; ++t) {
-      const int it = t - qt_begin;
-      if (t + NS - 1 < qt_end) copy_tile(t + NS - 1, (it + NS - 1) % NS);
-      const char* qs = smem + (it % NS) * STAGE;
-      const char* dos = qs + T::BYTES;
-      const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
-      f32x16 dp[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < DC; ++c)
-          dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dos + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], dp[qb]);
-      }
-      lds_barrier();  // P of this tile written by the dV wave
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(pbuf + (qb * 4 + r4) * 256 + 4 * lane);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * r4 + 4 * h32);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dp[qb][4 * r4 + i] = p4[i] * (dp[qb][4 * r4 + i] - d4[i]);
-        }
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const bf16x8 dsa = pack8(dp[qb], sh);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            acc[db] = mfma32(dsa, ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
-        }
-      }
-      end_tile(t);
-    }
-  }
-
-  // C layout: lane holds feature db*32 + l32 of keys kw0 + 8(r/4) + 4*h32 + r%4.
-  uint16_t* outp = (role == 0 ? dv : dk) + (size_t)bh * N * D;
-  const float oscale = role == 0 ? 1.f : scale;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      if (kr < N) outp[(size_t)kr * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(acc[db][r] * oscale, 0.f) & 0xffffu);
-    }
-}
-
-// dK, dV with a lagged dK wave.  As bwd_dkdv_kernel, waves g and g + 4 share a SIMD and the
-// same 32 keys, the first accumulating dV, the second dK, and P crosses from the first to the
-// second through LDS (here as bf16, the precision the dS product rounds to anyway).  The dK
+// dK, dV with a lagged dK wave.  Waves g and g + 4 share a SIMD and the same 32 keys, the
+// first accumulating dV, the second dK, and P crosses from the first to the second through
+// LDS (as bf16, the precision the dS product rounds to anyway).  The dK
 // wave works one query tile behind: in iteration t the dV wave forms S, P and P^T dO for
 // tile t while the dK wave forms dP, dS and dS^T Q for tile t-1 from the P written in
 // iteration t-1.  One barrier per tile instead of two, and each SIMD always holds one wave
@@ -311,7 +113,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_lag_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int Npad, float scale, float scale_log2, int BHkv, int Hq, int Hkv, int BHq) {
+    uint16_t* __restrict__ dv, SeqGeo geo, long long stat_stride, long long stat_half, float scale, float scale_log2,
+    int BHkv, int Hq, int Hkv) {
   constexpr int NW = 8, NG = 4, BK = NG * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32, NQB = BQ / 32;
   using T = BwdTile<D>;
   constexpr int STAGE = (2 * T::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // Q, dO, LSE2, D
@@ -328,27 +131,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // One workgroup per (batch, KV head, 128 keys).  With grouped-query heads the g query heads
   // sharing the KV head are visited one after the other ([OPT] §5.3 mapping kv = h / g), so
   // dK and dV accumulate the whole group's gradient without atomics.
-  const int bkv = blockIdx.x % BHkv;
+  const int bkv = blockIdx.x % BHkv, b = bkv / Hkv, hk = bkv - b * Hkv;
+  const int g = Hq / Hkv, h0 = hk * g;  // the group's first query head
+  const SeqRows sr = seq_rows(geo, b, h0, Hq, hk, Hkv);
+  const int Nq = sr.lq, Nk = sr.lk, doff = Nk - Nq;  // query i sees keys j <= i + doff (causal)
   // Causal: early key blocks see the most queries and are dispatched first.
   const int k0 = (blockIdx.x / BHkv) * BK;
+  if (k0 >= Nk) return;  // key block past the end of a shorter sequence
   const int kw0 = k0 + grp * 32;
-  const int g = Hq / Hkv;
-  const int hq0 = (bkv / Hkv) * Hq + (bkv % Hkv) * g;  // first query head (b*Hq + h) of the group
-  const uint16_t* qp = q + (size_t)hq0 * N * D;         // head i of the group: + i*N*D
-  const uint16_t* kp = k + (size_t)bkv * N * D;
-  const uint16_t* vp = v + (size_t)bkv * N * D;
-  const uint16_t* dop = dout + (size_t)hq0 * N * D;
-  // stats = [LSE2 | D], each [B*Hq, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
-  auto lse_off = [&](int h) __attribute__((always_inline)) { return (uint32_t)((size_t)(hq0 + h) * Npad * 4); };
-  auto dl_off = [&](int h) __attribute__((always_inline)) { return (uint32_t)(((size_t)BHq + hq0 + h) * Npad * 4); };
-  const int qt_begin = CAUSAL ? (k0 / BQ) : 0;
-  const int qt_end = (N + BQ - 1) / BQ;
+  // Query head h0 + i of the group: rows + i * geo.nq (the head stride of both layouts).
+  const uint16_t* qp = q + sr.q * D;
+  const uint16_t* kp = k + sr.k * D;
+  const uint16_t* vp = v + sr.k * D;
+  const uint16_t* dop = dout + sr.q * D;
+  // stats = [LSE2 | D]; LSE2 is the log-sum-exp times log2(e).  Head i of the group: + i*stride.
+  const float* lse_b = stats + stat_row(geo, stat_stride, b, h0, Hq);
+  const float* dl_b = lse_b + stat_half;
+  const int npad = (Nq + BQ - 1) / BQ * BQ;  // statistics rows of one head of this sequence
+  const int qt_begin = CAUSAL ? max(k0 - doff, 0) / BQ : 0;
+  const int qt_end = (Nq + BQ - 1) / BQ;
   // Virtual tiles vt = 0 .. g*nt - 1: query head vt / nt of the group, tile qt_begin + vt % nt.
   // The LDS ring slot and the P slot follow vt.
   const int nt = qt_end - qt_begin, nvt = g * nt;
+  uint16_t* outp = (role == 0 ? dv : dk) + sr.k * D;
+  if (nt <= 0) {  // no query sees these keys: dK = dV = 0
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        if (kr < Nk) outp[(size_t)kr * D + db * 32 + l32] = 0;
+      }
+    return;
+  }
 
-  // Tile copies, as in bwd_dkdv_kernel: wave w copies 1 KB pieces w, w + NW, ... of [Q | dO];
-  // rows past N read row N-1 (their LSE2 is +inf); waves 0 and 1 copy the 64 LSE2 and D values.
+  // Tile copies: wave w copies 1 KB pieces j = w, w + NW, ... of [Q tile | dO tile]; piece j
+  // covers tile rows RPC*(j % CPTT) ...; lane l fills physical chunk l, i.e. logical chunk
+  // (l%(D/8)) ^ swizzle(row), the same swizzle for all pieces of a wave.  Rows past the last
+  // query read the last query (their LSE2 is +inf, so they contribute nothing); waves 0 and 1
+  // copy the tile's 64 LSE2 and 64 D values (the padded rows hold +inf and 0).
   const int lrow = lane / (D / 8);
   const uint32_t loff0 =
       lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(RPC * wave + lrow, 0) >> 4) & (D / 8 - 1)));
@@ -360,16 +181,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const bool is_q = j < CPTT;
       const int jt = is_q ? j : j - CPTT;
       const int row0 = t * BQ + RPC * jt;
-      const uint16_t* base = (is_q ? qp : dop) + (size_t)h * N * D;
+      const uint16_t* base = (is_q ? qp : dop) + (size_t)h * geo.nq * D;
       char* d = dst + (is_q ? 0 : T::BYTES) + 1024 * jt;
-      if (row0 + RPC <= N) {
+      if (row0 + RPC <= Nq) {
         dma16(base, (uint32_t)row0 * (2 * D) + loff0, d);
       } else {
-        const int row = min(row0 + lrow, N - 1);
+        const int row = min(row0 + lrow, Nq - 1);
         dma16(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), d);
       }
     }
-    if (wave < 2) dma4(stats, (wave == 0 ? lse_off(h) : dl_off(h)) + 4 * (t * BQ + lane), dst + 2 * T::BYTES + wave * BQ * 4);
+    if (wave < 2)
+      dma4((wave == 0 ? lse_b : dl_b) + (size_t)h * stat_stride, 4 * min(t * BQ + lane, npad - 1),
+           dst + 2 * T::BYTES + wave * BQ * 4);
   };
 
   // Branch-free single pieces, for issue between the MFMAs of the interleaved tiles: piece i
@@ -377,21 +200,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // D; the copies of one kind write the same bytes).
   const void* qbase = wave_uniform(qp);
   const void* dobase = wave_uniform(dop);
-  const void* sbase = wave_uniform(stats);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto copy_piece = [&](int vt, int h, int t, int i) __attribute__((always_inline)) {
     const int j = wv + NW * i;
     const bool is_q = j < CPTT;
     const int jt = is_q ? j : j - CPTT;
-    const int row = min(t * BQ + RPC * jt + lrow, N - 1);
+    const int row = min(t * BQ + RPC * jt + lrow, Nq - 1);
     const uint32_t m0v = lds0 + (vt % NS) * STAGE + (is_q ? 0 : T::BYTES) + 1024 * jt;
-    const char* base = reinterpret_cast<const char*>(is_q ? qbase : dobase) + (size_t)h * N * D * 2;
+    const char* base = reinterpret_cast<const char*>(is_q ? qbase : dobase) + (size_t)h * geo.nq * D * 2;
     dma16_m0(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
   };
   auto copy_stats = [&](int vt, int h, int t) __attribute__((always_inline)) {
     const uint32_t m0v = lds0 + (vt % NS) * STAGE + 2 * T::BYTES + (wv & 1) * BQ * 4;
-    dma4_m0(sbase, ((wv & 1) ? dl_off(h) : lse_off(h)) + 4 * min(t * BQ + lane, Npad - 1), m0v);
+    const float* base = ((wv & 1) ? dl_b : lse_b) + (size_t)h * stat_stride;
+    dma4_m0(wave_uniform(base), 4 * min(t * BQ + lane, npad - 1), m0v);
   };
 
   copy_tile(0, 0, qt_begin);
@@ -403,7 +226,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     u32x4 a = {0u, 0u, 0u, 0u};
-    if (kj < N) a = ld_global16(kvp + (size_t)kj * D + 16 * c + 8 * h32);
+    if (kj < Nk) a = ld_global16(kvp + (size_t)kj * D + 16 * c + 8 * h32);
     kreg[c] = as_bf16x8(a);
   }
   f32x16 acc[DB];
@@ -436,8 +259,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       // Lane owns key kj; register r holds query q0 + 32 qb + 8(r/4) + 4*h32 + r%4.
-      // Queries before the key (causal) get P = 0.
-      const int qb0 = q0 + qb * 32;
+      // Queries that do not see the key (causal: kj > i + doff) get P = 0.
+      const int qb0 = q0 + qb * 32 + doff;
       const bool need_mask = CAUSAL && (qb0 < kw0 + 31);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -639,7 +462,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int vt = 0; vt <= nvt; ++vt) {
     const bool more = vt + 1 < nvt;
     const int ch = more ? h_nxt : g - 1, ct = more ? t_nxt : qt_end;
-    const bool ilv_dv = kIlv && role == 0 && vt < nvt && !(CAUSAL && t_cur * BQ < kw0 + 31);
+    const bool ilv_dv = kIlv && role == 0 && vt < nvt && !(CAUSAL && t_cur * BQ + doff < kw0 + 31);
     const bool ilv_dk = kIlv && role == 1 && vt > 0;
     if (!(XATTN_DKDV_SPREAD && (ilv_dv || ilv_dk)) && more) copy_tile(vt + 1, h_nxt, t_nxt);
     if (role == 0) {
@@ -662,14 +485,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // C layout: lane holds feature db*32 + l32 of keys kw0 + 8(r/4) + 4*h32 + r%4.
-  uint16_t* outp = (role == 0 ? dv : dk) + (size_t)bkv * N * D;
   const float oscale = role == 0 ? 1.f : scale;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      if (kr < N) outp[(size_t)kr * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(acc[db][r] * oscale, 0.f) & 0xffffu);
+      if (kr < Nk) outp[(size_t)kr * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(acc[db][r] * oscale, 0.f) & 0xffffu);
     }
 }
 
@@ -677,8 +499,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, int N,
-    int Npad, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv) {
+    const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, SeqGeo geo,
+    long long stat_stride, long long stat_half, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv) {
   constexpr int NW = 4, BM = NW * 32, BN = kBwdBK, KB = BN / 32, DC = D / 16, DB = D / 32;
   using T = BwdTile<D>;
   constexpr int STAGE = 2 * T::BYTES;  // K, V
@@ -690,26 +512,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qt = CAUSAL ? (n_qtiles - 1 - t_) : t_;
   const int q0 = qt * BM, qw0 = q0 + wave * 32, qi = qw0 + l32;
   // K/V of the query head's KV head (grouped-query: kv = h / (Hq/Hkv)).
-  const int bkv = (bh / Hq) * Hkv + (bh % Hq) / (Hq / Hkv);
-  const uint16_t* qp = q + (size_t)bh * N * D;
-  const uint16_t* kp = k + (size_t)bkv * N * D;
-  const uint16_t* vp = v + (size_t)bkv * N * D;
-  const uint16_t* dop = dout + (size_t)bh * N * D;
+  const int b = bh / Hq, hq = bh - b * Hq, hk = hq / (Hq / Hkv);
+  const SeqRows sr = seq_rows(geo, b, hq, Hq, hk, Hkv);
+  const int Nq = sr.lq, Nk = sr.lk;
+  if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
+  const int qd0 = qw0 + (Nk - Nq), kmax = qi + (Nk - Nq);  // causal: query i sees keys <= i + Nk - Nq
+  const uint16_t* qp = q + sr.q * D;
+  const uint16_t* kp = k + sr.k * D;
+  const uint16_t* vp = v + sr.k * D;
+  const uint16_t* dop = dout + sr.q * D;
 
   bf16x8 qreg[DC], doreg[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     u32x4 a = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u};
-    if (qi < N) {
+    if (qi < Nq) {
       a = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
       g = ld_global16(dop + (size_t)qi * D + 16 * c + 8 * h32);
     }
     qreg[c] = as_bf16x8(a);
     doreg[c] = as_bf16x8(g);
   }
-  // stats = [LSE2 | D], each [BH, Npad] fp32; LSE2 is the log-sum-exp times log2(e).
-  const float lse2 = qi < N ? stats[(size_t)bh * Npad + qi] : INFINITY;
-  const float dl = qi < N ? stats[((size_t)BH + bh) * Npad + qi] : 0.f;
+  // stats = [LSE2 | D]; LSE2 is the log-sum-exp times log2(e).
+  const float* st = stats + stat_row(geo, stat_stride, b, hq, Hq);
+  const float lse2 = qi < Nq ? st[qi] : INFINITY;
+  const float dl = qi < Nq ? st[stat_half + qi] : 0.f;
 
   f32x16 dq_acc[DB];
 #pragma unroll
@@ -717,13 +544,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int kv_end = CAUSAL ? min(Nk, q0 + BM + (Nk - Nq)) : Nk;
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   // K/V tiles arrive by direct global -> LDS copies (no staging registers, which lets two
   // workgroups share a CU).  Wave w copies 1 KB pieces j = w, w + NW, ... of [K tile | V
   // tile]; piece j covers tile rows RPC*(j % CPTT) ...; lane l fills physical chunk l, i.e.
   // logical chunk (l%(D/8)) ^ swizzle(row).  The swizzle depends on the row modulo 16 only,
-  // which is the same for all pieces of a wave.  Rows past N read row N-1 (masked below).
+  // which is the same for all pieces of a wave.  Rows past the last key read the last key
+  // (masked below).
   constexpr int RPC = 1024 / (2 * D), CPTT = T::BYTES / 1024, CPW = 2 * CPTT / NW;
   static_assert(CPTT % NW == 0 && NW % (16 / RPC) == 0, "pieces of a wave share their swizzle");
   const int lrow = lane / (D / 8);
@@ -739,10 +567,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int row0 = t * BN + RPC * jt;
       const uint16_t* base = is_k ? kp : vp;
       char* d = dst + (is_k ? 0 : T::BYTES) + 1024 * jt;
-      if (row0 + RPC <= N) {
+      if (row0 + RPC <= Nk) {
         dma16(base, (uint32_t)row0 * (2 * D) + loff0, d);
       } else {
-        const int row = min(row0 + lrow, N - 1);
+        const int row = min(row0 + lrow, Nk - 1);
         dma16(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), d);
       }
     }
@@ -758,11 +586,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int j = wv + NW * i;
     const bool is_k = j < CPTT;
     const int jt = is_k ? j : j - CPTT;
-    const int row = min(t * BN + RPC * jt + lrow, N - 1);
+    const int row = min(t * BN + RPC * jt + lrow, Nk - 1);
     const uint32_t m0v = lds0 + (t & 1) * STAGE + (is_k ? 0 : T::BYTES) + 1024 * jt;
     dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
   };
 
+  uint16_t* dqp = dq + sr.q * D;
+  if (ntiles == 0) {  // no key for any row of the tile: dQ = 0
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = qw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        if (qq < Nq) dqp[(size_t)qq * D + db * 32 + l32] = 0;
+      }
+    return;
+  }
   copy_tile(0, 0);
   wait_vmem();  // also covers the Q/dO loads
   lds_barrier();
@@ -771,7 +610,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int t0 = t * BN;
     const char* ks = smem + (t & 1) * STAGE;
     const char* vs = ks + T::BYTES;
-    if (CAUSAL && t0 > qw0 + 31) {
+    if (CAUSAL && t0 > qd0 + 31) {
 #pragma unroll
       for (int i = 0; i < CPW; ++i) copy_piece(t + 1, i);
     } else {
@@ -791,13 +630,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         // Lane owns query qi; register r holds key t0 + kb*32 + 8(r/4) + 4*h32 + r%4.
         const int kb0 = t0 + kb * 32;
-        const bool need_mask = (kb0 + 32 > N) || (CAUSAL && kb0 + 31 > qw0);
+        const bool need_mask = (kb0 + 32 > Nk) || (CAUSAL && kb0 + 31 > qd0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
           if (need_mask) {
             const int kj = kb0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            if (kj >= N || (CAUSAL && kj > qi)) p = 0.f;
+            if (kj >= Nk || (CAUSAL && kj > kmax)) p = 0.f;
           }
           dp[r] = p * (dp[r] - dl);
         }
@@ -816,46 +655,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lds_barrier();
   }
   // C layout: lane holds feature db*32 + l32 of queries qw0 + 8(r/4) + 4*h32 + r%4.
-  uint16_t* dqp = dq + (size_t)bh * N * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qq = qw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      if (qq < N) dqp[(size_t)qq * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(dq_acc[db][r] * scale, 0.f) & 0xffffu);
+      if (qq < Nq) dqp[(size_t)qq * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(dq_acc[db][r] * scale, 0.f) & 0xffffu);
     }
 }
 
 // ------------------------------------------------------------------ host launcher
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
-  const int BH = a.B * a.Hq;
-  const int rows_pad = BH * a.Npad;
+  const int BH = a.B * a.Hq, BHkv = a.B * a.Hkv;
   const float sl2 = a.scale * kLog2e;
+  const SeqGeo geo{a.cu_q, a.cu_k, a.Nq, a.Nk};
   float* lse2 = a.stats;
-  float* delta = a.stats + (size_t)BH * a.Npad;
+  float* delta = a.stats + a.stat_half;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((rows_pad + RPB - 1) / RPB), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, lse2, delta, a.N, a.Npad, rows_pad);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_kt = (a.N + 127) / 128;
-  const int BHkv = a.B * a.Hkv;
-  if (XATTN_DKDV_LAG || a.Hq != a.Hkv)
+  const int n_pb = ((a.max_q + 63) / 64 * 64 + RPB - 1) / RPB;
+  if (n_pb > 0) {
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(n_pb * BH), dim3(256), 0, a.stream, (const uint16_t*)a.o,
+                       (const uint16_t*)a.dout, a.lse, lse2, delta, geo, a.stat_stride, a.Hq, BH);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_kt = (a.max_k + 127) / 128;
+  if (n_kt > 0) {
     hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL>), dim3(n_kt * BHkv), dim3(512), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
-                       (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Npad, a.scale, sl2, BHkv,
-                       a.Hq, a.Hkv, BH);
-  else
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(512), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
-                     (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Npad, a.scale, sl2, BH);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_qt = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
-                     (const uint16_t*)a.dout, (uint16_t*)a.dq, a.N, a.Npad, a.scale, sl2, n_qt, BH, a.Hq, a.Hkv);
+                       (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, geo, a.stat_stride, a.stat_half,
+                       a.scale, sl2, BHkv, a.Hq, a.Hkv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_qt = (a.max_q + 127) / 128;
+  if (n_qt > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(256), 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats, (const uint16_t*)a.dout,
+                       (uint16_t*)a.dq, geo, a.stat_stride, a.stat_half, a.scale, sl2, n_qt, BH, a.Hq, a.Hkv);
   return hipGetLastError();
 }
 

@@ -21,13 +21,20 @@ struct FwdArgs {
   long long mask_sb, mask_sh;       // batch and head strides of block_mask in bytes
 };
 
+// Backward: dense [B,H,N,d] tensors (cu_q == nullptr, Nq == Nk == N) or packed
+// variable-length [H,total,d] tensors with offsets cu_q/cu_k [B+1] (Nq, Nk the totals, max_q,
+// max_k the longest sequences).  The workspace holds two fp32 halves (LSE*log2(e), then
+// D = rowsum(dO*O)) of `stat_half` floats; the rows of (b, h) start at (b*Hq + h)*stat_stride
+// (dense, stat_stride = roundup(N, 64)) or at h*stat_stride + cu_q[b] + 64b (packed,
+// stat_stride = total_q + 64B), so every sequence owns roundup(len, 64) rows.
 struct BwdArgs {
   const void* q; const void* k; const void* v; const void* o; const float* lse; const void* dout;
   void* dq; void* dk; void* dv;
-  int B, Hq, Hkv, N, d, causal;
+  const int* cu_q; const int* cu_k;
+  int B, Hq, Hkv, Nq, Nk, max_q, max_k, d, causal;
   float scale;
-  float* stats;  // [2, B*Hq, Npad] fp32 scratch in the caller's workspace: LSE*log2(e), then D
-  int Npad;      // N rounded up to a multiple of 64
+  float* stats;
+  long long stat_stride, stat_half;
   hipStream_t stream;
 };
 

@@ -155,6 +155,28 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int B, int Hq, int Hkv, int N, int d, attn_dtype_t dtype, int causal,
                        float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace attn_bwd_varlen needs: the same two fp32 statistics per query
+ * row, each sequence padded by up to 64 rows, i.e. 2 * Hq * (total_q + 64 * B) * 4 bytes,
+ * rounded up to 256. */
+size_t attn_bwd_varlen_workspace_bytes(int B, int Hq, int total_q);
+
+/*
+ * attn_bwd for the packed variable-length layout of attn_fwd_varlen ([NOTE] Method: no
+ * padding; item 3: recomputation): q/o/dout/dq [Hq,total_q,d], k/v/dk/dv [Hkv,total_k,d],
+ * lse [Hq,total_q] as attn_fwd_varlen wrote it, offsets cu_seqlens_q/k [B+1] (int32, device,
+ * 4-byte aligned), max_seqlen_q/k the longest query and key sequences (they size the grids).
+ * Causal masks per sequence are aligned at the bottom right (as attn_fwd_varlen).  Query rows
+ * that see no key get dq = 0; keys that no query sees get dk = dv = 0.
+ *   workspace  >= attn_bwd_varlen_workspace_bytes(B, Hq, total_q), 256-byte aligned
+ * Supported: BF16, d in {64, 128}, Hq a multiple of Hkv.  Deterministic (no atomics).
+ */
+attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                              int Hkv, int total_q, int total_k, int max_seqlen_q,
+                              int max_seqlen_k, int d, attn_dtype_t dtype, int causal, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Split count attn_decode uses for num_splits == 0 (the automatic choice), so callers can
  * size the workspace and reproduce the split.

@@ -31,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["upcast", "probabilities", "forward", "forward_kv", "forward_blocksparse", "forward_varlen", "forward_rows",
-           "backward",
+           "backward", "backward_kv", "backward_varlen",
            "decode", "split_kv_decode", "lse_merge", "attention_flops"]
 
 
@@ -227,6 +227,46 @@ def backward(q, k, v, dout, scale: float, causal: bool):
             ds = p * (dp - dd)
             dq[b, h] = scale * (ds @ k[b, kv])
             dk[b, kv] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def backward_kv(q, k, v, dout, scale: float, causal: bool):
+    """backward for Nq queries against Nk keys, the gradient of forward_kv (causal mask aligned
+    at the bottom right: query i sees keys j <= i + Nk - Nq).  Rows that see no key have P = 0
+    and contribute nothing; their dQ is 0."""
+    q, k, v, dout = upcast(q), upcast(k), upcast(v), upcast(dout)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if Nk == 0 or Nq == 0:
+        return dq, dk, dv
+    pos = np.arange(Nq) + (Nk - Nq)
+    for b in range(B):
+        for h in range(Hq):
+            kv = _kv_head(h, Hq, Hkv)
+            p, _ = _softmax_rows(_scores(q[b, h], k[b, kv], scale, causal, row_ids=pos))
+            o = p @ v[b, kv]
+            do = dout[b, h]
+            dv[b, kv] += p.T @ do
+            dp = do @ v[b, kv].T
+            dd = np.sum(do * o, axis=1, keepdims=True)
+            ds = p * (dp - dd)
+            dq[b, h] = scale * (ds @ k[b, kv])
+            dk[b, kv] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def backward_varlen(q, k, v, dout, cu_q, cu_k, scale: float, causal: bool):
+    """Gradient of forward_varlen: each packed sequence is backward_kv on its own rows.
+    q/dout [Hq, total_q, d], k/v [Hkv, total_k, d]; returns dQ, dK, dV in the same layouts."""
+    q, k, v, dout = upcast(q), upcast(k), upcast(v), upcast(dout)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        g = backward_kv(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], dout[None, :, q0:q1], scale, causal)
+        dq[:, q0:q1], dk[:, k0:k1], dv[:, k0:k1] = g[0][0], g[1][0], g[2][0]
     return dq, dk, dv
 
 

@@ -118,10 +118,11 @@ def make_decode(B, Hq, Hkv, L, d, seed=0, dtype="bf16"):
     return {"q": q, "k": caches[0], "v": caches[1]}
 
 
-def make_varlen(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", seed=0, qk_mult=1.0):
+def make_varlen(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", seed=0, qk_mult=1.0, with_dout=False):
     """Packed variable-length inputs: Q [Hq,total_q,d], K/V [Hkv,total_k,d] with sequence b
     at rows cu_q[b]..cu_q[b+1]-1 (cu_k likewise); cu_q, cu_k are int32 [B+1] running sums of
-    the lengths.  Drawn Q, K, V from one PCG64 stream, rounded as in make_prefill.
+    the lengths; optional dO [Hq,total_q,d].  Drawn Q, K, V, dO from one PCG64 stream,
+    rounded as in make_prefill.
     """
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
@@ -133,4 +134,7 @@ def make_varlen(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", seed=0, qk_mult=1.0):
         assert math.log2(qk_mult).is_integer()
         q *= np.float32(qk_mult)
         k *= np.float32(qk_mult)
-    return {"q": _as_io(q, dtype), "k": _as_io(k, dtype), "v": _as_io(v, dtype), "cu_q": cu_q, "cu_k": cu_k}
+    out = {"q": _as_io(q, dtype), "k": _as_io(k, dtype), "v": _as_io(v, dtype), "cu_q": cu_q, "cu_k": cu_k}
+    if with_dout:
+        out["dout"] = _as_io(normal_f32(rng, (Hq, int(cu_q[-1]), d)), dtype)
+    return out

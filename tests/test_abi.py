@@ -110,6 +110,22 @@ def test_bwd_validation():
     assert bwd(ws=P + 16) == 1               # workspace must be 256-byte aligned
 
 
+def test_bwd_varlen_validation():
+    need = lib.attn_bwd_varlen_workspace_bytes(3, 4, 100)
+    assert need == 2 * 4 * (100 + 64 * 3) * 4 // 256 * 256 + (256 if (2 * 4 * (100 + 192) * 4) % 256 else 0)
+
+    def bv(cu_q=P, cu_k=P, ws=P, ws_bytes=need, max_q=40, max_k=50, total_k=200, dt=1):
+        return lib.attn_bwd_varlen(P, P, P, P, P, P, P, P, P, cu_q, cu_k, 3, 4, 2, 100, total_k, max_q, max_k, 128, dt,
+                                   1, ctypes.c_float(0.1), ws, ws_bytes, None)
+    assert bv(cu_q=None) == 1
+    assert bv(cu_k=P + 1) == 1
+    assert bv(max_q=101) == 1
+    assert bv(max_k=201) == 1
+    assert bv(ws_bytes=need - 1) == 3
+    assert bv(ws=None) == 3
+    assert bv(dt=0) == 2
+
+
 def test_decode_plan_and_validation():
     s = lib.attn_decode_auto_splits(64, 32, 8, 8192, 128)
     assert 1 <= s <= 64

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from synth import default_scale, make_prefill, make_varlen
-from tests._util import assert_fwd_ok, fwd_errors, to_dev, to_host64
+from tests._util import BWD_REL_L2, assert_fwd_ok, fwd_errors, rel_l2, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -159,3 +159,61 @@ def test_fwd_varlen_equal_lengths_is_attn_fwd_bitwise(gpu_lib, d):
         torch.cuda.synchronize()
         assert torch.equal(fold(o1), o2)
         assert torch.equal(l1.transpose(0, 1).reshape(H, B * N), l2)
+
+
+# ----------------------------------------------------------------------------- packed backward
+def run_varlen_fwd_bwd(lib, x, causal, scale):
+    import torch
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "dout"))
+    cq, ck = torch.from_numpy(x["cu_q"]).cuda(), torch.from_numpy(x["cu_k"]).cuda()
+    max_q, max_k = int(np.diff(x["cu_q"]).max()), int(np.diff(x["cu_k"]).max())
+    o, lse = lib.attn_fwd_varlen(q, k, v, cq, ck, max_q, causal, scale)
+    grads = lib.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, max_q, max_k, causal, scale)
+    torch.cuda.synchronize()
+    return [to_host64(g) for g in grads]
+
+
+@pytest.mark.parametrize("case", sorted(VARLEN_CASES))
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen(gpu_lib, case, d, causal):
+    print(f"bwd_varlen {case} d={d} causal={causal}", flush=True)
+    lq, lk = VARLEN_CASES[case]
+    x = make_varlen(lq, lk, 4, 2, d, "bf16", seed=2800 + d, with_dout=True)
+    scale = default_scale(d)
+    dq, dk, dv = run_varlen_fwd_bwd(gpu_lib, x, causal, scale)
+    ref = oracle.backward_varlen(x["q"], x["k"], x["v"], x["dout"], x["cu_q"], x["cu_k"], scale, causal)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        err = rel_l2(g, r)
+        assert err <= BWD_REL_L2, (case, d, causal, name, err)
+    # Rows the mask leaves without any gradient: queries that see no key (no keys, or causal
+    # with i < Nq - Nk) and keys of sequences without queries must be exactly 0.
+    q_dead = np.zeros(x["q"].shape[1], bool)
+    k_dead = np.zeros(x["k"].shape[1], bool)
+    for b, (nq, nk) in enumerate(zip(lq, lk)):
+        q0, k0 = x["cu_q"][b], x["cu_k"][b]
+        if nk == 0:
+            q_dead[q0:q0 + nq] = True
+        elif causal and nq > nk:
+            q_dead[q0:q0 + nq - nk] = True
+        if nq == 0:
+            k_dead[k0:k0 + nk] = True
+    assert np.all(dq[:, q_dead] == 0.0) and np.all(dk[:, k_dead] == 0.0) and np.all(dv[:, k_dead] == 0.0), case
+
+
+def test_bwd_varlen_equal_lengths_is_attn_bwd_bitwise(gpu_lib):
+    """Equal lengths packed with the batch folded into the rows: same tiles as the dense backward."""
+    import torch
+    B, H, N, d = 2, 4, 333, 128
+    inp = make_prefill(B, H, H, N, d, "bf16", seed=2900, with_dout=True)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
+    fold = lambda t: t.transpose(0, 1).reshape(t.shape[1], B * t.shape[2], *t.shape[3:]).contiguous()
+    cu = torch.arange(0, B * N + 1, N, dtype=torch.int32, device=q.device)
+    for causal in (False, True):
+        o, lse = gpu_lib.attn_fwd(q, k, v, causal, default_scale(d))
+        g1 = gpu_lib.attn_bwd(q, k, v, o, lse, do, causal, default_scale(d))
+        g2 = gpu_lib.attn_bwd_varlen(fold(q), fold(k), fold(v), fold(o), fold(lse), fold(do), cu, cu, N, N, causal,
+                                     default_scale(d))
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(fold(a), b)

@@ -596,3 +596,59 @@ def test_blocksparse_brute_force_tiny():
             for c in range(d):
                 ref = math.fsum(math.exp(s[t] - m) / z * v[j, c] for t, j in enumerate(keys))
                 assert abs(o[0, 0, i, c] - ref) <= 1e-13
+
+
+# ----------------------------------------------------------------------------- packed backward
+def _loss_kv(q, k, v, dout, scale, causal):
+    o, _ = oracle.forward_kv(q, k, v, scale, causal)
+    return float(np.sum(o * dout))
+
+
+@pytest.mark.parametrize("Nq,Nk", [(3, 7), (6, 4), (5, 5)])
+def test_backward_kv_matches_central_differences(Nq, Nk):
+    """Gradient of the (pinned) forward_kv, bottom-right causal mask, grouped-query heads; with
+    Nk < Nq the rows that see no key must get dQ = 0."""
+    rng = np.random.default_rng(120 + Nq)
+    B, Hq, Hkv, d, scale, eps = 1, 2, 1, 3, 0.7, 1e-6
+    q, k, v = rng.standard_normal((B, Hq, Nq, d)), rng.standard_normal((B, Hkv, Nk, d)), rng.standard_normal((B, Hkv, Nk, d))
+    do = rng.standard_normal((B, Hq, Nq, d))
+    dq, dk, dv = oracle.backward_kv(q, k, v, do, scale, True)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            lp = _loss_kv(**{**args, name: xp}, dout=do, scale=scale, causal=True)
+            lm = _loss_kv(**{**args, name: xm}, dout=do, scale=scale, causal=True)
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7, err_msg=name)
+    if Nk < Nq:
+        assert np.all(dq[:, :, :Nq - Nk] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_varlen_equals_per_sequence_and_dense(causal):
+    Hq, Hkv, d = 4, 2, 5
+    lens_q, lens_k = [4, 0, 9, 2], [6, 3, 9, 0]
+    x = make_varlen(lens_q, lens_k, Hq, Hkv, d, "f32", seed=125)
+    rng = np.random.default_rng(126)
+    do = rng.standard_normal(x["q"].shape)
+    dq, dk, dv = oracle.backward_varlen(x["q"], x["k"], x["v"], do, x["cu_q"], x["cu_k"], 0.5, causal)
+    cq, ck = x["cu_q"], x["cu_k"]
+    for b in range(len(lens_q)):
+        sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        g = oracle.backward_kv(x["q"][None, :, sq], x["k"][None, :, sk], x["v"][None, :, sk], do[None, :, sq], 0.5,
+                               causal)
+        np.testing.assert_array_equal(dq[:, sq], g[0][0])
+        np.testing.assert_array_equal(dk[:, sk], g[1][0])
+        np.testing.assert_array_equal(dv[:, sk], g[2][0])
+    B, N = 3, 7
+    y = make_prefill(B, Hq, Hkv, N, d, "f32", seed=127, with_dout=True)
+    gd = oracle.backward(y["q"], y["k"], y["v"], y["dout"], 0.5, causal)
+    fold = lambda t: np.ascontiguousarray(t.transpose(1, 0, 2, 3).reshape(t.shape[1], B * N, d))
+    cu = np.arange(0, B * N + 1, N, dtype=np.int32)
+    gp = oracle.backward_varlen(fold(y["q"]), fold(y["k"]), fold(y["v"]), fold(y["dout"]), cu, cu, 0.5, causal)
+    for a, b in zip(gp, gd):
+        np.testing.assert_allclose(a, fold(b), rtol=1e-12, atol=1e-13)
