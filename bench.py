@@ -11,7 +11,7 @@ Reported value: forward+backward TFLOP/s with the algorithmic count 4 N^2 d per 
 algorithmic HBM GB/s (K + V + Q + O + LSE bytes).  Phase times come from HIP events on the
 stream the kernels run on.  The fp64 CPU oracle is timed beside it on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
 from __future__ import annotations
 
@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary workloads (chunked prefill, packed, block-sparse, d=64, "
+                         "variable-length decode) so that a profile holds the timed step only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -201,82 +204,111 @@ def main():
     ms_fwd, ms_bwd, ms_dec = (float(np.mean(x)) for x in (t_fwd, t_bwd, t_dec))
     ms_step = float(np.mean(t_step))
 
-    # Variable-length decode, outside the timed step: same cache, lengths vlens.
-    for _ in range(3):
-        attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
-    vev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    reps = 10
-    vev[0].record(stream)
-    for _ in range(reps):
-        attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
-    vev[1].record(stream)
-    torch.cuda.synchronize()
-    ms_vdec = vev[0].elapsed_time(vev[1]) / reps
-    vdec_bytes = int(vlens.sum()) * DHkv * d * 2 * 2 + 2 * DB * DHq * d * 2 + DB * DHq * 4
-
-    # Secondary forward lines, outside the timed step, FLOPs = 4 d per (query, key) pair the
-    # mask keeps.  Chunked prefill: a 1024-token chunk appended to 7168 cached tokens
-    # (Nk = 8192, causal aligned at the bottom right), B=4, Hq=32, Hkv=8, d=128.
-    def time_call(fn, reps=10):
+    # Secondary lines (skipped with --no-extras, e.g. under a profiler): each timed on its own,
+    # outside the timed step.
+    extras = {}
+    if not args.no_extras:
+        # Variable-length decode, outside the timed step: same cache, lengths vlens.
         for _ in range(3):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
+            attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
+        vev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 10
+        vev[0].record(stream)
         for _ in range(reps):
-            fn()
-        ev[1].record(stream)
+            attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
+        vev[1].record(stream)
         torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / reps
+        ms_vdec = vev[0].elapsed_time(vev[1]) / reps
+        vdec_bytes = int(vlens.sum()) * DHkv * d * 2 * 2 + 2 * DB * DHq * d * 2 + DB * DHq * 4
 
-    log("chunked prefill and packed variable-length forward")
-    CB, CHq, CHkv, CNq, CNk = 4, 32, 8, 1024, 8192
-    ch = make_prefill(CB, CHq, CHkv, CNq, d, "bf16", seed=1007, L=CNk)
-    cq, ck, cv = (to_dev(ch[x]) for x in ("q", "k", "v"))
-    del ch
-    co = torch.empty_like(cq)
-    clse = torch.empty((CB, CHq, CNq), dtype=torch.float32, device=dev)
-    ms_chunk = time_call(lambda: attn.attn_fwd_kv(cq, ck, cv, True, scale, o=co, lse=clse))
-    chunk_pairs = CNq * (CNk - CNq) + CNq * (CNq + 1) // 2
-    f_chunk = 4.0 * d * CB * CHq * chunk_pairs
-    del cq, ck, cv, co, clse
-    # Packed batch: 12 sequences, lengths uniform in [256, 4096] (seed 1008), H=16, d=128, causal.
-    vl = np.random.default_rng(1008).integers(256, 4097, 12)
-    VH = 16
-    px = make_varlen(vl, vl, VH, VH, d, "bf16", seed=1009, with_dout=True)
-    pq, pk, pv, pdo = (to_dev(px[x]) for x in ("q", "k", "v", "dout"))
-    pcu = torch.from_numpy(px["cu_q"]).to(dev)
-    del px
-    po = torch.empty_like(pq)
-    plse = torch.empty((VH, int(vl.sum())), dtype=torch.float32, device=dev)
-    ms_varlen = time_call(lambda: attn.attn_fwd_varlen(pq, pk, pv, pcu, pcu, int(vl.max()), True, scale, o=po,
-                                                      lse=plse))
-    f_varlen = 4.0 * d * VH * float(sum(int(n) * (int(n) + 1) // 2 for n in vl))
-    pg = [torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)]
-    pws = torch.empty(attn.attn_bwd_varlen_workspace_bytes(len(vl), VH, int(vl.sum())), dtype=torch.uint8, device=dev)
-    ms_varlen_bwd = time_call(lambda: attn.attn_bwd_varlen(pq, pk, pv, po, plse, pdo, pcu, pcu, int(vl.max()),
-                                                          int(vl.max()), True, scale, dq=pg[0], dk=pg[1], dv=pg[2],
-                                                          workspace=pws))
-    del pq, pk, pv, po, plse, pdo, pg, pws
-    # Block-sparse: B=1, H=32, N=16384, d=128, causal; query block i keeps key blocks i-7 .. i
-    # and block 0 (128x128 blocks), i.e. a 1024-key window plus the first block.
-    SH, SN = 32, 16384
-    sp = make_prefill(1, SH, SH, SN, d, "bf16", seed=1010)
-    sq_, sk_, sv_ = (to_dev(sp[x]) for x in ("q", "k", "v"))
-    del sp
-    nbk = SN // 128
-    bi, bj = np.meshgrid(np.arange(nbk), np.arange(nbk), indexing="ij")
-    smask = ((((bi - bj) >= 0) & ((bi - bj) < 8)) | (bj == 0)).astype(np.uint8)
-    smask_dev = torch.from_numpy(smask).to(dev)
-    so = torch.empty_like(sq_)
-    slse = torch.empty((1, SH, SN), dtype=torch.float32, device=dev)
-    ms_sparse = time_call(lambda: attn.attn_fwd_blocksparse(sq_, sk_, sv_, smask_dev, True, scale, o=so, lse=slse))
-    # Kept (query, key) pairs: whole kept blocks below the diagonal, plus the causal half (with
-    # the diagonal) of each diagonal block.
-    off = int(np.sum(smask * (bi > bj)))
-    sparse_pairs = off * 128 * 128 + nbk * 128 * 129 // 2
-    f_sparse = 4.0 * d * SH * sparse_pairs
-    del sq_, sk_, sv_, so, slse
+        # Secondary forward lines, outside the timed step, FLOPs = 4 d per (query, key) pair the
+        # mask keeps.  Chunked prefill: a 1024-token chunk appended to 7168 cached tokens
+        # (Nk = 8192, causal aligned at the bottom right), B=4, Hq=32, Hkv=8, d=128.
+        def time_call(fn, reps=10):
+            for _ in range(3):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(reps):
+                fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) / reps
 
+        log("chunked prefill and packed variable-length forward")
+        CB, CHq, CHkv, CNq, CNk = 4, 32, 8, 1024, 8192
+        ch = make_prefill(CB, CHq, CHkv, CNq, d, "bf16", seed=1007, L=CNk)
+        cq, ck, cv = (to_dev(ch[x]) for x in ("q", "k", "v"))
+        del ch
+        co = torch.empty_like(cq)
+        clse = torch.empty((CB, CHq, CNq), dtype=torch.float32, device=dev)
+        ms_chunk = time_call(lambda: attn.attn_fwd_kv(cq, ck, cv, True, scale, o=co, lse=clse))
+        chunk_pairs = CNq * (CNk - CNq) + CNq * (CNq + 1) // 2
+        f_chunk = 4.0 * d * CB * CHq * chunk_pairs
+        del cq, ck, cv, co, clse
+        # Packed batch: 12 sequences, lengths uniform in [256, 4096] (seed 1008), H=16, d=128, causal.
+        vl = np.random.default_rng(1008).integers(256, 4097, 12)
+        VH = 16
+        px = make_varlen(vl, vl, VH, VH, d, "bf16", seed=1009, with_dout=True)
+        pq, pk, pv, pdo = (to_dev(px[x]) for x in ("q", "k", "v", "dout"))
+        pcu = torch.from_numpy(px["cu_q"]).to(dev)
+        del px
+        po = torch.empty_like(pq)
+        plse = torch.empty((VH, int(vl.sum())), dtype=torch.float32, device=dev)
+        ms_varlen = time_call(lambda: attn.attn_fwd_varlen(pq, pk, pv, pcu, pcu, int(vl.max()), True, scale, o=po,
+                                                          lse=plse))
+        f_varlen = 4.0 * d * VH * float(sum(int(n) * (int(n) + 1) // 2 for n in vl))
+        pg = [torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)]
+        pws = torch.empty(attn.attn_bwd_varlen_workspace_bytes(len(vl), VH, int(vl.sum())), dtype=torch.uint8, device=dev)
+        ms_varlen_bwd = time_call(lambda: attn.attn_bwd_varlen(pq, pk, pv, po, plse, pdo, pcu, pcu, int(vl.max()),
+                                                              int(vl.max()), True, scale, dq=pg[0], dk=pg[1], dv=pg[2],
+                                                              workspace=pws))
+        del pq, pk, pv, po, plse, pdo, pg, pws
+        # Block-sparse: B=1, H=32, N=16384, d=128, causal; query block i keeps key blocks i-7 .. i
+        # and block 0 (128x128 blocks), i.e. a 1024-key window plus the first block.
+        SH, SN = 32, 16384
+        sp = make_prefill(1, SH, SH, SN, d, "bf16", seed=1010)
+        sq_, sk_, sv_ = (to_dev(sp[x]) for x in ("q", "k", "v"))
+        del sp
+        nbk = SN // 128
+        bi, bj = np.meshgrid(np.arange(nbk), np.arange(nbk), indexing="ij")
+        smask = ((((bi - bj) >= 0) & ((bi - bj) < 8)) | (bj == 0)).astype(np.uint8)
+        smask_dev = torch.from_numpy(smask).to(dev)
+        so = torch.empty_like(sq_)
+        slse = torch.empty((1, SH, SN), dtype=torch.float32, device=dev)
+        ms_sparse = time_call(lambda: attn.attn_fwd_blocksparse(sq_, sk_, sv_, smask_dev, True, scale, o=so, lse=slse))
+        # Kept (query, key) pairs: whole kept blocks below the diagonal, plus the causal half (with
+        # the diagonal) of each diagonal block.
+        off = int(np.sum(smask * (bi > bj)))
+        sparse_pairs = off * 128 * 128 + nbk * 128 * 129 // 2
+        f_sparse = 4.0 * d * SH * sparse_pairs
+        del sq_, sk_, sv_, so, slse
+
+        # Batched prefill, d=64: B=4, H=16, N=1024, causal, with LSE (seed 1002).
+        bp = make_prefill(4, 16, 16, 1024, 64, "bf16", seed=1002)
+        bq, bk, bv = (to_dev(bp[x]) for x in ("q", "k", "v"))
+        del bp
+        bo = torch.empty_like(bq)
+        blse = torch.empty((4, 16, 1024), dtype=torch.float32, device=dev)
+        ms_pre64 = time_call(lambda: attn.attn_fwd(bq, bk, bv, True, default_scale(64), o=bo, lse=blse))
+        f_pre64 = flops_fwd(4, 16, 1024, 64, True)
+        del bq, bk, bv, bo, blse
+        extras = {
+            "decode_varlen": {"GBps": vdec_bytes / (ms_vdec * 1e-3) / 1e9, "ms": ms_vdec,
+                              "lengths": "uniform in [L/2, L], seed 1006, mean %.0f" % float(vlens.mean())},
+            "fwd_chunk": {"TFLOPs": f_chunk / (ms_chunk * 1e-3) / 1e12, "ms": ms_chunk,
+                          "workload": "attn_fwd_kv B=4 Hq=32 Hkv=8 Nq=1024 Nk=8192 d=128 causal (bottom right)"},
+            "fwd_blocksparse": {"TFLOPs": f_sparse / (ms_sparse * 1e-3) / 1e12, "ms": ms_sparse,
+                                "workload": "attn_fwd_blocksparse B=1 H=32 N=16384 d=128 causal, 128x128 blocks: "
+                                            "8-block band + first block (%.1f%% of causal pairs kept)"
+                                            % (100.0 * sparse_pairs / (SN * (SN + 1) / 2))},
+            "fwd_varlen": {"TFLOPs": f_varlen / (ms_varlen * 1e-3) / 1e12, "ms": ms_varlen,
+                           "bwd_TFLOPs": 2.5 * f_varlen / (ms_varlen_bwd * 1e-3) / 1e12, "bwd_ms": ms_varlen_bwd,
+                           "workload": "attn_fwd_varlen 12 packed sequences, lengths uniform in [256, 4096] "
+                                       "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},
+            "fwd_prefill_d64": {"TFLOPs": f_pre64 / (ms_pre64 * 1e-3) / 1e12, "ms": ms_pre64,
+                                "workload": "attn_fwd B=4 H=16 N=1024 d=64 causal with LSE"},
+        }
     f_fwd = flops_fwd(B, H, N, d, True)
     f_bwd = 2.5 * f_fwd
     tflops = (f_fwd + f_bwd) / ((ms_fwd + ms_bwd) * 1e-3) / 1e12
@@ -324,18 +356,7 @@ def main():
                                "B=64 Hq=32 Hkv=8 L=8192 d=128", "parallelism": "none (one GPU)"},
         "fwd_TFLOPs": f_fwd / (ms_fwd * 1e-3) / 1e12, "bwd_TFLOPs": f_bwd / (ms_bwd * 1e-3) / 1e12,
         "decode_GBps": dec_gbs,
-        "decode_varlen": {"GBps": vdec_bytes / (ms_vdec * 1e-3) / 1e9, "ms": ms_vdec,
-                          "lengths": "uniform in [L/2, L], seed 1006, mean %.0f" % float(vlens.mean())},
-        "fwd_chunk": {"TFLOPs": f_chunk / (ms_chunk * 1e-3) / 1e12, "ms": ms_chunk,
-                      "workload": "attn_fwd_kv B=4 Hq=32 Hkv=8 Nq=1024 Nk=8192 d=128 causal (bottom right)"},
-        "fwd_blocksparse": {"TFLOPs": f_sparse / (ms_sparse * 1e-3) / 1e12, "ms": ms_sparse,
-                            "workload": "attn_fwd_blocksparse B=1 H=32 N=16384 d=128 causal, 128x128 blocks: "
-                                        "8-block band + first block (%.1f%% of causal pairs kept)"
-                                        % (100.0 * sparse_pairs / (SN * (SN + 1) / 2))},
-        "fwd_varlen": {"TFLOPs": f_varlen / (ms_varlen * 1e-3) / 1e12, "ms": ms_varlen,
-                       "bwd_TFLOPs": 2.5 * f_varlen / (ms_varlen_bwd * 1e-3) / 1e12, "bwd_ms": ms_varlen_bwd,
-                       "workload": "attn_fwd_varlen 12 packed sequences, lengths uniform in [256, 4096] "
-                                   "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},
+        **extras,
         "ms": {"fwd": ms_fwd, "bwd": ms_bwd, "decode": ms_dec, "fwd_min": min(t_fwd), "bwd_min": min(t_bwd),
                "decode_min": min(t_dec), "wall_per_step": wall / args.steps * 1e3},
         "roofline": roofline, "roofline_bwd": roofline_bwd, "roofline_decode": roofline_decode,
