@@ -44,6 +44,11 @@
 #ifndef XATTN_FWD128_WPE
 #define XATTN_FWD128_WPE 2
 #endif
+// d = 64 through the interleaved kernel (256-row tiles): measured 5-15% faster at N = 4096 but
+// 13% slower on 4 x 16 heads of N = 1024 (half as many workgroups), so off by default.
+#ifndef XATTN_FWD64_ILV
+#define XATTN_FWD64_ILV 0
+#endif
 #ifndef XATTN_FWD64_NQ
 #define XATTN_FWD64_NQ 1
 #endif
@@ -906,6 +911,12 @@ hipError_t launch_fwd(const FwdArgs& a) {
   if (a.d == 128) {
     using S = IlvShape<128, XATTN_ILV_RB>;
     return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, XATTN_ILV_RB), S::BM, S::NW * 64, a);
+  }
+#endif
+#if XATTN_FWD64_ILV
+  if (a.d == 64) {
+    using S = IlvShape<64, 1>;
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, 1), S::BM, S::NW * 64, a);
   }
 #endif
   if (a.d == 128) {
