@@ -284,6 +284,19 @@ def main():
         f_sparse = 4.0 * d * SH * sparse_pairs
         del sq_, sk_, sv_, so, slse
 
+        # Multi-token decode: 4 tokens per sequence on the decode cache (16 (token, head) rows per
+        # KV head), causal, seed 1011 for the queries.
+        MT = 4
+        mq = torch.from_numpy(np.ascontiguousarray(make_prefill(DB, DHq, DHkv, MT, d, "bf16", seed=1011)["q"])
+                              .view(np.int16)).view(torch.bfloat16).to(dev)
+        mo = torch.empty_like(mq)
+        mlse = torch.empty((DB, DHq, MT), dtype=torch.float32, device=dev)
+        mws = torch.empty(attn.attn_decode_multi_workspace_bytes(DB, DHq, DHkv, MT, DL, d, 0), dtype=torch.uint8,
+                          device=dev)
+        ms_mdec = time_call(lambda: attn.attn_decode_multi(mq, dk_, dv_, scale, causal=True, o=mo, lse=mlse,
+                                                           workspace=mws))
+        mdec_bytes = 2 * DB * DHkv * DL * d * 2 + 2 * DB * DHq * MT * d * 2 + DB * DHq * MT * 4
+        del mq, mo, mlse, mws
         # Batched prefill, d=64: B=4, H=16, N=1024, causal, with LSE (seed 1002).
         bp = make_prefill(4, 16, 16, 1024, 64, "bf16", seed=1002)
         bq, bk, bv = (to_dev(bp[x]) for x in ("q", "k", "v"))
@@ -306,7 +319,9 @@ def main():
                            "bwd_TFLOPs": 2.5 * f_varlen / (ms_varlen_bwd * 1e-3) / 1e12, "bwd_ms": ms_varlen_bwd,
                            "workload": "attn_fwd_varlen 12 packed sequences, lengths uniform in [256, 4096] "
                                        "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},
-            "fwd_prefill_d64": {"TFLOPs": f_pre64 / (ms_pre64 * 1e-3) / 1e12, "ms": ms_pre64,
+            "decode_multi": {"GBps": mdec_bytes / (ms_mdec * 1e-3) / 1e9, "ms": ms_mdec,
+                         "workload": "attn_decode_multi B=64 Hq=32 Hkv=8 T=4 L=8192 d=128 causal"},
+        "fwd_prefill_d64": {"TFLOPs": f_pre64 / (ms_pre64 * 1e-3) / 1e12, "ms": ms_pre64,
                                 "workload": "attn_fwd B=4 H=16 N=1024 d=64 causal with LSE"},
         }
     f_fwd = flops_fwd(B, H, N, d, True)

@@ -23,6 +23,7 @@ EXPORTS = (
     "attn_fwd_blocksparse",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen", "attn_decode_auto_splits",
     "attn_decode_workspace_bytes", "attn_decode", "attn_decode_varlen",
+    "attn_decode_multi_workspace_bytes", "attn_decode_multi",
 )
 
 _lib = None
@@ -72,6 +73,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_decode_multi_workspace_bytes.restype = sz
+    lib.attn_decode_multi_workspace_bytes.argtypes = [i] * 7
+    lib.attn_decode_multi.restype = i
+    lib.attn_decode_multi.argtypes = [vp] * 6 + [i] * 8 + [f, i, vp, sz, vp]
     lib.attn_decode_varlen.restype = i
     lib.attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     _lib = lib
@@ -325,4 +330,34 @@ def attn_decode_varlen(q, k_cache, v_cache, seqlens, scale: float, num_splits: i
     _check(lib.attn_decode_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq,
                                   Hkv, L, d, _dtype_code(q), float(scale), int(num_splits), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, lse
+
+
+def attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, num_splits=0) -> int:
+    return int(load().attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, num_splits))
+
+
+def attn_decode_multi(q, k_cache, v_cache, scale: float, causal: bool = True, seqlens=None, num_splits: int = 0,
+                      o=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """T tokens per sequence: q [B,Hq,T,d] against caches [B,Hkv,L,d] (optional int32 seqlens [B]);
+    causal: token t sees keys j <= len - T + t."""
+    import torch
+    lib = load()
+    _require(q.dim() == 4 and k_cache.dim() == 4 and v_cache.dim() == 4, "q [B,Hq,T,d], caches [B,Hkv,L,d]")
+    for t in (q, k_cache, v_cache) + (() if seqlens is None else (seqlens,)):
+        _require(t.is_cuda and t.is_contiguous(), "inputs must be contiguous CUDA tensors")
+    B, Hq, T, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _require(tuple(k_cache.shape) == (B, Hkv, L, d) == tuple(v_cache.shape), "cache shape mismatch")
+    if seqlens is not None:
+        _require(tuple(seqlens.shape) == (B,) and seqlens.dtype == torch.int32, "seqlens must be int32 [B]")
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                 T, L, d, _dtype_code(q), int(bool(causal)), float(scale), int(num_splits),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, lse

@@ -260,19 +260,26 @@ int attn_decode_auto_splits(int B, int Hq, int Hkv, int L, int d) {
   return auto_splits(B, Hkv, L);
 }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int num_splits) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || d <= 0 || num_splits < 0) return 0;
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int L, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || L <= 0 || d <= 0 || num_splits < 0) return 0;
   int splits, kps;
   decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
-  const size_t rows = (size_t)splits * B * Hq;
+  const size_t rows = (size_t)splits * B * Hq * T;
   return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int num_splits) {
+  return attn_decode_multi_workspace_bytes(B, Hq, Hkv, 1, L, d, num_splits);
 }
 
 static attn_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
                                  void* o, float* lse, int B, int Hq, int Hkv, int L, int d, attn_dtype_t dtype,
-                                 float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                                 float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream,
+                                 int T = 1, int causal = 0) {
   if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-null");
+  if (T <= 0) return fail(ATTN_ERR_INVALID_ARG, "T must be positive (got %d)", T);
   RETURN_IF(check_heads(B, Hq, Hkv, L, d));
+  if ((long long)B * Hq * T > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "B*Hq*T exceeds 2^31-1");
   RETURN_IF(check_scale(scale));
   if (num_splits < 0) return fail(ATTN_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", num_splits);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || (lse && !aligned16(lse)))
@@ -281,17 +288,19 @@ static attn_status_t decode_impl(const void* q, const void* k_cache, const void*
                                       "decode supports bf16 only");
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
   if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", Hq / Hkv);
-  const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, L, d, num_splits);
+  if (T * (Hq / Hkv) > 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most 16 (token, head) rows per KV head (T=%d, group %d)", T, Hq / Hkv);
+  const size_t need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, num_splits);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "attn_decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   int splits, kps;
   decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
-  const size_t rows = (size_t)splits * B * Hq;
+  const size_t rows = (size_t)splits * B * Hq * T;
   float* part_o = (float*)workspace;
   float* part_lse = (float*)((char*)workspace + align_up(rows * d * sizeof(float), 256));
   xattn::DecodeArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, L, d, scale, splits, kps, part_o, part_lse,
-                      (hipStream_t)stream, seqlens};
+                      (hipStream_t)stream, seqlens, T, causal ? 1 : 0};
   return from_hip(xattn::launch_decode(a), "attn_decode launch");
 }
 
@@ -300,6 +309,15 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, nullptr, o, lse, B, Hq, Hkv, L, d, dtype, scale, num_splits, workspace,
                      workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_multi(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
+                                void* o, float* lse, int B, int Hq, int Hkv, int T, int L, int d, attn_dtype_t dtype,
+                                int causal, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (seqlens && !aligned16(seqlens)) return fail(ATTN_ERR_INVALID_ARG, "seqlens must be 16-byte aligned");
+  return decode_impl(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, L, d, dtype, scale, num_splits, workspace,
+                     workspace_bytes, stream, T, causal);
 }
 
 attn_status_t attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,

@@ -23,6 +23,9 @@
 //     cross-wave combine needs LDS.
 //   * Each chunk writes (O_s normalised, lse_s); the merge kernel combines the chunks with
 //     weights 2^(lse_s - max) — exact by the order independence of [OPT] §3.2.2.
+//   * Multi-token decode: T new tokens per sequence; the MFMA rows are the T x g (token,
+//     head) pairs of the group (at most 16), so the cache is still read once per group.  With
+//     the causal mask aligned at the bottom right, token t sees keys j <= len - T + t.
 #include <type_traits>
 #include <utility>
 
@@ -38,7 +41,7 @@ template <int D, int GP>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq, int Hkv, int L,
-    int splits, int keys_per_split, float scale_log2, const int* __restrict__ seqlens) {
+    int splits, int keys_per_split, float scale_log2, const int* __restrict__ seqlens, int T, int causal) {
   constexpr int EPL = D / 16;  // features per lane in the P V product
   constexpr int DC = D / 32;   // 32-wide feature chunks of the score MFMA
   __shared__ float s_m[kDecWaves][GP];
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int g = Hq / Hkv;
+  const int g = Hq / Hkv, R = T * g;  // MFMA row r < R: token r / g of head kvh*g + r % g
   const int split = blockIdx.x % splits;
   const int bk = blockIdx.x / splits;  // b * Hkv + kv head
   const int b = bk / Hkv, kvh = bk - b * Hkv;
@@ -58,15 +61,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
   const uint16_t* kp = kc + (size_t)bk * L * D;
   const uint16_t* vp = vc + (size_t)bk * L * D;
 
+  // Causal: the last key row col's token sees (rows past R see every key; they are never
+  // written).
+  const int ctok = col / g;
+  const int klast = (causal && col < R) ? len - T + ctok : L;
   bf16x8 qB[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     u32x4 u = {0u, 0u, 0u, 0u};
-    if (col < g) u = ld_global16(q + (size_t)(b * Hq + kvh * g + col) * D + 32 * c + 8 * grp);
+    if (col < R)
+      u = ld_global16(q + ((size_t)(b * Hq + kvh * g + col - ctok * g) * T + ctok) * D + 32 * c + 8 * grp);
     qB[c] = as_bf16x8(u);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // The running max starts finite (kMaxInit), so rows whose keys a chunk masks entirely get
+  // probability 0 there, and a row without any key ends with l = 0.
+  float m_run = kMaxInit, l_run = 0.f;
   float acc[GP][EPL];
 #pragma unroll
   for (int h = 0; h < GP; ++h)
@@ -113,7 +123,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (k0 + blk * 16 + 4 * grp + r >= kend) sc[blk][r] = -INFINITY;
+        const int key = k0 + blk * 16 + 4 * grp + r;
+        if (key >= kend || key > klast) sc[blk][r] = -INFINITY;
         mx = fmaxf(mx, sc[blk][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
     // Lazy reference max (as in the forward kernel): move m_run and rescale only when some
     // head's chunk max exceeds it by more than 2^kDecLazy; the result is unchanged.
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kDecLazy) != 0) {
-      const float m_new = fmaxf(m_run, mx);  // finite: the chunk holds >= 1 valid key
+      const float m_new = fmaxf(m_run, mx);  // finite: m_run starts at kMaxInit
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -181,23 +192,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
     s_l[wave][lane] = l_tot;
   }
   __syncthreads();
-  for (int i = tid; i < g * D; i += kDecWaves * 64) {
-    const int h = i / D, d = i - h * D;
-    float M = -INFINITY;
+  for (int i = tid; i < R * D; i += kDecWaves * 64) {
+    const int h = i / D, d = i - h * D;  // MFMA row h: token h / g, head kvh*g + h % g
+    float M = kMaxInit;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      if (s_m[w][h] != -INFINITY) {
-        const float wt = fast_exp2(s_m[w][h] - M);
-        num = fmaf(wt, s_acc[w][h][d], num);
-        den = fmaf(wt, s_l[w][h], den);
-      }
+      const float wt = fast_exp2(s_m[w][h] - M);  // a wave that saw no key has l = 0
+      num = fmaf(wt, s_acc[w][h][d], num);
+      den = fmaf(wt, s_l[w][h], den);
     }
-    const size_t row = (size_t)(split * B + b) * Hq + kvh * g + h;
-    // A chunk past the sequence's end holds no key: partial O = 0, lse = -inf (weight 0).
-    const bool empty = M == -INFINITY;
+    const int tok = h / g;
+    const size_t row = ((size_t)(split * B + b) * Hq + kvh * g + h - tok * g) * T + tok;
+    // A chunk holding no key of this row: partial O = 0, lse = -inf (weight 0 in the merge).
+    const bool empty = !(den > 0.f);
     part_o[row * D + d] = empty ? 0.f : num / den;
     if (d == 0) part_lse[row] = empty ? -INFINITY : M + fast_log2(den);
   }
@@ -230,17 +240,17 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const float sl2 = a.scale * kLog2e;
   hipLaunchKernelGGL((decode_split_kernel<D, GP>), dim3(a.B * a.Hkv * a.splits), dim3(kDecWaves * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.part_o,
-                     a.part_lse, a.B, a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2, a.seqlens);
+                     a.part_lse, a.B, a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2, a.seqlens, a.T, a.causal);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, a.stream, a.part_o, a.part_lse,
-                     (uint16_t*)a.o, a.lse, a.B * a.Hq, a.splits);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hq * a.T), dim3(D), 0, a.stream, a.part_o, a.part_lse,
+                     (uint16_t*)a.o, a.lse, a.B * a.Hq * a.T, a.splits);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a) {
-  const int g = a.Hq / a.Hkv;
+  const int g = a.T * (a.Hq / a.Hkv);  // MFMA rows per group
   if (g <= 1) return launch_decode_t<D, 1>(a);
   if (g <= 2) return launch_decode_t<D, 2>(a);
   if (g <= 4) return launch_decode_t<D, 4>(a);

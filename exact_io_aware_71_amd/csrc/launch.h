@@ -48,6 +48,8 @@ struct DecodeArgs {
   float* part_lse;      // [splits, B, Hq] fp32 (base-2 log-sum-exp of the scaled scores)
   hipStream_t stream;
   const int* seqlens;   // [B] keys per sequence (device), clamped to [0, L]; null = L for all
+  int T;                // query tokens per sequence (T * Hq/Hkv <= 16); q/o [B,Hq,T,d]
+  int causal;           // token t sees keys j <= len - T + t
 };
 
 // Longest key sequence the block-sparse forward walks (its tile list holds 8192 tiles of 64).

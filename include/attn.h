@@ -221,6 +221,30 @@ attn_status_t attn_decode_varlen(const void* q, const void* k_cache, const void*
                                  int L, int d, attn_dtype_t dtype, float scale, int num_splits,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace attn_decode_multi needs for T tokens per sequence (0 splits = automatic,
+ * the same split choice as attn_decode). */
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int L, int d, int num_splits);
+
+/*
+ * Multi-token decode: T new tokens per sequence against its cache ([OPT] §4.2.2 for one token;
+ * T > 1 is the verification step of speculative decoding, between decode and the chunked
+ * prefill of attn_fwd_kv).  Same split-KV + LSE merge as attn_decode; the T tokens of all
+ * g = Hq/Hkv heads of a KV head are processed together, so the cache is read once per group.
+ *   q [B,Hq,T,d], o [B,Hq,T,d], lse [B,Hq,T] fp32 (optional)
+ *   k_cache/v_cache [B,Hkv,L,d]; seqlens [B] int32 device (16-byte aligned) or NULL for L
+ *   causal != 0   token t sees keys j <= len - T + t (the tokens are the last T cached
+ *                 positions of their sequence); causal == 0: every token sees all len keys
+ * A token that sees no key gets o = 0 and lse = -inf.  T = 1 computes what attn_decode (or,
+ * with seqlens, attn_decode_varlen) computes.
+ * Supported: BF16, d in {64, 128}, T * Hq/Hkv <= 16.  Workspace as
+ * attn_decode_multi_workspace_bytes().  Bitwise deterministic for a fixed split count.
+ */
+attn_status_t attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                                const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv,
+                                int T, int L, int d, attn_dtype_t dtype, int causal, float scale,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["upcast", "probabilities", "forward", "forward_kv", "forward_blocksparse", "forward_varlen", "forward_rows",
-           "backward", "backward_kv", "backward_varlen",
+           "backward", "backward_kv", "backward_varlen", "decode_multi",
            "decode", "split_kv_decode", "lse_merge", "attention_flops"]
 
 
@@ -295,6 +295,25 @@ def decode(q, k_cache, v_cache, scale: float, seqlens=None):
             kk, vv = upcast(k_cache[b, kv, :n]), upcast(v_cache[b, kv, :n])
             p, lse[b, rows] = _softmax_rows(_scores(qg, kk, scale, False))
             o[b, rows] = p @ vv
+    return o, lse
+
+
+def decode_multi(q, k_cache, v_cache, scale: float, causal: bool, seqlens=None):
+    """T query tokens per sequence against its cache: q [B,Hq,T,d], caches [B,Hkv,L,d].
+
+    Sequence b holds seqlens[b] keys (clamped to [0, L]; all L without seqlens) and its T
+    tokens are the last T of them, so this is forward_kv of the T queries against those keys
+    (causal aligned at the bottom right: token t sees keys j <= len - T + t).  T = 1 is
+    decode ([OPT] §4.2.2).  Returns O [B,Hq,T,d], LSE [B,Hq,T].
+    """
+    B, Hq, T, d = np.asarray(q).shape
+    L = np.asarray(k_cache).shape[2]
+    o = np.zeros((B, Hq, T, np.asarray(v_cache).shape[3]))
+    lse = np.full((B, Hq, T), -np.inf)
+    for b in range(B):
+        n = L if seqlens is None else min(max(int(seqlens[b]), 0), L)
+        ob, lb = forward_kv(q[b:b + 1], k_cache[b:b + 1, :, :n], v_cache[b:b + 1, :, :n], scale, causal)
+        o[b], lse[b] = ob[0], lb[0]
     return o, lse
 
 

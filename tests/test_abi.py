@@ -146,6 +146,14 @@ def test_decode_plan_and_validation():
     assert dec(ws_bytes=need - 4) == 3
     assert dec(scale=float("inf")) == 1
 
+    def decm(T=4, Hq=32, Hkv=8, seqlens=P):
+        return lib.attn_decode_multi(P, P, P, seqlens, P, P, 64, Hq, Hkv, T, 8192, 128, 1, 1, ctypes.c_float(0.1), 0, P,
+                                     1 << 30, None)
+    assert decm(T=0) == 1
+    assert decm(T=5) == 2            # 5 tokens x 4 heads > 16 rows
+    assert decm(seqlens=P + 4) == 1  # misaligned
+    assert lib.attn_decode_multi_workspace_bytes(64, 32, 8, 4, 8192, 128, 0) >= 4 * need - 1024
+
     def decv(seqlens=P, d=128):
         return lib.attn_decode_varlen(P, P, P, seqlens, P, P, 64, 32, 8, 8192, d, 1, ctypes.c_float(0.1), 0, P,
                                       need, None)

@@ -299,3 +299,54 @@ def test_bwd_from_oracle_forward(gpu_lib):
     dq, dk, dv = gpu_lib.attn_bwd(q, k, v, o, lse, do, True, scale)
     torch.cuda.synchronize()
     check_bwd([to_host64(t) for t in (dq, dk, dv)], inp, scale, True, tag="oracle-fwd")
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+def run_decode_multi(lib, q, kc, vc, lens, causal, splits, scale):
+    import torch
+    sl = None if lens is None else torch.tensor(np.asarray(lens, dtype=np.int32)).cuda()
+    o, lse = lib.attn_decode_multi(to_dev(q), to_dev(kc), to_dev(vc), scale, causal=causal, seqlens=sl,
+                                   num_splits=splits)
+    torch.cuda.synchronize()
+    return to_host64(o), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("T,Hq,Hkv", [(1, 8, 2), (2, 8, 2), (4, 8, 2), (3, 10, 2), (16, 4, 4)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [0, 3, 16])
+def test_decode_multi(gpu_lib, T, Hq, Hkv, d, causal, splits):
+    from tests.test_gpu_kv_varlen import check_rows
+    print(f"decode_multi T={T} Hq={Hq} Hkv={Hkv} d={d} causal={causal} splits={splits}", flush=True)
+    B, L = 6, 1000
+    rng = np.random.default_rng(4000 + T + d)
+    x = make_prefill(B, Hq, Hkv, T, d, "bf16", seed=4100 + T * Hq + d, qk_mult=2.0, L=L)
+    lens = [1000, 0, 1, T - 1 if T > 1 else 2, 33, int(rng.integers(2, L))]
+    scale = default_scale(d)
+    o, lse = run_decode_multi(gpu_lib, x["q"], x["k"], x["v"], lens, causal, splits, scale)
+    o_ref, lse_ref = oracle.decode_multi(x["q"], x["k"], x["v"], scale, causal, seqlens=lens)
+    check_rows(o, lse, o_ref, lse_ref, f"T={T} d={d} causal={causal} splits={splits}")
+
+
+def test_decode_multi_single_token_is_decode_bitwise(gpu_lib, decode_inputs):
+    import torch
+    _, inp = decode_inputs
+    q, kc, vc = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    scale = default_scale(128)
+    o1, l1 = gpu_lib.attn_decode(q, kc, vc, scale)
+    o2, l2 = gpu_lib.attn_decode_multi(q[:, :, None, :].contiguous(), kc, vc, scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[:, :, 0]) and torch.equal(l1, l2[:, :, 0])
+
+
+def test_decode_multi_full_size_sampled_batches(gpu_lib, decode_inputs):
+    """4 tokens per sequence on the decode cache (B=64, Hq=32, Hkv=8, L=8192): 16 (token, head)
+    rows per KV head; sampled batches against the oracle."""
+    _, inp = decode_inputs
+    T = 4
+    q = make_prefill(64, 32, 8, T, 128, "bf16", seed=4200)["q"]
+    scale = default_scale(128)
+    o, lse = run_decode_multi(gpu_lib, q, inp["k"], inp["v"], None, True, 0, scale)
+    for b in (0, 37, 63):
+        o_ref, lse_ref = oracle.decode_multi(q[b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1], scale, True)
+        assert_fwd_ok(fwd_errors(o[b:b + 1], o_ref, lse[b:b + 1], lse_ref), f"b{b}")

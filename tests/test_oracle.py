@@ -652,3 +652,29 @@ def test_backward_varlen_equals_per_sequence_and_dense(causal):
     gp = oracle.backward_varlen(fold(y["q"]), fold(y["k"]), fold(y["v"]), fold(y["dout"]), cu, cu, 0.5, causal)
     for a, b in zip(gp, gd):
         np.testing.assert_allclose(a, fold(b), rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+def test_decode_multi_pins():
+    """T = 1 is decode (with and without lengths); T causal tokens are the last T rows of the
+    causal forward over the sequence's keys; a sequence shorter than T leaves its first tokens
+    without keys."""
+    B, Hq, Hkv, L, d, T = 3, 4, 2, 21, 5, 3
+    rng = np.random.default_rng(130)
+    q, kc, vc = rng.standard_normal((B, Hq, T, d)), rng.standard_normal((B, Hkv, L, d)), rng.standard_normal((B, Hkv, L, d))
+    lens = [21, 2, 9]
+    o1, l1 = oracle.decode_multi(q[:, :, :1], kc, vc, 0.6, True, seqlens=lens)
+    od, ld = oracle.decode(q[:, :, 0], kc, vc, 0.6, seqlens=lens)
+    np.testing.assert_allclose(o1[:, :, 0], od, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1[:, :, 0], ld, rtol=1e-13)
+    o, lse = oracle.decode_multi(q, kc, vc, 0.6, True, seqlens=lens)
+    b, n = 2, lens[2]
+    qfull = np.concatenate([rng.standard_normal((1, Hq, n - T, d)), q[b:b + 1]], axis=2)
+    of, lf = oracle.forward(qfull, kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], 0.6, True)
+    np.testing.assert_allclose(o[b], of[0, :, n - T:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[b], lf[0, :, n - T:], rtol=1e-13)
+    assert np.all(lse[1, :, 0] == -np.inf) and np.all(o[1, :, 0] == 0.0)   # len 2 < T = 3
+    on, ln = oracle.decode_multi(q, kc, vc, 0.6, False, seqlens=lens)
+    for t in range(T):
+        od, ld = oracle.decode(q[:, :, t], kc, vc, 0.6, seqlens=lens)
+        np.testing.assert_allclose(on[:, :, t], od, rtol=1e-12, atol=1e-13)
