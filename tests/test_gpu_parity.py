@@ -350,3 +350,58 @@ def test_decode_multi_full_size_sampled_batches(gpu_lib, decode_inputs):
     for b in (0, 37, 63):
         o_ref, lse_ref = oracle.decode_multi(q[b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1], scale, True)
         assert_fwd_ok(fwd_errors(o[b:b + 1], o_ref, lse[b:b + 1], lse_ref), f"b{b}")
+
+
+# ----------------------------------------------------------------------------- HIP graph capture
+def test_hip_graph_replay_matches_eager(gpu_lib):
+    """Every entry point enqueues kernels only (no allocation, no memset), so a captured graph of
+    forward, backward, decode and the packed forward replays to the eager results bit for bit,
+    with eager work and synchronisation between replays."""
+    import torch
+    d = 128
+    scale = default_scale(d)
+    inp = make_prefill(1, 4, 2, 300, d, "bf16", seed=4300, with_dout=True)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
+    dec = make_decode(4, 8, 2, 1000, d, seed=4301)
+    dq_, dk_, dv_ = (to_dev(dec[n]) for n in ("q", "k", "v"))
+    from synth import make_varlen
+    px = make_varlen([5, 0, 300, 77], [5, 9, 300, 200], 4, 2, d, "bf16", seed=4302)
+    pq, pk, pv = (to_dev(px[n]) for n in ("q", "k", "v"))
+    cq, ck = torch.from_numpy(px["cu_q"]).cuda(), torch.from_numpy(px["cu_k"]).cuda()
+
+    o, lse = torch.empty_like(q), torch.empty((1, 4, 300), dtype=torch.float32, device="cuda")
+    g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    wsb = torch.empty(gpu_lib.attn_bwd_workspace_bytes(1, 4, 2, 300, d), dtype=torch.uint8, device="cuda")
+    od, ld = torch.empty_like(dq_), torch.empty((4, 8), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(gpu_lib.attn_decode_workspace_bytes(4, 8, 2, 1000, d, 3), dtype=torch.uint8, device="cuda")
+    po, pl = torch.empty_like(pq), torch.empty((4, pq.shape[1]), dtype=torch.float32, device="cuda")
+
+    def work():
+        gpu_lib.attn_fwd(q, k, v, True, scale, o=o, lse=lse)
+        gpu_lib.attn_bwd(q, k, v, o, lse, do, True, scale, dq=g[0], dk=g[1], dv=g[2], workspace=wsb)
+        gpu_lib.attn_decode(dq_, dk_, dv_, scale, num_splits=3, o=od, lse=ld, workspace=wsd)
+        gpu_lib.attn_fwd_varlen(pq, pk, pv, cq, ck, 300, True, scale, o=po, lse=pl)
+
+    outs = (o, lse, *g, od, ld, po, pl)
+    work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()  # warm-up on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), (rep, i)
+        del junk
