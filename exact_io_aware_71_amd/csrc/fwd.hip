@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // A wave whose queries all precede this tile has nothing to add (causal skip), nor one whose
     // query block drops it.
     const bool keep = !SPARSE || ((e >> (14 + (qw0 - q0) / kSparseBlock)) & 1) != 0;
-    const bool active = keep && (!CAUSAL || (t0 <= qd0 + NQ * 32 - 1));
+    const bool active = keep && qw0 < Nq && (!CAUSAL || (t0 <= qd0 + NQ * 32 - 1));
     if (active) {
       f32x16 s[KB][NQ];
 #pragma unroll
@@ -428,7 +428,10 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
   const uint16_t* vp = v + sr.k * D;
   const int qw0 = q0 + wave * (RB * 32);  // rows qw0 + 32 rb + l32
   // Causal masks align the last query with the last key: query i sees keys j <= i + Nk - Nq.
-  const int qd0 = qw0 + (Nk - Nq);        // last key visible to the wave's first row
+  // A wave without query rows (past the end of a shorter sequence) skips all its MFMA work:
+  // under the causal test its limit lies before every key.
+  const bool has_rows = qw0 < Nq;
+  const int qd0 = has_rows ? qw0 + (Nk - Nq) : -(1 << 29);  // last key visible to the wave's first row
 
   // Q^T operands: lane holds query qw0 + 32 rb + l32, features 16c + 8*h32 .. +7.
   bf16x8 qreg[RB][DC];
@@ -535,10 +538,12 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
       return *reinterpret_cast<const bf16x8*>(ks + ofs.k[j - NPV]);
     }
   };
-  // A wave has work in step u while key block u-1 still holds keys at or before its last row.
-  // (Block-sparse: always; dropped and masked blocks give probability 0.)
+  // A wave has work in step u if it holds a query row and key block u-1 still holds keys at
+  // or before its last row (block-sparse: every step; dropped and masked blocks give
+  // probability 0).
   auto active = [&](int u) __attribute__((always_inline)) {
-    return SPARSE || !CAUSAL || (u - 1) * 32 <= qd0 + RB * 32 - 1;
+    if constexpr (SPARSE || !CAUSAL) return has_rows;
+    else return (u - 1) * 32 <= qd0 + RB * 32 - 1;
   };
   auto kt = [&](int i) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) return entry(i) & 0x3fff;
