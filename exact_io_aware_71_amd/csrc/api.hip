@@ -264,7 +264,7 @@ size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int L, i
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || L <= 0 || d <= 0 || num_splits < 0) return 0;
   int splits, kps;
   decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
-  const size_t rows = (size_t)splits * B * Hq * T;
+  const size_t rows = (size_t)splits * xattn::decode_partials_per_split(T, Hq / Hkv) * B * Hq * T;
   return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
 }
 
@@ -287,16 +287,16 @@ static attn_status_t decode_impl(const void* q, const void* k_cache, const void*
   if (dtype != ATTN_BF16) return fail(dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG,
                                       "decode supports bf16 only");
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
-  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", Hq / Hkv);
-  if (T * (Hq / Hkv) > 16)
-    return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most 16 (token, head) rows per KV head (T=%d, group %d)", T, Hq / Hkv);
+  if (T * (Hq / Hkv) > xattn::kDecMaxRows)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most %d (token, head) rows per KV head (T=%d, group %d)",
+                xattn::kDecMaxRows, T, Hq / Hkv);
   const size_t need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, num_splits);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "attn_decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   int splits, kps;
   decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
-  const size_t rows = (size_t)splits * B * Hq * T;
+  const size_t rows = (size_t)splits * xattn::decode_partials_per_split(T, Hq / Hkv) * B * Hq * T;
   float* part_o = (float*)workspace;
   float* part_lse = (float*)((char*)workspace + align_up(rows * d * sizeof(float), 256));
   xattn::DecodeArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, L, d, scale, splits, kps, part_o, part_lse,

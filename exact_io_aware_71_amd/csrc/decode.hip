@@ -24,8 +24,10 @@
 //   * Each chunk writes (O_s normalised, lse_s); the merge kernel combines the chunks with
 //     weights 2^(lse_s - max) — exact by the order independence of [OPT] §3.2.2.
 //   * Multi-token decode: T new tokens per sequence; the MFMA rows are the T x g (token,
-//     head) pairs of the group (at most 16), so the cache is still read once per group.  With
-//     the causal mask aligned at the bottom right, token t sees keys j <= len - T + t.
+//     head) pairs of the group, so the cache is still read once per group.  With the causal
+//     mask aligned at the bottom right, token t sees keys j <= len - T + t.  Up to 8 rows the
+//     kernel below runs (P V on the vector ALU); from 9 to 32 rows decode_mma_kernel, whose
+//     P V runs on the matrix cores.
 #include <type_traits>
 #include <utility>
 
@@ -213,6 +215,151 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
   }
 }
 
+// Decode with up to 32 (token, head) rows per KV head on the matrix cores, as the forward
+// computes a 32-row block: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K rows straight from
+// global memory as the A operand, the rows' Q^T resident as the B operand), so that in the C
+// layout each lane owns one row and 16 keys; the probabilities are then already the B operand
+// of O^T += V^T P^T, whose V^T operand is read with the transposing ds_read_b64_tr_b16 from a
+// per-wave double-buffered LDS copy of the 32-key V block (direct global -> LDS, swizzled as
+// the forward's tiles).  Each of the four waves walks every fourth 32-key block of the
+// workgroup's chunk and writes its own partial (O_w, lse_w): the merge kernel combines
+// 4 x splits partials, exactly as it combines chunks.
+template <int D>
+__global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq, int Hkv, int L,
+    int splits, int keys_per_split, float scale_log2, const int* __restrict__ seqlens, int T, int causal) {
+  constexpr int DC = D / 16, DB = D / 32;
+  constexpr int VBYTES = 32 * D * 2;      // one 32-key V block
+  constexpr int NCP = VBYTES / 1024;      // 1 KB copies per block
+  constexpr int RPC = 1024 / (2 * D);     // rows per 1 KB copy
+  __shared__ __attribute__((aligned(1024))) char vbuf[kDecWaves * 2 * VBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  const int g = Hq / Hkv, R = T * g;
+  const int split = blockIdx.x % splits;
+  const int bk = blockIdx.x / splits;  // b * Hkv + kv head
+  const int b = bk / Hkv, kvh = bk - b * Hkv;
+  const int len = seqlens != nullptr ? min(max(seqlens[b], 0), L) : L;
+  const int kbeg = split * keys_per_split;
+  const int kend = max(kbeg, min(len, kbeg + keys_per_split));
+  const uint16_t* kp = kc + (size_t)bk * L * D;
+  const uint16_t* vp = vc + (size_t)bk * L * D;
+
+  // Row l32: token l32 / g of head kvh*g + l32 % g.  Q^T operand: features 16c + 8*h32 .. +7.
+  const int tok = l32 / g, hh = l32 - tok * g;
+  const bool row_ok = l32 < R;
+  const int klast = (causal && row_ok) ? len - T + tok : 0x7fffffff;  // last key of the row
+  bf16x8 qreg[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (row_ok) u = ld_global16(q + ((size_t)(b * Hq + kvh * g + hh) * T + tok) * D + 16 * c + 8 * h32);
+    qreg[c] = as_bf16x8(u);
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_run = kMaxInit, l_run = 0.f;
+
+  // V copies: 1 KB piece j of a block covers rows RPC*j ..; lane l fills physical chunk l,
+  // i.e. it reads logical chunk (l%(D/8)) ^ swizzle(row).  Rows past kend read row kend-1
+  // (finite data; their probabilities are 0).
+  const int lrow = lane / (D / 8);
+  const void* vbase = wave_uniform(vp);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)vbuf;
+  const uint32_t wdst = lds0 + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (2 * VBYTES);
+  const int nblk = (kend - kbeg + 31) / 32;
+  auto issue = [&](int blk, int stage, bf16x8 (&kop)[DC]) __attribute__((always_inline)) {
+    const int k0 = kbeg + 32 * blk;
+    const int key = min(k0 + l32, kend - 1);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) kop[c] = as_bf16x8(ld_global16(kp + (size_t)key * D + 16 * c + 8 * h32));
+#pragma unroll
+    for (int j = 0; j < NCP; ++j) {
+      const int r = RPC * j + lrow;
+      const int row = min(k0 + r, kend - 1);
+      const uint32_t off = (uint32_t)row * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(r, 0) >> 4) & (D / 8 - 1)));
+      dma16_m0(vbase, off, wdst + stage * VBYTES + 1024 * j);
+    }
+  };
+  // Block blk uses stage st and K operands kcur; the next block of this wave (blk + 4) is
+  // issued into the other stage and knxt first.  Two calls per loop trip keep the register
+  // sets static.
+  auto step = [&](int blk, int st, bf16x8 (&kcur)[DC], bf16x8 (&knxt)[DC]) __attribute__((always_inline)) {
+    if (blk + kDecWaves < nblk) {
+      issue(blk + kDecWaves, st ^ 1, knxt);
+      wait_vmem_n<DC + NCP>();
+    } else {
+      wait_vmem();
+    }
+    const int k0 = kbeg + 32 * blk;
+    f32x16 sv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) sv = mfma32(kcur[c], qreg[c], sv);
+    // Lane owns row l32; register r holds key k0 + 8(r/4) + 4*h32 + r%4.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      if (key >= kend || key > klast) sv[r] = -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = max_xor32(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kDecLazy) != 0) {  // lazy reference max
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sv[r] = fast_exp2(fmaf(sv[r], scale_log2, -m_run));
+      rs += sv[r];
+    }
+    l_run += rs;
+    const char* vs = vbuf + (wave * 2 + st) * VBYTES;
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(sv[8 * sh + 2 * e], sv[8 * sh + 2 * e + 1]);
+      const bf16x8 pb = as_bf16x8(u);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = mfma32(ld_tr_operand<D>(vs, 16 * sh, db * 32, lane), pb, acc[db]);
+    }
+  };
+  bf16x8 kA[DC], kB[DC];
+  if (wave < nblk) issue(wave, 0, kA);
+  for (int blk = wave; blk < nblk; blk += 2 * kDecWaves) {
+    step(blk, 0, kA, kB);
+    if (blk + kDecWaves < nblk) step(blk + kDecWaves, 1, kB, kA);
+  }
+
+  // Partial of this wave: rows r < R, O^T C layout (lane l32 = row, register r = feature
+  // db*32 + 8(r/4) + 4*h32 + r%4).  A row that saw no key writes O = 0, lse = -inf.
+  const float lt = sum_xor32(l_run);
+  const bool empty = !(lt > 0.f);
+  const float inv = empty ? 0.f : 1.f / lt;
+  if (row_ok) {
+    const size_t row = ((size_t)((split * kDecWaves + wave) * B + b) * Hq + kvh * g + hh) * T + tok;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part_o[row * D + db * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)] = acc[db][r] * inv;
+    if (h32 == 0) part_lse[row] = empty ? -INFINITY : m_run + fast_log2(lt);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, uint16_t* __restrict__ o,
@@ -249,8 +396,22 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
 }
 
 template <int D>
+static hipError_t launch_decode_mma(const DecodeArgs& a) {
+  const float sl2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((decode_mma_kernel<D>), dim3(a.B * a.Hkv * a.splits), dim3(kDecWaves * 64), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.part_o, a.part_lse, a.B,
+                     a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2, a.seqlens, a.T, a.causal);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hq * a.T), dim3(D), 0, a.stream, a.part_o, a.part_lse,
+                     (uint16_t*)a.o, a.lse, a.B * a.Hq * a.T, a.splits * kDecWaves);
+  return hipGetLastError();
+}
+
+template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a) {
   const int g = a.T * (a.Hq / a.Hkv);  // MFMA rows per group
+  if (decode_uses_mma(a.T, a.Hq / a.Hkv)) return launch_decode_mma<D>(a);
   if (g <= 1) return launch_decode_t<D, 1>(a);
   if (g <= 2) return launch_decode_t<D, 2>(a);
   if (g <= 4) return launch_decode_t<D, 4>(a);
