@@ -349,9 +349,9 @@ def main():
     }
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
     roofline["traffic"] = load_traffic("fwd_ilv_kernel", fwd_digest)
-    bwd_traffic = [load_traffic(kn, bwd_digest) for kn in ("bwd_prep_kernel", "bwd_dkdv_lag_kernel", "bwd_dq_kernel")]
+    bwd_traffic = [load_traffic(kn, bwd_digest) for kn in ("bwd_dq_kernel", "bwd_dkdv_lag_kernel")]
     roofline_bwd = {
-        "kernel": "bwd_prep_kernel + bwd_dkdv_lag_kernel + bwd_dq_kernel (attn_bwd, causal, B*H=32, N=4096, d=128)",
+        "kernel": "bwd_dq_kernel + bwd_dkdv_lag_kernel (attn_bwd, causal, B*H=32, N=4096, d=128)",
         "bound": "mfma", "achieved": f_bwd / (ms_bwd * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": f_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "traffic": None if None in bwd_traffic else sum(bwd_traffic),

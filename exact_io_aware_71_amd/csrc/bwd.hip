@@ -12,8 +12,11 @@
 //   P = exp(scale S - LSE), dV = P^T dO, dP = dO V^T, D_i = sum_c dO_ic O_ic,
 //   dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
-// Three launches, deterministic (no atomics):
-//   1. bwd_prep_kernel: D = rowsum(dO * O) and LSE * log2(e), into row-padded arrays of the
+// Two launches, deterministic (no atomics):
+//   1. bwd_dq_kernel: one workgroup per 128 queries; S^T = K Q^T and dP^T = V dO^T with
+//      Q and dO resident in registers, K/V tiles streamed through LDS; dS^T in the C layout
+//      is the A operand of dQ = dS K, K entering through the transposing read.  It also
+//      writes D = rowsum(dO * O) and LSE * log2(e) of its rows into row-padded arrays of the
 //      caller's workspace (padding rows get LSE = +inf, so their probabilities vanish).
 //   2. bwd_dkdv_lag_kernel: one workgroup per 128 keys of a KV head; each wave keeps its 32
 //      keys' K (or V) rows in registers as the B operand of S = Q K^T (or dP = dO V^T) and
@@ -22,9 +25,6 @@
 //      so P and dS are already the A operand of dV = P^T dO and dK = dS^T Q; dO and Q enter
 //      those products through the transposing ds_read_b64_tr_b16.  Causal: query tiles
 //      before the diagonal are never visited.
-//   3. bwd_dq_kernel: one workgroup per 128 queries; S^T = K Q^T and dP^T = V dO^T with
-//      Q and dO resident in registers, K/V tiles streamed through LDS; dS^T in the C layout
-//      is the A operand of dQ = dS K, K entering through the transposing read.
 // Every kernel takes the per-sequence row map of the forward (dense [B,H,N,d], or packed
 // variable-length [H,total,d] with offsets), and causal masks aligned at the bottom right:
 // query i of Nq sees keys j <= i + Nk - Nq.
@@ -48,41 +48,6 @@ namespace xattn {
 __device__ __forceinline__ size_t stat_row(const SeqGeo& g, long long stride, int b, int h, int Hq) {
   if (g.cu_q == nullptr) return ((size_t)b * Hq + h) * stride;
   return (size_t)h * stride + min(max(g.cu_q[b], 0), g.nq) + 64 * (size_t)b;
-}
-
-// One block per (batch, head, RPB rows): rows below the sequence's length get its statistics,
-// rows up to the next multiple of 64 the padding (LSE2 = +inf, D = 0).
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
-                                                       const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse, float* __restrict__ lse2,
-                                                       float* __restrict__ delta, SeqGeo geo, long long stat_stride,
-                                                       int Hq, int BH) {
-  constexpr int LPR = D / 8;             // lanes per row, 8 features each
-  constexpr int RPB = 256 / LPR;         // rows per block
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.x % BH, b = bh / Hq, h = bh - b * Hq;
-  const SeqRows sr = seq_rows(geo, b, h, Hq, 0, 1);
-  const int i = (blockIdx.x / BH) * RPB + tid / LPR;
-  const int c = tid % LPR;
-  const int npad = (sr.lq + 63) / 64 * 64;
-  if (i >= npad) return;                 // whole rows only: the reduction below stays in-row
-  const bool real = i < sr.lq;
-  float s = 0.f;
-  if (real) {
-    const size_t off = (sr.q + i) * D + 8 * c;
-    const u32x4 a = ld_global16(o + off);
-    const u32x4 g = ld_global16(dout + off);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, LPR);
-  if (c == 0) {
-    const size_t r = stat_row(geo, stat_stride, b, h, Hq) + i;
-    delta[r] = s;
-    lse2[r] = real ? lse[sr.q + i] * kLog2e : INFINITY;
-  }
 }
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int sh) {
@@ -496,11 +461,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ dQ
+// Also forms the per-row statistics the dK/dV kernel reads (it runs first): LSE2 = LSE*log2(e)
+// and D = rowsum(dO * O) for its 128 rows, padding rows up to the sequence's multiple of 64
+// getting +inf and 0.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, SeqGeo geo,
-    long long stat_stride, long long stat_half, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv) {
+    const uint16_t* __restrict__ o, const float* __restrict__ lse, float* __restrict__ stats,
+    const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, SeqGeo geo, long long stat_stride,
+    long long stat_half, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv) {
   constexpr int NW = 4, BM = NW * 32, BN = kBwdBK, KB = BN / 32, DC = D / 16, DB = D / 32;
   using T = BwdTile<D>;
   constexpr int STAGE = 2 * T::BYTES;  // K, V
@@ -523,20 +492,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* dop = dout + sr.q * D;
 
   bf16x8 qreg[DC], doreg[DC];
+  float dsum = 0.f;  // this lane's half of rowsum(dO * O)
+  const uint16_t* op = o + sr.q * D;
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
-    u32x4 a = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u};
+    u32x4 a = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u}, w = {0u, 0u, 0u, 0u};
     if (qi < Nq) {
       a = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
       g = ld_global16(dop + (size_t)qi * D + 16 * c + 8 * h32);
+      w = ld_global16(op + (size_t)qi * D + 16 * c + 8 * h32);
     }
     qreg[c] = as_bf16x8(a);
     doreg[c] = as_bf16x8(g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dsum += bf16_lo(g[e]) * bf16_lo(w[e]) + bf16_hi(g[e]) * bf16_hi(w[e]);
   }
-  // stats = [LSE2 | D]; LSE2 is the log-sum-exp times log2(e).
-  const float* st = stats + stat_row(geo, stat_stride, b, hq, Hq);
-  const float lse2 = qi < Nq ? st[qi] : INFINITY;
-  const float dl = qi < Nq ? st[stat_half + qi] : 0.f;
+  // Statistics of row qi: LSE2 = LSE*log2(e) and D = rowsum(dO * O) (the other half of the
+  // row's features sits in lane qi + 32).  Rows past the sequence up to its multiple of 64 are
+  // padding (+inf, 0) so that the dK/dV kernel's 64-row tile copies need no bounds check.
+  const float dtot = sum_xor32(dsum);
+  const float dl = qi < Nq ? dtot : 0.f;
+  const float lse2 = qi < Nq ? lse[sr.q + qi] * kLog2e : INFINITY;
+  {
+    float* st = stats + stat_row(geo, stat_stride, b, hq, Hq);
+    if (h32 == 0 && qi < (Nq + 63) / 64 * 64) {
+      st[qi] = lse2;
+      st[stat_half + qi] = dl;
+    }
+  }
 
   f32x16 dq_acc[DB];
 #pragma unroll
@@ -670,30 +653,22 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int BH = a.B * a.Hq, BHkv = a.B * a.Hkv;
   const float sl2 = a.scale * kLog2e;
   const SeqGeo geo{a.cu_q, a.cu_k, a.Nq, a.Nk};
-  float* lse2 = a.stats;
-  float* delta = a.stats + a.stat_half;
-  constexpr int RPB = 256 / (D / 8);
-  const int n_pb = ((a.max_q + 63) / 64 * 64 + RPB - 1) / RPB;
-  if (n_pb > 0) {
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(n_pb * BH), dim3(256), 0, a.stream, (const uint16_t*)a.o,
-                       (const uint16_t*)a.dout, a.lse, lse2, delta, geo, a.stat_stride, a.Hq, BH);
+  // dQ first: it also writes the row statistics the dK/dV kernel reads.
+  const int n_qt = (a.max_q + 127) / 128;
+  if (n_qt > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(256), 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o, a.lse, a.stats,
+                       (const uint16_t*)a.dout, (uint16_t*)a.dq, geo, a.stat_stride, a.stat_half, a.scale, sl2, n_qt,
+                       BH, a.Hq, a.Hkv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int n_kt = (a.max_k + 127) / 128;
-  if (n_kt > 0) {
+  if (n_kt > 0)
     hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL>), dim3(n_kt * BHkv), dim3(512), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
                        (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, geo, a.stat_stride, a.stat_half,
                        a.scale, sl2, BHkv, a.Hq, a.Hkv);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int n_qt = (a.max_q + 127) / 128;
-  if (n_qt > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(256), 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats, (const uint16_t*)a.dout,
-                       (uint16_t*)a.dq, geo, a.stat_stride, a.stat_half, a.scale, sl2, n_qt, BH, a.Hq, a.Hkv);
   return hipGetLastError();
 }
 

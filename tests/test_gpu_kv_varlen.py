@@ -217,3 +217,20 @@ def test_bwd_varlen_equal_lengths_is_attn_bwd_bitwise(gpu_lib):
         torch.cuda.synchronize()
         for a, b in zip(g1, g2):
             assert torch.equal(fold(a), b)
+
+
+@pytest.fixture(scope="module")
+def two_million_keys():
+    return make_prefill(1, 1, 1, 8, 64, "bf16", seed=2950, L=(1 << 21) + 5)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_kv_two_million_keys(gpu_lib, two_million_keys, causal):
+    """Byte offsets near the top of one head's range: 8 queries against 2^21 + 5 keys (d = 64,
+    K and V 256 MiB each), every row against the oracle."""
+    inp = two_million_keys
+    print(f"fwd_kv Nq=8 Nk={inp['k'].shape[2]} causal={causal}", flush=True)
+    scale = default_scale(64)
+    o, lse = run_kv(gpu_lib, inp, causal, scale)
+    o_ref, lse_ref = oracle.forward_kv(inp["q"], inp["k"], inp["v"], scale, causal)
+    check_rows(o, lse, o_ref, lse_ref, f"causal={causal}")
