@@ -49,6 +49,9 @@
 #ifndef XATTN_FWD64_ILV
 #define XATTN_FWD64_ILV 0
 #endif
+#ifndef XATTN_FWD64_ILV_NW
+#define XATTN_FWD64_ILV_NW 8
+#endif
 #ifndef XATTN_FWD64_NQ
 #define XATTN_FWD64_NQ 1
 #endif
@@ -385,10 +388,10 @@ __device__ __forceinline__ void mfma_qk_next(f32x16& c, const bf16x8& a, const b
 }
 __device__ __forceinline__ void qk_result_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-template <int D, int RB_>
+template <int D, int RB_, int NW_ = 8 / RB_>
 struct IlvShape {
   static constexpr int BN = kFwdBN, DC = D / 16, DB = D / 32;
-  static constexpr int RB = RB_, NW = 8 / RB, BM = NW * RB * 32;
+  static constexpr int RB = RB_, NW = NW_, BM = NW * RB * 32;
   static constexpr int TILE = BN * D * 2;          // bytes of one K or V tile
   static constexpr int NS = 4;                     // stages per ring
   static constexpr int RPC = 1024 / (2 * D);       // tile rows per 1 KB wave copy
@@ -397,16 +400,18 @@ struct IlvShape {
   static constexpr int NQK = DC;                   // K operands per 32-key block
 };
 
-template <int D, int RB_, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 / RB_, 2 / RB_))) void fwd_ilv_kernel(
+template <int D, int RB_, int NW_, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB_, 2 / RB_))) void fwd_ilv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask bm,
     float scale_log2, int n_qtiles, int BH) {
-  using S = IlvShape<D, RB_>;
+  using S = IlvShape<D, RB_, NW_>;
   constexpr int BN = S::BN, DC = S::DC, DB = S::DB, RB = S::RB, NS = S::NS, NW = S::NW;
   constexpr int TILE = S::TILE, CPW = S::CPW, RPC = S::RPC, NPV = S::NPV, NQK = S::NQK;
   constexpr int NOPS = NPV + NQK, NMF = RB * NOPS, L = XATTN_ILV_LOOKAHEAD;
   static_assert(NS == 4 && CPW <= 4, "copy schedule");
+  constexpr int CSP = NMF / CPW;  // MFMA slots per copy
+  static_assert(NMF % CPW == 0, "copies spread evenly over the step");
   __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];  // [K ring | V ring]
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];             // kept key tiles
   __shared__ int tcount;
@@ -696,7 +701,8 @@ __global__ __launch_bounds__(64 * 8 / RB_) __attribute__((amdgpu_waves_per_eu(2 
             pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
           }
         });
-        if constexpr (i % 8 == XATTN_ILV_COPY_SLOT && i / 8 < CPW) copy(ctile, ckt, cis_k, i / 8);
+        // The step's CPW copies, one every CSP slots (slots 6 and 14 at d = 128).
+        if constexpr (i % CSP == XATTN_ILV_COPY_SLOT % CSP && i / CSP < CPW) copy(ctile, ckt, cis_k, i / CSP);
         sched_fence();
       });
       if (XATTN_ILV_PRIO) __builtin_amdgcn_s_setprio(0);
@@ -915,13 +921,13 @@ hipError_t launch_fwd(const FwdArgs& a) {
 #if XATTN_FWD_ILV
   if (a.d == 128) {
     using S = IlvShape<128, XATTN_ILV_RB>;
-    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, XATTN_ILV_RB), S::BM, S::NW * 64, a);
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, XATTN_ILV_RB, S::NW), S::BM, S::NW * 64, a);
   }
 #endif
 #if XATTN_FWD64_ILV
   if (a.d == 64) {
-    using S = IlvShape<64, 1>;
-    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, 1), S::BM, S::NW * 64, a);
+    using S = IlvShape<64, 1, XATTN_FWD64_ILV_NW>;
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, 1, S::NW), S::BM, S::NW * 64, a);
   }
 #endif
   if (a.d == 128) {
