@@ -21,7 +21,8 @@ ATTN_F32, ATTN_BF16 = 0, 1
 EXPORTS = (
     "attn_abi_version", "attn_status_str", "attn_last_error", "attn_fwd", "attn_fwd_kv", "attn_fwd_varlen",
     "attn_fwd_blocksparse",
-    "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen", "attn_decode_auto_splits",
+    "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
+    "attn_bwd_blocksparse", "attn_decode_auto_splits",
     "attn_decode_workspace_bytes", "attn_decode", "attn_decode_varlen",
     "attn_decode_multi_workspace_bytes", "attn_decode_multi",
 )
@@ -63,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd.restype = i
     lib.attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.attn_bwd_blocksparse.restype = i
+    lib.attn_bwd_blocksparse.argtypes = [vp] * 10 + [ctypes.c_longlong, ctypes.c_longlong] + [i] * 7 + [f, vp, sz, vp]
     lib.attn_bwd_varlen_workspace_bytes.restype = sz
     lib.attn_bwd_varlen_workspace_bytes.argtypes = [i, i, i]
     lib.attn_bwd_varlen.restype = i
@@ -239,6 +242,49 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None
     _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                         B, Hq, Hkv, N, d, _dtype_code(q), int(bool(causal)), float(scale), _ptr(workspace),
                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
+def _mask_strides(m, B, Hq, nqb, nkb):
+    """Validated byte strides (batch, head) of a uint8 block mask [B|1, Hq|1, nqb, nkb] or a
+    lower-rank broadcast of it."""
+    import torch
+    _require(m.is_cuda and m.dtype == torch.uint8 and 2 <= m.dim() <= 4, "block_mask must be a uint8 CUDA tensor")
+    _require(tuple(m.shape[-2:]) == (nqb, nkb), f"block_mask must end in [{nqb}, {nkb}]")
+    _require(m.stride(-1) == 1 and m.stride(-2) == nkb, "block_mask rows must be dense")
+    sb = sh = 0
+    if m.dim() == 4:
+        _require(m.shape[0] in (1, B), "block_mask batch dim must be 1 or B")
+        sb = 0 if m.shape[0] == 1 else m.stride(0)
+    if m.dim() >= 3:
+        _require(m.shape[-3] in (1, Hq), "block_mask head dim must be 1 or Hq")
+        sh = 0 if m.shape[-3] == 1 else m.stride(-3)
+    return sb, sh
+
+
+def attn_bwd_blocksparse(q, k, v, o, lse, dout, block_mask, causal: bool, scale: float, dq=None, dk=None, dv=None,
+                         workspace=None, stream=None):
+    """Backward of attn_fwd_blocksparse for square attention (q/k/v [B,H,N,d])."""
+    import torch
+    lib = load()
+    for t in (q, k, v, o, lse, dout):
+        _require(t.is_cuda and t.is_contiguous(), "all inputs must be contiguous CUDA tensors")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    _require(tuple(k.shape) == (B, Hkv, N, d) == tuple(v.shape), "k/v shape mismatch (square attention only)")
+    _require(tuple(lse.shape) == (B, Hq, N) and lse.dtype == torch.float32, "lse must be fp32 [B,Hq,N]")
+    nb = -(-N // SPARSE_BLOCK)
+    sb, sh = _mask_strides(block_mask, B, Hq, nb, nb)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(block_mask), sb, sh, B, Hq, Hkv, N, d, _dtype_code(q),
+                                    int(bool(causal)), float(scale), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return dq, dk, dv
 
 

@@ -201,7 +201,8 @@ size_t attn_bwd_varlen_workspace_bytes(int B, int Hq, int total_q) {
 static attn_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dout, void* dq, void* dk, void* dv, const int* cu_q, const int* cu_k, int B,
                               int Hq, int Hkv, int Nq, int Nk, int max_q, int max_k, int d, attn_dtype_t dtype,
-                              int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                              int causal, float scale, void* workspace, size_t workspace_bytes, void* stream,
+                              const unsigned char* block_mask = nullptr, long long mask_sb = 0, long long mask_sh = 0) {
   if ((Nq > 0 && (!q || !o || !lse || !dout || !dq)) || (Nk > 0 && (!k || !v || !dk || !dv)))
     return fail(ATTN_ERR_INVALID_ARG, "all tensor pointers of attn_bwd must be non-null");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
@@ -228,7 +229,8 @@ static attn_status_t bwd_impl(const void* q, const void* k, const void* v, const
   const long long stride = cu_q ? (long long)Nq + 64LL * B : bwd_npad(Nq);
   const long long half = cu_q ? (long long)Hq * stride : (long long)B * Hq * stride;
   xattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, B, Hq, Hkv, Nq, Nk, max_q, max_k, d,
-                   causal ? 1 : 0, scale, (float*)workspace, stride, half, (hipStream_t)stream};
+                   causal ? 1 : 0, scale, (float*)workspace, stride, half, (hipStream_t)stream, block_mask, mask_sb,
+                   mask_sh};
   return from_hip(xattn::launch_bwd(a), "attn_bwd launch");
 }
 
@@ -239,6 +241,24 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N must be positive (got %d)", N);
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, B, Hq, Hkv, N, N, N, N, d, dtype, causal,
                   scale, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                   const void* dout, void* dq, void* dk, void* dv, const unsigned char* block_mask,
+                                   long long mask_stride_b, long long mask_stride_h, int B, int Hq, int Hkv, int N,
+                                   int d, attn_dtype_t dtype, int causal, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!block_mask) return fail(ATTN_ERR_INVALID_ARG, "block_mask must be non-null");
+  if (mask_stride_b < 0 || mask_stride_h < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "mask strides must be >= 0 (got %lld, %lld)", mask_stride_b, mask_stride_h);
+  if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N must be positive (got %d)", N);
+  // The dK/dV workgroup lists its group's kept (head, 64-row tile) pairs: at most 8191 of them,
+  // tiles below 2048 and at most 32 heads per group.
+  if (Hkv > 0 && Hq % Hkv == 0 &&
+      ((long long)(Hq / Hkv) * ((N + 63) / 64) > xattn::kMaxSparseKeys / 64 || N > 2048 * 64 || Hq / Hkv > 32))
+    return fail(ATTN_ERR_UNSUPPORTED, "block-sparse backward supports (Hq/Hkv) * ceil(N/64) <= 8191, N <= 131072");
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, B, Hq, Hkv, N, N, N, N, d, dtype, causal, scale,
+                  workspace, workspace_bytes, stream, block_mask, mask_stride_b, mask_stride_h);
 }
 
 attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,

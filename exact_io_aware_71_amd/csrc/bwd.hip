@@ -66,6 +66,37 @@ struct BwdTile {
   static constexpr int BYTES = 64 * D * 2;   // one swizzled 64-row tile
 };
 
+// Block-sparse dK/dV: lists the (query head, query tile) pairs of a workgroup that the mask
+// keeps, in the order the virtual tile sequence visits them: heads h0 .. h0+g-1 of the group,
+// 64-row tiles qt_begin .. qt_begin+nt-1 each, against key block kb; entry = tile | (head
+// offset << 11).  Wave 0 compacts 64 pairs per ballot; the count lands in the list's last
+// entry and is returned to every thread (one barrier).
+__device__ __forceinline__ int build_qtile_list(const BlockMask& bm, int b, int h0, int g, int kb, int qt_begin, int nt,
+                                                uint16_t* list) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    int n = 0;
+    const int total = g * nt;
+    for (int i0 = 0; i0 < total; i0 += 64) {
+      const int i = i0 + lane;
+      bool keep = false;
+      int e = 0;
+      if (i < total) {
+        const int hh = i / nt, t = qt_begin + (i - hh * nt);
+        keep = bm.mask[b * bm.sb + (h0 + hh) * bm.sh + (size_t)(t >> 1) * bm.nkb + kb] != 0;
+        e = t | (hh << 11);
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (keep) list[pos] = (uint16_t)e;
+      n += __builtin_popcountll(bal);
+    }
+    if (lane == 0) list[kMaxSparseTiles - 1] = (uint16_t)n;
+  }
+  __syncthreads();
+  return list[kMaxSparseTiles - 1];
+}
+
 // dK, dV with a lagged dK wave.  Waves g and g + 4 share a SIMD and the same 32 keys, the
 // first accumulating dV, the second dK, and P crosses from the first to the second through
 // LDS (as bf16, the precision the dS product rounds to anyway).  The dK
@@ -74,12 +105,12 @@ struct BwdTile {
 // iteration t-1.  One barrier per tile instead of two, and each SIMD always holds one wave
 // in each kind of phase.  LDS: a three-stage ring of [Q | dO | LSE2 | D] tiles (t-1, t and
 // the copy of t+1) and two P buffers.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_lag_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, SeqGeo geo, long long stat_stride, long long stat_half, float scale, float scale_log2,
-    int BHkv, int Hq, int Hkv) {
+    uint16_t* __restrict__ dv, SeqGeo geo, BlockMask bm, long long stat_stride, long long stat_half, float scale,
+    float scale_log2, int BHkv, int Hq, int Hkv) {
   constexpr int NW = 8, NG = 4, BK = NG * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32, NQB = BQ / 32;
   using T = BwdTile<D>;
   constexpr int STAGE = (2 * T::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // Q, dO, LSE2, D
@@ -90,6 +121,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(CPTT % NW == 0 || (2 * CPTT) % NW == 0, "tile pieces split over the waves");
   static_assert(NW % (16 / RPC) == 0, "pieces of a wave share their swizzle");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + 2 * PBYTES];
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];  // kept (head, query tile) pairs
+  static_assert(!SPARSE || BK == kSparseBlock, "a workgroup's keys form one mask block");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
   const int grp = wave & (NG - 1), role = wave / NG;
@@ -115,11 +148,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int npad = (Nq + BQ - 1) / BQ * BQ;  // statistics rows of one head of this sequence
   const int qt_begin = CAUSAL ? max(k0 - doff, 0) / BQ : 0;
   const int qt_end = (Nq + BQ - 1) / BQ;
-  // Virtual tiles vt = 0 .. g*nt - 1: query head vt / nt of the group, tile qt_begin + vt % nt.
-  // The LDS ring slot and the P slot follow vt.
-  const int nt = qt_end - qt_begin, nvt = g * nt;
+  // Virtual tiles vt = 0 .. g*nt - 1: query head vt / nt of the group, tile qt_begin + vt % nt
+  // (block-sparse: the kept pairs of the list, in the same order).  The LDS ring slot and the
+  // P slot follow vt.
+  const int nt = qt_end - qt_begin;
+  int nvt = g * nt;
+  if constexpr (SPARSE) nvt = nt > 0 ? build_qtile_list(bm, b, h0, g, k0 / kSparseBlock, qt_begin, nt, tlist) : 0;
+  auto entry = [&](int i) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_readfirstlane((int)tlist[min(i, nvt - 1)]);
+  };
   uint16_t* outp = (role == 0 ? dv : dk) + sr.k * D;
-  if (nt <= 0) {  // no query sees these keys: dK = dV = 0
+  if (nvt <= 0) {  // no query sees these keys: dK = dV = 0
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -182,7 +221,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dma4_m0(wave_uniform(base), 4 * min(t * BQ + lane, npad - 1), m0v);
   };
 
-  copy_tile(0, 0, qt_begin);
+  int h_cur = 0, t_cur = qt_begin;  // (head, tile) of vt
+  if constexpr (SPARSE) {
+    const int e = entry(0);
+    h_cur = e >> 11;
+    t_cur = e & 2047;
+  }
+  copy_tile(0, h_cur, t_cur);
   // K^T (dV wave) or V^T (dK wave), the B operand of S = Q K^T or dP = dO V^T: lane owns key
   // kw0 + l32.
   const int kj = kw0 + l32;
@@ -422,11 +467,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // piece every third MFMA of the first half of an interleaved tile.  Past the end the last
   // head's tile qt_end is copied, its rows and statistics clamped to the last ones, into the
   // stage nobody reads in this iteration.
-  int h_cur = 0, t_cur = qt_begin;                                   // of vt
   int h_nxt = nt == 1 ? 1 : 0, t_nxt = nt == 1 ? qt_begin : qt_begin + 1;  // of vt + 1
+  int h_end = g - 1, t_end = qt_end;  // copied past the end (clamped rows, an idle stage)
+  if constexpr (SPARSE) {
+    const int e = entry(1), l = entry(nvt - 1);
+    h_nxt = e >> 11;
+    t_nxt = e & 2047;
+    h_end = l >> 11;
+    t_end = l & 2047;
+  }
   for (int vt = 0; vt <= nvt; ++vt) {
     const bool more = vt + 1 < nvt;
-    const int ch = more ? h_nxt : g - 1, ct = more ? t_nxt : qt_end;
+    const int ch = more ? h_nxt : h_end, ct = more ? t_nxt : t_end;
     const bool ilv_dv = kIlv && role == 0 && vt < nvt && !(CAUSAL && t_cur * BQ + doff < kw0 + 31);
     const bool ilv_dk = kIlv && role == 1 && vt > 0;
     if (!(XATTN_DKDV_SPREAD && (ilv_dv || ilv_dk)) && more) copy_tile(vt + 1, h_nxt, t_nxt);
@@ -443,7 +495,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lds_barrier();
     h_cur = h_nxt;
     t_cur = t_nxt;
-    if (++t_nxt == qt_end) {
+    if constexpr (SPARSE) {
+      const int e = entry(vt + 2);
+      h_nxt = e >> 11;
+      t_nxt = e & 2047;
+    } else if (++t_nxt == qt_end) {
       t_nxt = qt_begin;
       ++h_nxt;
     }
@@ -464,16 +520,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Also forms the per-row statistics the dK/dV kernel reads (it runs first): LSE2 = LSE*log2(e)
 // and D = rowsum(dO * O) for its 128 rows, padding rows up to the sequence's multiple of 64
 // getting +inf and 0.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const float* __restrict__ lse, float* __restrict__ stats,
-    const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, SeqGeo geo, long long stat_stride,
+    const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, SeqGeo geo, BlockMask bm, long long stat_stride,
     long long stat_half, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv) {
   constexpr int NW = 4, BM = NW * 32, BN = kBwdBK, KB = BN / 32, DC = D / 16, DB = D / 32;
+  static_assert(!SPARSE || BM == kSparseBlock, "a workgroup's queries form one mask block");
   using T = BwdTile<D>;
   constexpr int STAGE = 2 * T::BYTES;  // K, V
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];  // kept key tiles (block-sparse)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
   const int bh = blockIdx.x % BH;
@@ -528,7 +586,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
 
   const int kv_end = CAUSAL ? min(Nk, q0 + BM + (Nk - Nq)) : Nk;
-  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // Block-sparse: walk only the key tiles the workgroup's query block keeps (position t holds
+  // key tile kt(t)); dropped blocks hold no score, so no further masking is needed.
+  if constexpr (SPARSE) ntiles = build_tile_list<1>(bm, b, hq, q0 / kSparseBlock, ntiles, tlist);
+  auto kt = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tlist[min(t, ntiles - 1)]) & 0x3fff;
+    else return t;
+  };
   // K/V tiles arrive by direct global -> LDS copies (no staging registers, which lets two
   // workgroups share a CU).  Wave w copies 1 KB pieces j = w, w + NW, ... of [K tile | V
   // tile]; piece j covers tile rows RPC*(j % CPTT) ...; lane l fills physical chunk l, i.e.
@@ -565,11 +630,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const void* vbase = wave_uniform(vp);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto copy_piece = [&](int t, int i) __attribute__((always_inline)) {
+  auto copy_piece = [&](int t, int ktile, int i) __attribute__((always_inline)) {
     const int j = wv + NW * i;
     const bool is_k = j < CPTT;
     const int jt = is_k ? j : j - CPTT;
-    const int row = min(t * BN + RPC * jt + lrow, Nk - 1);
+    const int row = min(ktile * BN + RPC * jt + lrow, Nk - 1);
     const uint32_t m0v = lds0 + (t & 1) * STAGE + (is_k ? 0 : T::BYTES) + 1024 * jt;
     dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
   };
@@ -585,17 +650,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     return;
   }
-  copy_tile(0, 0);
+  copy_tile(kt(0), 0);
   wait_vmem();  // also covers the Q/dO loads
   lds_barrier();
   // Tile t+1 is copied during tile t (past the end: rows clamped, into the idle stage).
   for (int t = 0; t < ntiles; ++t) {
-    const int t0 = t * BN;
+    const int t0 = kt(t) * BN, kn = kt(t + 1);
     const char* ks = smem + (t & 1) * STAGE;
     const char* vs = ks + T::BYTES;
     if (CAUSAL && t0 > qd0 + 31) {
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) copy_piece(t + 1, i);
+      for (int i = 0; i < CPW; ++i) copy_piece(t + 1, kn, i);
     } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -609,7 +674,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + off);
           s = mfma32(ak, qreg[c], s);
           dp = mfma32(av, doreg[c], dp);
-          if (kb == 0 && c < CPW) copy_piece(t + 1, c);
+          if (kb == 0 && c < CPW) copy_piece(t + 1, kn, c);
         }
         // Lane owns query qi; register r holds key t0 + kb*32 + 8(r/4) + 4*h32 + r%4.
         const int kb0 = t0 + kb * 32;
@@ -648,33 +713,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ host launcher
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int BH = a.B * a.Hq, BHkv = a.B * a.Hkv;
   const float sl2 = a.scale * kLog2e;
   const SeqGeo geo{a.cu_q, a.cu_k, a.Nq, a.Nk};
+  const BlockMask bm{a.block_mask, a.mask_sb, a.mask_sh, (a.Nq + kSparseBlock - 1) / kSparseBlock,
+                     (a.Nk + kSparseBlock - 1) / kSparseBlock};
   // dQ first: it also writes the row statistics the dK/dV kernel reads.
   const int n_qt = (a.max_q + 127) / 128;
   if (n_qt > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(256), 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o, a.lse, a.stats,
-                       (const uint16_t*)a.dout, (uint16_t*)a.dq, geo, a.stat_stride, a.stat_half, a.scale, sl2, n_qt,
-                       BH, a.Hq, a.Hkv);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(n_qt * BH), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o, a.lse,
+                       a.stats, (const uint16_t*)a.dout, (uint16_t*)a.dq, geo, bm, a.stat_stride, a.stat_half, a.scale,
+                       sl2, n_qt, BH, a.Hq, a.Hkv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int n_kt = (a.max_k + 127) / 128;
   if (n_kt > 0)
-    hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL>), dim3(n_kt * BHkv), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL, SPARSE>), dim3(n_kt * BHkv), dim3(512), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
-                       (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, geo, a.stat_stride, a.stat_half,
-                       a.scale, sl2, BHkv, a.Hq, a.Hkv);
+                       (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, geo, bm, a.stat_stride,
+                       a.stat_half, a.scale, sl2, BHkv, a.Hq, a.Hkv);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
-  return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a) {
+  if (a.block_mask) return a.causal ? launch_bwd_t<D, true, true>(a) : launch_bwd_t<D, false, true>(a);
+  return a.causal ? launch_bwd_t<D, true, false>(a) : launch_bwd_t<D, false, false>(a);
 }
+
+hipError_t launch_bwd(const BwdArgs& a) { return a.d == 128 ? launch_bwd_d<128>(a) : launch_bwd_d<64>(a); }
 
 }  // namespace xattn

@@ -267,7 +267,9 @@ __device__ __forceinline__ SeqRows seq_rows(const SeqGeo& g, int b, int hq, int 
 // drops (zero) every score of query block i (rows 128i .. 128i+127) against key block j
 // (keys 128j .. 128j+127).  Strides of 0 share one mask across batches or heads.
 constexpr int kSparseBlock = 128;
-constexpr int kMaxSparseTiles = 8192;  // 64-key tiles a workgroup can list (kMaxSparseKeys / 64)
+// A tile list is an LDS array of kMaxSparseTiles uint16 entries whose last entry holds the
+// count, so at most kMaxSparseTiles - 1 tiles (16 KB in all: two dQ workgroups still fit a CU).
+constexpr int kMaxSparseTiles = 8192;
 struct BlockMask {
   const unsigned char* mask;  // nullptr: dense
   long long sb, sh;
@@ -278,8 +280,7 @@ struct BlockMask {
 // blocks (starting at block qb0) keeps: entry = t | (keep bits of the QB blocks) << 14.
 // Wave 0 compacts 64 tiles per ballot; returns the count to every thread (one barrier).
 template <int QB>
-__device__ __forceinline__ int build_tile_list(const BlockMask& bm, int b, int h, int qb0, int T, uint16_t* list,
-                                               int* count) {
+__device__ __forceinline__ int build_tile_list(const BlockMask& bm, int b, int h, int qb0, int T, uint16_t* list) {
   static_assert(QB >= 1 && QB <= 2, "two keep bits per entry");
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid < 64) {
@@ -298,10 +299,10 @@ __device__ __forceinline__ int build_tile_list(const BlockMask& bm, int b, int h
       if (keep != 0) list[pos] = (uint16_t)(t | (keep << 14));
       n += __builtin_popcountll(bal);
     }
-    if (lane == 0) *count = n;
+    if (lane == 0) list[kMaxSparseTiles - 1] = (uint16_t)n;
   }
   __syncthreads();
-  return *count;
+  return list[kMaxSparseTiles - 1];
 }
 
 // Initial running max of the forward kernels: the most negative finite float rather than

@@ -65,7 +65,7 @@
 namespace xattn {
 
 constexpr int kFwdBN = 64;  // keys per tile
-static_assert(kMaxSparseTiles * kFwdBN == kMaxSparseKeys, "block-sparse tile list size");
+static_assert((kMaxSparseTiles - 1) * kFwdBN == kMaxSparseKeys, "block-sparse tile list size");
 constexpr float kLazy = 8.f; // log2 of the largest un-normalised probability allowed
 
 template <int D>
@@ -99,7 +99,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   using Lds = FwdLds<D>;
   __shared__ __attribute__((aligned(16))) char smem[Lds::TOTAL];
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];  // kept key tiles (block-sparse)
-  __shared__ int tcount;
   static_assert(!SPARSE || BM % kSparseBlock == 0, "query tile must cover whole mask blocks");
 
   const int tid = threadIdx.x;
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // Block-sparse: walk only the tiles one of the workgroup's query blocks keeps; walk position
   // t holds key tile kt(t) and the wave skips tiles its own block drops.  Dense: kt(t) = t.
   if constexpr (SPARSE)
-    ntiles = build_tile_list<SPARSE ? BM / kSparseBlock : 1>(bm, b, hq, q0 / kSparseBlock, ntiles, tlist, &tcount);
+    ntiles = build_tile_list<SPARSE ? BM / kSparseBlock : 1>(bm, b, hq, q0 / kSparseBlock, ntiles, tlist);
   auto entry = [&](int t) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tlist[t]);
     else return t;
@@ -414,7 +413,6 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   static_assert(NMF % CPW == 0, "copies spread evenly over the step");
   __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];  // [K ring | V ring]
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];             // kept key tiles
-  __shared__ int tcount;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
@@ -490,7 +488,7 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   int T = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   // Block-sparse: the workgroup walks only the tiles that one of its query blocks keeps; tile
   // position i of the walk holds key tile kt(i).  Dense: kt(i) = i.
-  if constexpr (SPARSE) T = build_tile_list<S::BM / kSparseBlock>(bm, b, hq, q0 / kSparseBlock, T, tlist, &tcount);
+  if constexpr (SPARSE) T = build_tile_list<S::BM / kSparseBlock>(bm, b, hq, q0 / kSparseBlock, T, tlist);
   if (T == 0) {  // no key for any row of the tile (empty key sequence, causal with Nk < Nq, or
     epilogue();  // every block dropped)
     return;

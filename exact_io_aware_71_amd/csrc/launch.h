@@ -36,6 +36,8 @@ struct BwdArgs {
   float* stats;
   long long stat_stride, stat_half;
   hipStream_t stream;
+  const unsigned char* block_mask;  // optional [B, Hq, ceil(N/128), ceil(N/128)] keep bytes (dense layout only)
+  long long mask_sb, mask_sh;       // batch and head strides of block_mask in bytes
 };
 
 struct DecodeArgs {
@@ -52,8 +54,8 @@ struct DecodeArgs {
   int causal;           // token t sees keys j <= len - T + t
 };
 
-// Longest key sequence the block-sparse forward walks (its tile list holds 8192 tiles of 64).
-constexpr int kMaxSparseKeys = 8192 * 64;
+// Longest key sequence the block-sparse forward walks (its tile list holds 8191 tiles of 64).
+constexpr int kMaxSparseKeys = 8191 * 64;
 
 // Decode path: rows = T * (Hq/Hkv) (token, head) pairs per KV head.  Up to XATTN_DEC_VALU_ROWS
 // rows the vector-ALU kernel (one partial per workgroup), above it the matrix-core kernel

@@ -106,7 +106,8 @@ attn_status_t attn_fwd_kv(const void* q, const void* k, const void* v, void* o, 
  * Score (i, j) enters the softmax iff its block is kept (and j <= i + Nk - Nq when causal); a
  * row that keeps no key gets o = 0 and lse = -inf.  Dropped blocks are neither loaded nor
  * multiplied where a whole workgroup (256 query rows at d = 128, 128 at d = 64) drops them.
- * Supported: BF16, d in {64, 128}, Nk <= 524288.  Other arguments as attn_fwd_kv.
+ * Supported: BF16, d in {64, 128}, Nk <= 524224 (8191 tiles of 64).  Other arguments as
+ * attn_fwd_kv.
  */
 attn_status_t attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                    const unsigned char* block_mask, long long mask_stride_b,
@@ -154,6 +155,24 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
                        int B, int Hq, int Hkv, int N, int d, attn_dtype_t dtype, int causal,
                        float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of attn_fwd_blocksparse for square attention (Nq = Nk = N): the gradient of exact
+ * attention under the block keep-mask (same layout and strides as attn_fwd_blocksparse, 128 x
+ * 128 blocks), by recomputation.  Both backward kernels walk only kept tiles: the dQ workgroup
+ * of 128 queries (one mask row of blocks) its kept 64-key tiles, the dK/dV workgroup of 128
+ * keys (one mask column) its kept (query head, 64-query tile) pairs.  Rows that keep no key get
+ * dq = 0, keys that no query keeps get dk = dv = 0.
+ *   q, k, v, o, lse, dout   as attn_bwd, with o and lse from attn_fwd_blocksparse (same mask)
+ *   workspace               >= attn_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+ * Supported: BF16, d in {64, 128}, (Hq/Hkv) * ceil(N/64) <= 8191, N <= 131072.
+ */
+attn_status_t attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                   const unsigned char* block_mask, long long mask_stride_b,
+                                   long long mask_stride_h, int B, int Hq, int Hkv, int N, int d,
+                                   attn_dtype_t dtype, int causal, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attn_bwd_varlen needs: the same two fp32 statistics per query
  * row, each sequence padded by up to 64 rows, i.e. 2 * Hq * (total_q + 64 * B) * 4 bytes,

@@ -31,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["upcast", "probabilities", "forward", "forward_kv", "forward_blocksparse", "forward_varlen", "forward_rows",
-           "backward", "backward_kv", "backward_varlen", "decode_multi",
+           "backward", "backward_kv", "backward_blocksparse", "backward_varlen", "decode_multi",
            "decode", "split_kv_decode", "lse_merge", "attention_flops"]
 
 
@@ -247,6 +247,37 @@ def backward_kv(q, k, v, dout, scale: float, causal: bool):
         for h in range(Hq):
             kv = _kv_head(h, Hq, Hkv)
             p, _ = _softmax_rows(_scores(q[b, h], k[b, kv], scale, causal, row_ids=pos))
+            o = p @ v[b, kv]
+            do = dout[b, h]
+            dv[b, kv] += p.T @ do
+            dp = do @ v[b, kv].T
+            dd = np.sum(do * o, axis=1, keepdims=True)
+            ds = p * (dp - dd)
+            dq[b, h] = scale * (ds @ k[b, kv])
+            dk[b, kv] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def backward_blocksparse(q, k, v, dout, block_mask, scale: float, causal: bool, block: int = 128):
+    """Gradient of forward_blocksparse (the textbook softmax chain rule under the element mask
+    the blocks expand to; causal aligned at the bottom right).  Rows that keep no key have P = 0
+    and contribute nothing."""
+    q, k, v, dout = upcast(q), upcast(k), upcast(v), upcast(dout)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    nqb, nkb = -(-Nq // block), -(-Nk // block)
+    mask = np.broadcast_to(np.asarray(block_mask) != 0, (B, Hq, nqb, nkb))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    if Nk == 0 or Nq == 0:
+        return dq, dk, dv
+    pos = np.arange(Nq) + (Nk - Nq)
+    qi, kj = np.arange(Nq) // block, np.arange(Nk) // block
+    for b in range(B):
+        for h in range(Hq):
+            kv = _kv_head(h, Hq, Hkv)
+            s = _scores(q[b, h], k[b, kv], scale, causal, row_ids=pos)
+            s = np.where(mask[b, h][qi[:, None], kj[None, :]], s, -np.inf)
+            p, _ = _softmax_rows(s)
             o = p @ v[b, kv]
             do = dout[b, h]
             dv[b, kv] += p.T @ do

@@ -88,8 +88,21 @@ def test_fwd_blocksparse_validation():
     assert bs(sh=-4) == 1
     assert bs(Nq=0) == 1
     assert bs(dt=0, d=64) == 2           # fp32 is dense only
-    assert bs(Nk=524288 + 64) == 2       # beyond the tile list
+    assert bs(Nk=524224 + 1) == 2        # beyond the tile list
     assert bs(d=96) == 2
+
+
+def test_bwd_blocksparse_validation():
+    def bb(mask=P, sb=0, sh=0, N=1024, Hq=4, Hkv=2, dt=1, ws_bytes=1 << 30):
+        return lib.attn_bwd_blocksparse(P, P, P, P, P, P, P, P, P, mask, sb, sh, 1, Hq, Hkv, N, 128, dt, 1,
+                                        ctypes.c_float(0.1), P, ws_bytes, None)
+    assert bb(mask=None) == 1
+    assert bb(sh=-1) == 1
+    assert bb(N=0) == 1
+    assert bb(N=131072 + 64) == 2            # tiles beyond 2047
+    assert bb(N=65536, Hq=16, Hkv=2) == 2    # 8 heads x 1024 tiles > 8191 pairs
+    assert bb(dt=0) == 2
+    assert bb(ws_bytes=16) == 3
 
 
 def bwd(ws=P, ws_bytes=1 << 30, Hq=2, Hkv=2, d=128, dt=1, scale=0.1, dq=P):

@@ -88,3 +88,55 @@ def test_blocksparse_shared_mask_equals_per_head_copy(gpu_lib):
     o2, l2 = gpu_lib.attn_fwd_blocksparse(q, k, v, m4, True, default_scale(128))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------- backward
+from tests._util import BWD_REL_L2, rel_l2  # noqa: E402
+
+
+def run_sparse_fwd_bwd(lib, inp, mask, causal, scale):
+    import torch
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
+    m = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda()
+    o, lse = lib.attn_fwd_blocksparse(q, k, v, m, causal, scale)
+    grads = lib.attn_bwd_blocksparse(q, k, v, o, lse, do, m, causal, scale)
+    torch.cuda.synchronize()
+    return [to_host64(g) for g in grads]
+
+
+@pytest.mark.parametrize("N", [300, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("density", [0.3, 0.7])
+def test_bwd_blocksparse_random_masks(gpu_lib, N, d, causal, density):
+    print(f"bwd blocksparse N={N} d={d} causal={causal} density={density}", flush=True)
+    B, Hq, Hkv = 1, 4, 2
+    inp = make_prefill(B, Hq, Hkv, N, d, "bf16", seed=3500 + N + d, with_dout=True)
+    rng = np.random.default_rng(3600 + N + d + int(causal))
+    nb = nblk(N)
+    mask = (rng.random((B, Hq, nb, nb)) < density).astype(np.uint8)
+    mask[0, 1, 0, :] = 0       # a query block that keeps nothing
+    mask[0, 2, :, nb - 1] = 0  # a key block that head 2 never keeps
+    scale = default_scale(d)
+    dq, dk, dv = run_sparse_fwd_bwd(gpu_lib, inp, mask, causal, scale)
+    ref = oracle.backward_blocksparse(inp["q"], inp["k"], inp["v"], inp["dout"], mask, scale, causal)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        err = rel_l2(g, r)
+        assert err <= BWD_REL_L2, (N, d, causal, density, name, err)
+    assert np.all(dq[0, 1, :min(BLK, N)] == 0.0)  # rows that keep no key
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_blocksparse_full_mask_is_attn_bwd_bitwise(gpu_lib, d):
+    import torch
+    N = 333
+    inp = make_prefill(2, 4, 2, N, d, "bf16", seed=3700 + d, with_dout=True)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
+    ones = torch.ones((nblk(N), nblk(N)), dtype=torch.uint8, device=q.device)
+    for causal in (False, True):
+        o, lse = gpu_lib.attn_fwd(q, k, v, causal, default_scale(d))
+        g1 = gpu_lib.attn_bwd(q, k, v, o, lse, do, causal, default_scale(d))
+        g2 = gpu_lib.attn_bwd_blocksparse(q, k, v, o, lse, do, ones, causal, default_scale(d))
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)

@@ -678,3 +678,45 @@ def test_decode_multi_pins():
     for t in range(T):
         od, ld = oracle.decode(q[:, :, t], kc, vc, 0.6, seqlens=lens)
         np.testing.assert_allclose(on[:, :, t], od, rtol=1e-12, atol=1e-13)
+
+
+def _loss_bs(q, k, v, dout, mask, scale, causal, block):
+    o, _ = oracle.forward_blocksparse(q, k, v, mask, scale, causal, block=block)
+    return float(np.sum(o * dout))
+
+
+def test_backward_blocksparse_pins():
+    """Central differences of the (pinned) forward_blocksparse on a tiny case with an empty row
+    of blocks; the full mask equals backward_kv; a block-diagonal mask equals the packed
+    backward of one-block sequences."""
+    rng = np.random.default_rng(140)
+    B, Hq, Hkv, N, d, blk, scale, eps = 1, 2, 1, 6, 3, 2, 0.8, 1e-6
+    q, k, v = rng.standard_normal((B, Hq, N, d)), rng.standard_normal((B, Hkv, N, d)), rng.standard_normal((B, Hkv, N, d))
+    do = rng.standard_normal((B, Hq, N, d))
+    mask = np.array([[[1, 0, 1], [0, 0, 0], [1, 1, 0]], [[0, 1, 1], [1, 0, 1], [1, 1, 1]]])[None]
+    for causal in (False, True):
+        g = oracle.backward_blocksparse(q, k, v, do, mask, scale, causal, block=blk)
+        for name, x, gx in (("q", q, g[0]), ("k", k, g[1]), ("v", v, g[2])):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args = {"q": q, "k": k, "v": v}
+                lp = _loss_bs(**{**args, name: xp}, dout=do, mask=mask, scale=scale, causal=causal, block=blk)
+                lm = _loss_bs(**{**args, name: xm}, dout=do, mask=mask, scale=scale, causal=causal, block=blk)
+                num[idx] = (lp - lm) / (2 * eps)
+            np.testing.assert_allclose(gx, num, rtol=1e-6, atol=1e-7, err_msg=f"{name} causal={causal}")
+        assert np.all(g[0][0, 0, 2:4] == 0.0)  # head 0, query block 1 keeps nothing
+    gf = oracle.backward_blocksparse(q, k, v, do, np.ones((3, 3)), scale, True, block=blk)
+    gk = oracle.backward_kv(q, k, v, do, scale, True)
+    for a, c in zip(gf, gk):
+        np.testing.assert_allclose(a, c, rtol=1e-12, atol=1e-13)
+    lens = [blk] * 3
+    x = make_varlen(lens, lens, Hq, Hkv, d, "f32", seed=141)
+    dox = rng.standard_normal(x["q"].shape)
+    gb = oracle.backward_blocksparse(x["q"][None], x["k"][None], x["v"][None], dox[None], np.eye(3), scale, True,
+                                     block=blk)
+    gv = oracle.backward_varlen(x["q"], x["k"], x["v"], dox, x["cu_q"], x["cu_k"], scale, True)
+    for a, c in zip(gb, gv):
+        np.testing.assert_allclose(a[0], c, rtol=1e-12, atol=1e-13)
