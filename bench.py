@@ -267,8 +267,8 @@ def main():
         # Block-sparse: B=1, H=32, N=16384, d=128, causal; query block i keeps key blocks i-7 .. i
         # and block 0 (128x128 blocks), i.e. a 1024-key window plus the first block.
         SH, SN = 32, 16384
-        sp = make_prefill(1, SH, SH, SN, d, "bf16", seed=1010)
-        sq_, sk_, sv_ = (to_dev(sp[x]) for x in ("q", "k", "v"))
+        sp = make_prefill(1, SH, SH, SN, d, "bf16", seed=1010, with_dout=True)
+        sq_, sk_, sv_, sdo = (to_dev(sp[x]) for x in ("q", "k", "v", "dout"))
         del sp
         nbk = SN // 128
         bi, bj = np.meshgrid(np.arange(nbk), np.arange(nbk), indexing="ij")
@@ -282,7 +282,11 @@ def main():
         off = int(np.sum(smask * (bi > bj)))
         sparse_pairs = off * 128 * 128 + nbk * 128 * 129 // 2
         f_sparse = 4.0 * d * SH * sparse_pairs
-        del sq_, sk_, sv_, so, slse
+        sg = [torch.empty_like(sq_), torch.empty_like(sk_), torch.empty_like(sv_)]
+        sws = torch.empty(attn.attn_bwd_workspace_bytes(1, SH, SH, SN, d), dtype=torch.uint8, device=dev)
+        ms_sparse_bwd = time_call(lambda: attn.attn_bwd_blocksparse(sq_, sk_, sv_, so, slse, sdo, smask_dev, True, scale,
+                                                                    dq=sg[0], dk=sg[1], dv=sg[2], workspace=sws))
+        del sq_, sk_, sv_, sdo, so, slse, sg, sws
 
         # Multi-token decode: 4 tokens per sequence on the decode cache (16 (token, head) rows per
         # KV head), causal, seed 1011 for the queries.
@@ -312,6 +316,7 @@ def main():
             "fwd_chunk": {"TFLOPs": f_chunk / (ms_chunk * 1e-3) / 1e12, "ms": ms_chunk,
                           "workload": "attn_fwd_kv B=4 Hq=32 Hkv=8 Nq=1024 Nk=8192 d=128 causal (bottom right)"},
             "fwd_blocksparse": {"TFLOPs": f_sparse / (ms_sparse * 1e-3) / 1e12, "ms": ms_sparse,
+                                "bwd_TFLOPs": 2.5 * f_sparse / (ms_sparse_bwd * 1e-3) / 1e12, "bwd_ms": ms_sparse_bwd,
                                 "workload": "attn_fwd_blocksparse B=1 H=32 N=16384 d=128 causal, 128x128 blocks: "
                                             "8-block band + first block (%.1f%% of causal pairs kept)"
                                             % (100.0 * sparse_pairs / (SN * (SN + 1) / 2))},
