@@ -11,6 +11,11 @@ Reported value: forward+backward TFLOP/s with the algorithmic count 4 N^2 d per 
 algorithmic HBM GB/s (K + V + Q + O + LSE bytes).  Phase times come from HIP events on the
 stream the kernels run on.  The fp64 CPU oracle is timed beside it on a bounded sample.
 
+Secondary lines, each timed on its own after the step (skipped with --no-extras): decode with
+per-sequence cache lengths, multi-token decode, chunked prefill (Nq != Nk), packed sequences of
+different lengths (forward and backward), a block-sparse mask (forward and backward) and the
+d=64 batched prefill.  Their FLOP counts are 4 d per (query, key) pair the mask keeps.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 """
 from __future__ import annotations
