@@ -307,7 +307,7 @@ static attn_status_t decode_impl(const void* q, const void* k_cache, const void*
   if (dtype != ATTN_BF16) return fail(dtype == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG,
                                       "decode supports bf16 only");
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "decode supports d in {64, 128} (got %d)", d);
-  if (T * (Hq / Hkv) > xattn::kDecMaxRows)
+  if ((long long)T * (Hq / Hkv) > xattn::kDecMaxRows)
     return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most %d (token, head) rows per KV head (T=%d, group %d)",
                 xattn::kDecMaxRows, T, Hq / Hkv);
   const size_t need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, num_splits);
@@ -316,6 +316,8 @@ static attn_status_t decode_impl(const void* q, const void* k_cache, const void*
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   int splits, kps;
   decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
+  if ((long long)B * Hkv * ((T * (Hq / Hkv) + 31) / 32) * splits > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large");
   const size_t rows = (size_t)splits * xattn::decode_partials_per_split(T, Hq / Hkv) * B * Hq * T;
   float* part_o = (float*)workspace;
   float* part_lse = (float*)((char*)workspace + align_up(rows * d * sizeof(float), 256));

@@ -215,15 +215,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
   }
 }
 
-// Decode with up to 32 (token, head) rows per KV head on the matrix cores, as the forward
-// computes a 32-row block: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K rows straight from
+// Decode with (token, head) rows of a KV head on the matrix cores, 32 per workgroup, as the
+// forward computes a 32-row block: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K rows straight from
 // global memory as the A operand, the rows' Q^T resident as the B operand), so that in the C
 // layout each lane owns one row and 16 keys; the probabilities are then already the B operand
 // of O^T += V^T P^T, whose V^T operand is read with the transposing ds_read_b64_tr_b16 from a
 // per-wave double-buffered LDS copy of the 32-key V block (direct global -> LDS, swizzled as
 // the forward's tiles).  Each of the four waves walks every fourth 32-key block of the
 // workgroup's chunk and writes its own partial (O_w, lse_w): the merge kernel combines
-// 4 x splits partials, exactly as it combines chunks.
+// 4 x splits partials, exactly as it combines chunks.  More than 32 rows take several
+// workgroups, each reading the cache once.
 template <int D>
 __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -236,9 +237,11 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(1024))) char vbuf[kDecWaves * 2 * VBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
-  const int g = Hq / Hkv, R = T * g;
+  const int g = Hq / Hkv, R = T * g, nrc = (R + 31) / 32;
+  // Workgroup (b*Hkv + kv head, 32-row chunk rc of the group's R rows, key chunk split).
   const int split = blockIdx.x % splits;
-  const int bk = blockIdx.x / splits;  // b * Hkv + kv head
+  const int rc = (blockIdx.x / splits) % nrc;
+  const int bk = blockIdx.x / (splits * nrc);  // b * Hkv + kv head
   const int b = bk / Hkv, kvh = bk - b * Hkv;
   const int len = seqlens != nullptr ? min(max(seqlens[b], 0), L) : L;
   const int kbeg = split * keys_per_split;
@@ -246,9 +249,11 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const uint16_t* kp = kc + (size_t)bk * L * D;
   const uint16_t* vp = vc + (size_t)bk * L * D;
 
-  // Row l32: token l32 / g of head kvh*g + l32 % g.  Q^T operand: features 16c + 8*h32 .. +7.
-  const int tok = l32 / g, hh = l32 - tok * g;
-  const bool row_ok = l32 < R;
+  // Row r = 32 rc + l32: token r / g of head kvh*g + r % g.  Q^T operand: features 16c +
+  // 8*h32 .. +7.
+  const int row_r = 32 * rc + l32;
+  const int tok = row_r / g, hh = row_r - tok * g;
+  const bool row_ok = row_r < R;
   const int klast = (causal && row_ok) ? len - T + tok : 0x7fffffff;  // last key of the row
   bf16x8 qreg[DC];
 #pragma unroll
@@ -398,7 +403,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
 template <int D>
 static hipError_t launch_decode_mma(const DecodeArgs& a) {
   const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((decode_mma_kernel<D>), dim3(a.B * a.Hkv * a.splits), dim3(kDecWaves * 64), 0, a.stream,
+  const int nrc = (a.T * (a.Hq / a.Hkv) + 31) / 32;  // 32-row chunks per KV head
+  hipLaunchKernelGGL((decode_mma_kernel<D>), dim3(a.B * a.Hkv * nrc * a.splits), dim3(kDecWaves * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.part_o, a.part_lse, a.B,
                      a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2, a.seqlens, a.T, a.causal);
   hipError_t e = hipGetLastError();

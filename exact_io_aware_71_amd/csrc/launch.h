@@ -50,7 +50,7 @@ struct DecodeArgs {
   float* part_lse;      // [splits * partials per split, B, Hq, T] fp32 (base-2 log-sum-exp)
   hipStream_t stream;
   const int* seqlens;   // [B] keys per sequence (device), clamped to [0, L]; null = L for all
-  int T;                // query tokens per sequence (T * Hq/Hkv <= 32); q/o [B,Hq,T,d]
+  int T;                // query tokens per sequence (T * Hq/Hkv <= kDecMaxRows); q/o [B,Hq,T,d]
   int causal;           // token t sees keys j <= len - T + t
 };
 
@@ -59,13 +59,13 @@ constexpr int kMaxSparseKeys = 8191 * 64;
 
 // Decode path: rows = T * (Hq/Hkv) (token, head) pairs per KV head.  Up to XATTN_DEC_VALU_ROWS
 // rows the vector-ALU kernel (one partial per workgroup), above it the matrix-core kernel
-// (one partial per wave: four per workgroup) up to kDecMaxRows.  Measured on the 2 GiB decode
+// (one partial per wave: four per workgroup; 32 rows per workgroup) up to kDecMaxRows.  Measured on the 2 GiB decode
 // cache: at 4 and 8 rows the vector-ALU kernel is 3-6% faster, at 16 rows the matrix-core one
 // 1.7x (its P V no longer scales with the row count).
 #ifndef XATTN_DEC_VALU_ROWS
 #define XATTN_DEC_VALU_ROWS 8
 #endif
-constexpr int kDecMaxRows = 32;
+constexpr int kDecMaxRows = 4096;
 inline bool decode_uses_mma(int T, int g) { return T * g > XATTN_DEC_VALU_ROWS; }
 inline int decode_partials_per_split(int T, int g) { return decode_uses_mma(T, g) ? 4 : 1; }
 

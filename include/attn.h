@@ -217,7 +217,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int num
  *   num_splits                 0 = attn_decode_auto_splits(), else 1..L (clamped to
  *                              ceil(L/32) chunks of whole 32-key blocks)
  *   workspace                  >= attn_decode_workspace_bytes(...) bytes, 256-byte aligned
- * Supported: BF16, d in {64, 128}, 1 <= Hq/Hkv <= 32.  Bitwise deterministic for a fixed
+ * Supported: BF16, d in {64, 128}, 1 <= Hq/Hkv <= 4096.  Bitwise deterministic for a fixed
  * split count.
  */
 attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
@@ -255,8 +255,9 @@ size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int L, i
  *                 positions of their sequence); causal == 0: every token sees all len keys
  * A token that sees no key gets o = 0 and lse = -inf.  T = 1 computes what attn_decode (or,
  * with seqlens, attn_decode_varlen) computes.
- * Supported: BF16, d in {64, 128}, T * Hq/Hkv <= 32.  Workspace as
- * attn_decode_multi_workspace_bytes().  Bitwise deterministic for a fixed split count.
+ * Supported: BF16, d in {64, 128}, T * Hq/Hkv <= 4096 (beyond 32 rows per KV head the cache is
+ * read once per 32 rows).  Workspace as attn_decode_multi_workspace_bytes().  Bitwise
+ * deterministic for a fixed split count.
  */
 attn_status_t attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
                                 const int* seqlens, void* o, float* lse, int B, int Hq, int Hkv,

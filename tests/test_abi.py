@@ -151,7 +151,8 @@ def test_decode_plan_and_validation():
     def dec(Hq=32, Hkv=8, d=128, dt=1, splits=0, ws=P, ws_bytes=need, scale=0.1):
         return lib.attn_decode(P, P, P, P, P, 64, Hq, Hkv, 8192, d, dt, ctypes.c_float(scale), splits, ws,
                                ws_bytes, None)
-    assert dec(Hq=66, Hkv=2) == 2   # 33 heads per group (at most 32 rows per KV head)
+    assert lib.attn_decode(P, P, P, P, P, 1, 8194, 2, 64, 128, 1, ctypes.c_float(0.1), 0, P, 1 << 30, None) == 2
+    assert b"rows per KV head" in lib.attn_last_error()  # 4097 heads per group
     assert dec(d=32) == 2
     assert dec(dt=0) == 2
     assert dec(splits=-1) == 1
@@ -163,7 +164,7 @@ def test_decode_plan_and_validation():
         return lib.attn_decode_multi(P, P, P, seqlens, P, P, 64, Hq, Hkv, T, 8192, 128, 1, 1, ctypes.c_float(0.1), 0, P,
                                      1 << 30, None)
     assert decm(T=0) == 1
-    assert decm(T=9) == 2            # 9 tokens x 4 heads > 32 rows
+    assert decm(T=1025) == 2         # 1025 tokens x 4 heads > 4096 rows per KV head
     assert decm(seqlens=P + 4) == 1  # misaligned
     assert lib.attn_decode_multi_workspace_bytes(64, 32, 8, 4, 8192, 128, 0) >= 4 * need - 1024
 

@@ -185,7 +185,7 @@ def test_decode_full_size_sampled_batches(gpu_lib, decode_inputs, splits):
 
 
 @pytest.mark.parametrize("L", [1, 33, 1000])
-@pytest.mark.parametrize("g", [1, 3, 4, 5, 16, 32])
+@pytest.mark.parametrize("g", [1, 3, 4, 5, 16, 32, 48])
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_small(gpu_lib, L, g, d):
     import torch
@@ -312,7 +312,7 @@ def run_decode_multi(lib, q, kc, vc, lens, causal, splits, scale):
 
 
 @pytest.mark.parametrize("T,Hq,Hkv", [(1, 8, 2), (2, 8, 2), (4, 8, 2), (3, 10, 2), (16, 4, 4), (8, 8, 2), (32, 2, 2),
-                                     (2, 32, 2), (5, 6, 2)])
+                                     (2, 32, 2), (5, 6, 2), (16, 8, 2), (40, 2, 2), (3, 32, 2)])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("splits", [0, 3, 16])
