@@ -329,8 +329,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // work at the same time within one wave.  The S and P register sets alternate roles between
 // even and odd steps.  K and V arrive in 64-key tiles through direct global -> LDS copies
 // into two rings of four stages (128 KB); the two steps of tile t read K_t, K_{t+1}, V_{t-1},
-// V_t, copy K_{t+3} and V_{t+2}, and end with one barrier.  A rescale of O forced by a moved
-// running max is applied after the step's MFMAs, before P_u is added.
+// V_t, copy K_{t+3} and V_{t+2}, and end with one barrier.  With 32-key tiles (64 KB, four
+// waves: two workgroups per CU) each step is a tile of its own: step t reads K_{t+1} and
+// V_{t-1}, copies K_{t+3} and V_{t+2}, and ends with the barrier.  A rescale of O forced by a
+// moved running max is applied after the step's MFMAs, before P_u is added.
 #ifndef XATTN_FWD_ILV
 #define XATTN_FWD_ILV 1
 #endif
@@ -354,6 +356,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #endif
 #ifndef XATTN_ILV_RB
 #define XATTN_ILV_RB 1
+#endif
+// Dense and packed d = 128 inputs come in two shapes.  Wide: 8 waves (256 query rows) with
+// 64-key tiles, one workgroup per CU (128 KB of LDS).  Narrow: 4 waves (128 rows) with 32-key
+// tiles (64 KB), two workgroups per CU, so that one's prologue (Q loads, first copies) and
+// epilogue (O stores) overlap the other's steps; it pays twice the copies and barriers per
+// key.  Measured per workgroup, prologue plus epilogue cost about as much as 4-5 64-key tiles,
+// so the narrow shape wins when a query tile walks few keys (+8% at N = 2048 causal, +18% at
+// N = 512, +10% on packed batches of 256-4096 tokens), ties at 2048 keys (N = 4096 causal)
+// and loses 2-5% on long walks (non-causal N = 4096, causal N = 16384, a 1024-query chunk
+// onto 8192 keys).  Both give bit-identical results (same 32-key block order and arithmetic).
+// The narrow shape is taken below XATTN_FWD128_NARROW_KEYS average keys per query tile
+// (0: never), or when the wide grid would leave CUs idle.
+#ifndef XATTN_FWD128_NARROW_KEYS
+#define XATTN_FWD128_NARROW_KEYS 2048
 #endif
 // 1: the running max is checked through the row sums of the new probabilities instead of a
 // per-step row max (see the step below).
@@ -387,30 +403,34 @@ __device__ __forceinline__ void mfma_qk_next(f32x16& c, const bf16x8& a, const b
 }
 __device__ __forceinline__ void qk_result_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-template <int D, int RB_, int NW_ = 8 / RB_>
+template <int D, int RB_, int NW_ = 8 / RB_, int BN_ = kFwdBN>
 struct IlvShape {
-  static constexpr int BN = kFwdBN, DC = D / 16, DB = D / 32;
+  static constexpr int BN = BN_, DC = D / 16, DB = D / 32;
+  static constexpr int SPT = BN / 32;              // 32-key steps per tile
   static constexpr int RB = RB_, NW = NW_, BM = NW * RB * 32;
   static constexpr int TILE = BN * D * 2;          // bytes of one K or V tile
   static constexpr int NS = 4;                     // stages per ring
   static constexpr int RPC = 1024 / (2 * D);       // tile rows per 1 KB wave copy
-  static constexpr int CPW = TILE / 1024 / NW;     // copies per wave and tile
+  static constexpr int CPW = TILE / 1024 / NW;     // copies per wave and tile of one tensor
+  static constexpr int CPS = SPT == 2 ? CPW : 2 * CPW;  // copies per wave and step
+  static_assert(SPT == 1 || SPT == 2, "32- or 64-key tiles");
   static constexpr int NPV = 2 * DB;               // V^T operands per 32-key block
   static constexpr int NQK = DC;                   // K operands per 32-key block
 };
 
-template <int D, int RB_, int NW_, bool CAUSAL, bool SPARSE>
+template <int D, int RB_, int NW_, int BN_, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB_, 2 / RB_))) void fwd_ilv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask bm,
     float scale_log2, int n_qtiles, int BH) {
-  using S = IlvShape<D, RB_, NW_>;
-  constexpr int BN = S::BN, DC = S::DC, DB = S::DB, RB = S::RB, NS = S::NS, NW = S::NW;
-  constexpr int TILE = S::TILE, CPW = S::CPW, RPC = S::RPC, NPV = S::NPV, NQK = S::NQK;
+  using S = IlvShape<D, RB_, NW_, BN_>;
+  constexpr int BN = S::BN, SPT = S::SPT, DC = S::DC, DB = S::DB, RB = S::RB, NS = S::NS, NW = S::NW;
+  constexpr int TILE = S::TILE, CPW = S::CPW, CPS = S::CPS, RPC = S::RPC, NPV = S::NPV, NQK = S::NQK;
   constexpr int NOPS = NPV + NQK, NMF = RB * NOPS, L = XATTN_ILV_LOOKAHEAD;
-  static_assert(NS == 4 && CPW <= 4, "copy schedule");
-  constexpr int CSP = NMF / CPW;  // MFMA slots per copy
-  static_assert(NMF % CPW == 0, "copies spread evenly over the step");
+  static_assert(NS == 4 && CPS <= 4, "copy schedule");
+  static_assert(!SPARSE || BN == 64, "the block-sparse tile list counts 64-key tiles");
+  constexpr int CSP = NMF / CPS;  // MFMA slots per copy
+  static_assert(NMF % CPS == 0, "copies spread evenly over the step");
   __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];  // [K ring | V ring]
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];             // kept key tiles
 
@@ -493,6 +513,9 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     epilogue();  // every block dropped)
     return;
   }
+  // 32-key tiles go two per pass: an odd count gets one more tile past the last key (clamped
+  // copies, every score masked: probabilities 0), whose step does the last P V product.
+  if constexpr (SPT == 1) T += T & 1;
   auto entry = [&](int i) __attribute__((always_inline)) -> int {
     return __builtin_amdgcn_readfirstlane((int)tlist[min(i, T - 1)]);
   };
@@ -523,12 +546,14 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     const uint32_t m0v = wdst + (is_k ? 0 : NS * TILE) + (tile & (NS - 1)) * TILE + 1024 * i;
     dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff[i] - lrow * (2 * D)), m0v);
   };
-  // LDS base of 32-key block u of K (V): tile u/2, rows 32*(u%2) ..
+  // LDS base of 32-key block u of K (V): tile u/SPT, rows 32*(u%SPT) ..  (u = -1 at the
+  // first step: the zeroed last stage.)
+  constexpr int SPT_SH = SPT == 2 ? 1 : 0;
   auto kblk = [&](int u) __attribute__((always_inline)) {
-    return smem + ((u >> 1) & (NS - 1)) * TILE + (u & 1) * 32 * (2 * D);
+    return smem + ((u >> SPT_SH) & (NS - 1)) * TILE + (u & (SPT - 1)) * 32 * (2 * D);
   };
   auto vblk = [&](int u) __attribute__((always_inline)) {
-    return smem + NS * TILE + ((u >> 1) & (NS - 1)) * TILE + (u & 1) * 32 * (2 * D);
+    return smem + NS * TILE + ((u >> SPT_SH) & (NS - 1)) * TILE + (u & (SPT - 1)) * 32 * (2 * D);
   };
   // Operand j of a step: j < NPV are V^T operands (sh, db), db fastest; then the K operands c.
   auto operand = [&](const char* ks, const char* vs, auto jc) __attribute__((always_inline)) -> bf16x8 {
@@ -551,6 +576,19 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   auto kt = [&](int i) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) return entry(i) & 0x3fff;
     else return i;
+  };
+  // Copy ci (< CPS) of step phase ph (0 .. SPT-1) of the steps of tile t: with 64-key tiles
+  // the first step copies K_{t+3}, the second V_{t+2}; with 32-key tiles the one step copies
+  // both.
+  auto step_copy = [&](int t, auto phc, int ci) __attribute__((always_inline)) {
+    constexpr int ph = decltype(phc)::value;
+    if constexpr (SPT == 2) {
+      if constexpr (ph == 0) copy(t + 3, kt(t + 3), true, ci);
+      else copy(t + 2, kt(t + 2), false, ci);
+    } else {
+      if (ci < CPW) copy(t + 3, kt(t + 3), true, ci);
+      else copy(t + 2, kt(t + 2), false, ci - CPW);
+    }
   };
 
   // Prologue: K_0, K_1, K_2, V_0, V_1; V stage 3 (read as block -1, with P_{-1} = 0) is zeroed.
@@ -598,17 +636,16 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     }
   }
 
-  // Step u: sc = S_u (complete), sn <- S_{u+1}, pp = P_{u-1}, pc <- P_u; copies of the
-  // step's half of the tile's copy list (K_{t+3} on even steps, V_{t+2} on odd ones).  Tiles
-  // past the end are copied too, clamped to the last key, into stages nobody reads any more, so
-  // every step issues the same copies and the wait counts stay fixed.  ctile is the walk
-  // position of the copied tile (its ring stage), ckt its key tile; kcur is the key tile of
-  // S_u and keep whether the wave's query block keeps it (block-sparse).
-  auto step = [&](int u, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2], u32x4(&pc)[RB][2],
-                  int ctile, int ckt, bool cis_k, int kcur, bool keep) __attribute__((always_inline)) {
+  // Step u (phase ph of tile t = u / SPT): sc = S_u (complete), sn <- S_{u+1}, pp = P_{u-1},
+  // pc <- P_u; the step's share of the tile's copy list (step_copy).  Tiles past the end are
+  // copied too, clamped to the last key, into stages nobody reads any more, so every step
+  // issues the same copies and the wait counts stay fixed.  kcur is the key tile of S_u and
+  // keep whether the wave's query block keeps it (block-sparse).
+  auto step = [&](int u, auto phc, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2], u32x4(&pc)[RB][2],
+                  int t, int kcur, bool keep) __attribute__((always_inline)) {
     if (active(u)) {
       if constexpr (RB > 1 && XATTN_ILV_QKASM != 0) qk_result_fence();  // S_u came from asm MFMAs
-      const int u0 = kcur * BN + (u & 1) * 32;  // first key of S_u
+      const int u0 = kcur * BN + (u & (SPT - 1)) * 32;  // first key of S_u
       const bool drop = SPARSE && !keep;
       if (drop || (u0 + 32 > Nk) || (CAUSAL && u0 + 31 > qd0)) {
 #pragma unroll
@@ -699,8 +736,8 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
             pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
           }
         });
-        // The step's CPW copies, one every CSP slots (slots 6 and 14 at d = 128).
-        if constexpr (i % CSP == XATTN_ILV_COPY_SLOT % CSP && i / CSP < CPW) copy(ctile, ckt, cis_k, i / CSP);
+        // The step's CPS copies, one every CSP slots (slots 6 and 14 with 64-key tiles at d = 128).
+        if constexpr (i % CSP == XATTN_ILV_COPY_SLOT % CSP && i / CSP < CPS) step_copy(t, phc, i / CSP);
         sched_fence();
       });
       if (XATTN_ILV_PRIO) __builtin_amdgcn_s_setprio(0);
@@ -769,7 +806,7 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
     } else {
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) copy(ctile, ckt, cis_k, i);
+      for (int i = 0; i < CPS; ++i) step_copy(t, phc, i);
     }
   };
 
@@ -780,18 +817,26 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       kc = e & 0x3fff;
       keep = (e >> (14 + wblk)) & 1;
     }
-    step(2 * t, sA, sB, pA, pB, t + 3, kt(t + 3), true, kc, keep != 0);
-    step(2 * t + 1, sB, sA, pB, pA, t + 2, kt(t + 2), false, kc, keep != 0);
-    // K_{t+2} and V_{t+1} (copied in tile t-1) must have landed; this tile's copies may stay
-    // in flight.
+    if constexpr (SPT == 2) {
+      step(2 * t, std::integral_constant<int, 0>{}, sA, sB, pA, pB, t, kc, keep != 0);
+      step(2 * t + 1, std::integral_constant<int, 1>{}, sB, sA, pB, pA, t, kc, keep != 0);
+    } else {  // two 32-key tiles per pass (T is even), so the register roles stay fixed
+      step(t, std::integral_constant<int, 0>{}, sA, sB, pA, pB, t, kc, keep != 0);
+      wait_vmem_n<2 * CPW>();
+      lds_barrier();
+      ++t;
+      step(t, std::integral_constant<int, 0>{}, sB, sA, pB, pA, t, t, true);
+    }
+    // Everything copied before this tile's steps must have landed (64-key tiles: K_{t+2} and
+    // V_{t+1}; 32-key tiles: K_{t+2} and V_t); this tile's copies may stay in flight.
     wait_vmem_n<2 * CPW>();
     lds_barrier();
   }
   wait_vmem();
 
-  // P_{2T-1} V_{2T-1}.
-  if (active(2 * T)) {
-    const char* vs = vblk(2 * T - 1);
+  // P_{last} V_{last} (the last step is odd, so P is in pA).
+  if (active(SPT * T)) {
+    const char* vs = vblk(SPT * T - 1);
     static_for<NPV>([&](auto jc) {
       constexpr int j = decltype(jc)::value, db = j % DB, sh = j / DB;
       const bf16x8 a = operand(vs, vs, jc);
@@ -918,14 +963,31 @@ hipError_t launch_fwd(const FwdArgs& a) {
     return launch_fwd_grid<float>(a.causal ? fwd_f32_kernel<true> : fwd_f32_kernel<false>, 128, 256, a);
 #if XATTN_FWD_ILV
   if (a.d == 128) {
-    using S = IlvShape<128, XATTN_ILV_RB>;
-    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, XATTN_ILV_RB, S::NW), S::BM, S::NW * 64, a);
+    if (a.block_mask) {  // the block-sparse tile list counts 64-key tiles
+      using S = IlvShape<128, XATTN_ILV_RB>;
+      return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, XATTN_ILV_RB, S::NW, S::BN), S::BM,
+                                       S::NW * 64, a);
+    }
+    // Average keys walked by one query tile (packed: per-sequence averages).
+    const double nq = a.cu_q ? (double)a.Nq / a.B : (double)a.Nq;
+    const double nk = a.cu_q ? (double)a.Nk / a.B : (double)a.Nk;
+    const double walk = a.causal ? (nk > nq ? nk - nq : 0.0) + 0.5 * (nq < nk ? nq : nk) : nk;
+    using W = IlvShape<128, 1, 8, 64>;
+    using N = IlvShape<128, 1, 4, 32>;
+    const long long wide_grid = (long long)((a.max_q + W::BM - 1) / W::BM) * a.B * a.Hq;
+    if (walk < XATTN_FWD128_NARROW_KEYS || wide_grid < 256)
+      return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, 1, N::NW, N::BN, true, false>
+                                                : fwd_ilv_kernel<128, 1, N::NW, N::BN, false, false>,
+                                       N::BM, N::NW * 64, a);
+    return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, 1, W::NW, W::BN, true, false>
+                                              : fwd_ilv_kernel<128, 1, W::NW, W::BN, false, false>,
+                                     W::BM, W::NW * 64, a);
   }
 #endif
 #if XATTN_FWD64_ILV
   if (a.d == 64) {
     using S = IlvShape<64, 1, XATTN_FWD64_ILV_NW>;
-    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, 1, S::NW), S::BM, S::NW * 64, a);
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, 1, S::NW, S::BN), S::BM, S::NW * 64, a);
   }
 #endif
   if (a.d == 128) {

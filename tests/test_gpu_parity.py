@@ -77,6 +77,39 @@ def test_fwd_long4k_full_heads(gpu_lib):
             assert_fwd_ok(fwd_errors(o[:, h:h + 1], o_ref, lse[:, h:h + 1], lse_ref), f"h{h} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_fwd_shapes_agree(gpu_lib, causal):
+    """d = 128 runs in two workgroup shapes (256 query rows with 64-key tiles, or 128 rows
+    with 32-key tiles), chosen by the average key walk and by how many CUs the wide grid
+    fills.  32 heads at N = 4096 take the wide shape (walk >= 2048 keys, 512 workgroups);
+    two of those heads alone take the narrow one (32 wide workgroups would leave CUs idle).
+    Heads are independent and both shapes take the same 32-key blocks in the same order, so
+    the results must agree exactly; the narrow run, a long walk, is also checked on sampled
+    rows against the oracle."""
+    w = WORKLOADS["long4k"]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed + 11, qk_mult=w.qk_mult)
+    scale = default_scale(w.d)
+    o_wide, lse_wide = run_fwd(gpu_lib, inp, causal, scale)
+    sl = {kk: np.ascontiguousarray(inp[kk][:, 5:7]) for kk in ("q", "k", "v")}
+    o_nar, lse_nar = run_fwd(gpu_lib, sl, causal, scale)
+    assert np.array_equal(o_nar, o_wide[:, 5:7]) and np.array_equal(lse_nar, lse_wide[:, 5:7])
+    rows = sample_rows(w.N, 17 + int(causal), extra=60)
+    o_ref, lse_ref = oracle.forward_rows(sl["q"], sl["k"], sl["v"], scale, causal, rows)
+    assert_fwd_ok(fwd_errors(o_nar[:, :, rows], o_ref, lse_nar[:, :, rows], lse_ref), "narrow long walk")
+
+
+@pytest.mark.parametrize("N", [970, 1001])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_odd_key_tiles(gpu_lib, N, causal):
+    """N = 970 leaves 31 32-key tiles (an odd count, padded by one fully masked tile) for every
+    query tile without the causal mask and for the last one with it; N = 1001 leaves 32."""
+    inp = make_prefill(1, 4, 2, N, 128, "bf16", seed=N + int(causal))
+    scale = default_scale(128)
+    o, lse = run_fwd(gpu_lib, inp, causal, scale)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], scale, causal)
+    assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), f"N={N}")
+
+
 @pytest.mark.parametrize("N", [1, 2, 17, 100, 257, 300])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
