@@ -9,7 +9,9 @@ One step = one pass of the whole path on synthetic inputs already resident in HB
 Reported value: forward+backward TFLOP/s with the algorithmic count 4 N^2 d per head
 (halved for causal) for the forward and 2.5x that for the backward.  Decode is reported as
 algorithmic HBM GB/s (K + V + Q + O + LSE bytes).  Phase times come from HIP events on the
-stream the kernels run on.  The fp64 CPU oracle is timed beside it on a bounded sample.
+stream the kernels run on, over K steps after W untimed warm-up steps (default 50: after an
+idle gap the shader clock needs some 25 ms of load to settle, and the timed steps should not
+include that ramp).  The fp64 CPU oracle is timed beside it on a bounded sample.
 
 Secondary lines, each timed on its own after the step (skipped with --no-extras): decode with
 per-sequence cache lengths, multi-token decode, chunked prefill (Nq != Nk), packed sequences of
@@ -128,7 +130,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the secondary workloads (chunked prefill, packed, block-sparse, d=64, "
@@ -213,32 +215,33 @@ def main():
     # outside the timed step.
     extras = {}
     if not args.no_extras:
-        # Variable-length decode, outside the timed step: same cache, lengths vlens.
-        for _ in range(3):
-            attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
-        vev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        reps = 10
-        vev[0].record(stream)
-        for _ in range(reps):
-            attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o, lse=dec_lse, workspace=ws_d)
-        vev[1].record(stream)
-        torch.cuda.synchronize()
-        ms_vdec = vev[0].elapsed_time(vev[1]) / reps
-        vdec_bytes = int(vlens.sum()) * DHkv * d * 2 * 2 + 2 * DB * DHq * d * 2 + DB * DHq * 4
-
-        # Secondary forward lines, outside the timed step, FLOPs = 4 d per (query, key) pair the
-        # mask keeps.  Chunked prefill: a 1024-token chunk appended to 7168 cached tokens
-        # (Nk = 8192, causal aligned at the bottom right), B=4, Hq=32, Hkv=8, d=128.
-        def time_call(fn, reps=10):
-            for _ in range(3):
-                fn()
+        def time_call(fn, reps=20, warm_ms=40.0):
+            """Mean ms of one call over `reps` back-to-back calls, after about `warm_ms` of
+            back-to-back warm-up calls: inputs are generated on the host with the GPU idle, and
+            after such a gap the shader clock takes some 25 ms of load to settle."""
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            fn()
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            for _ in range(min(4000, int(warm_ms / max(ev[0].elapsed_time(ev[1]), 1e-3)) + 3)):
+                fn()
             ev[0].record(stream)
             for _ in range(reps):
                 fn()
             ev[1].record(stream)
             torch.cuda.synchronize()
             return ev[0].elapsed_time(ev[1]) / reps
+
+        # Variable-length decode, outside the timed step: same cache, lengths vlens.
+        ms_vdec = time_call(lambda: attn.attn_decode_varlen(dq_, dk_, dv_, vlens_dev, scale, num_splits=0, o=dec_o,
+                                                            lse=dec_lse, workspace=ws_d))
+        vdec_bytes = int(vlens.sum()) * DHkv * d * 2 * 2 + 2 * DB * DHq * d * 2 + DB * DHq * 4
+
+        # Secondary forward lines, outside the timed step, FLOPs = 4 d per (query, key) pair the
+        # mask keeps.  Chunked prefill: a 1024-token chunk appended to 7168 cached tokens
+        # (Nk = 8192, causal aligned at the bottom right), B=4, Hq=32, Hkv=8, d=128.
 
         log("chunked prefill and packed variable-length forward")
         CB, CHq, CHkv, CNq, CNk = 4, 32, 8, 1024, 8192
