@@ -40,6 +40,13 @@
 #ifndef XATTN_DKDV_SPREAD
 #define XATTN_DKDV_SPREAD 1
 #endif
+// dQ: slot-interleaved tile body (0: block by block) and its LDS operand lookahead.
+#ifndef XATTN_DQ_ILV
+#define XATTN_DQ_ILV 1
+#endif
+#ifndef XATTN_DQ_LOOKAHEAD
+#define XATTN_DQ_LOOKAHEAD 4
+#endif
 
 namespace xattn {
 
@@ -517,6 +524,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ dQ
+// Slot of vector group g (0..3) within an interleaved phase of L MFMA slots.
+constexpr int dq_vslot(int L, int g) { return 1 + g * (L - 2) / 3; }
+
 // Also forms the per-row statistics the dK/dV kernel reads (it runs first): LSE2 = LSE*log2(e)
 // and D = rowsum(dO * O) for its 128 rows, padding rows up to the sequence's multiple of 64
 // getting +inf and 0.
@@ -654,6 +664,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wait_vmem();  // also covers the Q/dO loads
   lds_barrier();
   // Tile t+1 is copied during tile t (past the end: rows clamped, into the idle stage).
+#if XATTN_DQ_ILV
+  // Interleaved tile: the MFMAs of one 64-key tile run in fixed slots and the vector work of
+  // each key block sits between the MFMAs that do not depend on it.  Slot phases (one MFMA
+  // per slot, DC = D/16 slots for a score block, 2*DB for a dQ block):
+  //   A: S_0 = K_0 Q^T          B: dP_0 = V_0 dO^T    || P_0 = 2^(S_0 scale log2 e - LSE2)
+  //   C: S_1                    || dS_0 = P_0 (dP_0 - D), packed to bf16
+  //   D: dP_1                   || P_1
+  //   E: dQ += dS_0 K_0         || dS_1
+  //   F: dQ += dS_1 K_1
+  // Masked keys (causal, or past the last key) get P = 0 in a uniform branch taken only by
+  // blocks that hold such a key.  Per accumulator the products are summed in the same order
+  // as block by block, so the result does not depend on this schedule.  The next tile's copy
+  // pieces go out on the odd slots of phases A and B; LDS operands are read LA slots ahead.
+  constexpr int LA = XATTN_DQ_LOOKAHEAD;
+  constexpr int PA = 0, PB = DC, PC = 2 * DC, PD = 3 * DC, PE = 4 * DC, PF = 4 * DC + 2 * DB, NSLOT = 4 * DC + 4 * DB;
+  static_assert(CPW <= DC, "copy pieces fit the odd slots of phases A and B");
+  static_assert((STAGE & (STAGE - 1)) == 0 && STAGE >= 2 * T::BYTES, "stage toggled by XOR");
+  TileOffsets<D> ofs;  // operand offsets of the current stage (toggled per tile)
+  ofs.init(lane);
+  // Operand j of a tile: [A | B | C | D] row-major K or V chunks, [E | F] K^T of block 0 / 1.
+  auto opnd = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < PE) {
+      constexpr int ph = j / DC, c = j % DC, kb = ph / 2, isv = ph % 2;
+      return *reinterpret_cast<const bf16x8*>(smem + ofs.k[c] + (isv * T::BYTES + kb * 32 * 2 * D));
+    } else {
+      constexpr int jj = j - PE, kb = jj / (2 * DB), sh = (jj % (2 * DB)) / DB, db = jj % DB;
+      constexpr int roff = (kb * 32 + 16 * sh) * 2 * D;
+      return join_tr(ds_read_tr16(smem + ofs.v[db][0] + roff), ds_read_tr16(smem + ofs.v[db][1] + roff));
+    }
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = kt(t) * BN, kn = kt(t + 1);
+    if (CAUSAL && t0 > qd0 + 31) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) copy_piece(t + 1, kn, i);
+    } else {
+      f32x16 s0, dp0, s1, dp1;
+      bf16x8 ds0[2], ds1[2];
+      bf16x8 buf[LA];
+      static_for<LA>([&](auto jc) { buf[decltype(jc)::value] = opnd(jc); });
+      // Keys of block kb for this lane: t0 + 32 kb + 8(r/4) + 4*h32 + r%4.
+      auto mask_block = [&](f32x16& p, int kb) __attribute__((always_inline)) {
+        const int kb0 = t0 + kb * 32;
+        if ((kb0 + 32 > Nk) || (CAUSAL && kb0 + 31 > qd0)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kj = kb0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+            if (kj >= Nk || (CAUSAL && kj > kmax)) p[r] = 0.f;
+          }
+        }
+      };
+      auto exp_group = [&](f32x16& x, int g) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * g + e] = fast_exp2(fmaf(x[4 * g + e], scale_log2, -lse2));
+        asm volatile("" : "+v"(x[4 * g]), "+v"(x[4 * g + 1]), "+v"(x[4 * g + 2]), "+v"(x[4 * g + 3]));
+      };
+      auto ds_group = [&](const f32x16& p, f32x16& dp, bf16x8 (&ds)[2], int g) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * g + e] = p[4 * g + e] * (dp[4 * g + e] - dl);
+        if (g % 2 == 1) {
+          ds[g / 2] = pack8(dp, g / 2);
+          asm volatile("" : "+v"(ds[g / 2]));
+        }
+      };
+      sched_fence();
+      static_for<NSLOT>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        // Uniform mask branches before the first vector work that reads P of a block.
+        if constexpr (i == PC) { sched_fence(); mask_block(s0, 0); sched_fence(); }
+        if constexpr (i == PE) { sched_fence(); mask_block(s1, 1); sched_fence(); }
+        if constexpr (i < PB) {
+          if constexpr (i == PA) { s0 = mfma32(buf[i % LA], qreg[0], f32x16{}); }
+          else s0 = mfma32(buf[i % LA], qreg[i - PA], s0);
+        } else if constexpr (i < PC) {
+          if constexpr (i == PB) dp0 = mfma32(buf[i % LA], doreg[0], f32x16{});
+          else dp0 = mfma32(buf[i % LA], doreg[i - PB], dp0);
+        } else if constexpr (i < PD) {
+          if constexpr (i == PC) s1 = mfma32(buf[i % LA], qreg[0], f32x16{});
+          else s1 = mfma32(buf[i % LA], qreg[i - PC], s1);
+        } else if constexpr (i < PE) {
+          if constexpr (i == PD) dp1 = mfma32(buf[i % LA], doreg[0], f32x16{});
+          else dp1 = mfma32(buf[i % LA], doreg[i - PD], dp1);
+        } else if constexpr (i < PF) {
+          constexpr int jj = i - PE, sh = jj / DB, db = jj % DB;
+          dq_acc[db] = mfma32(ds0[sh], buf[i % LA], dq_acc[db]);
+        } else {
+          constexpr int jj = i - PF, sh = jj / DB, db = jj % DB;
+          dq_acc[db] = mfma32(ds1[sh], buf[i % LA], dq_acc[db]);
+        }
+        if constexpr (i + LA < NSLOT) buf[i % LA] = opnd(std::integral_constant<int, i + LA>{});
+        static_for<4>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          if constexpr (i == PB + dq_vslot(DC, g)) exp_group(s0, g);
+          if constexpr (i == PC + dq_vslot(DC, g)) ds_group(s0, dp0, ds0, g);
+          if constexpr (i == PD + dq_vslot(DC, g)) exp_group(s1, g);
+          if constexpr (i == PE + dq_vslot(2 * DB, g)) ds_group(s1, dp1, ds1, g);
+        });
+        if constexpr (i % 2 == 1 && i / 2 < CPW) copy_piece(t + 1, kn, i / 2);
+        sched_fence();
+      });
+    }
+    ofs.toggle(STAGE);
+    wait_vmem();  // tile t+1 has landed
+    lds_barrier();
+  }
+#else
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = kt(t) * BN, kn = kt(t + 1);
     const char* ks = smem + (t & 1) * STAGE;
@@ -702,6 +819,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vmem();  // tile t+1 has landed
     lds_barrier();
   }
+#endif
   // C layout: lane holds feature db*32 + l32 of queries qw0 + 8(r/4) + 4*h32 + r%4.
 #pragma unroll
   for (int db = 0; db < DB; ++db)
