@@ -133,6 +133,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
   const int grp = wave & (NG - 1), role = wave / NG;
+  // MFMA operands from the swizzled LDS tiles of the ring stage this wave reads: per-lane
+  // offsets of row block 0 of that stage (the swizzle repeats every 16 rows), other row blocks
+  // and the dO tile by constants.  Row-major operand: rows row0 + lane%32, chunk 2c + lane/32;
+  // transposed operand: as ld_tr_operand at column db*32.  The offsets move one stage per
+  // iteration (loop-carried, so the compiler keeps 16 registers instead of one per operand).
+  TileOffsets<D> ofs;
+  ofs.init(lane);
   // One workgroup per (batch, KV head, 128 keys).  With grouped-query heads the g query heads
   // sharing the KV head are visited one after the other ([OPT] §5.3 mapping kv = h / g), so
   // dK and dV accumulate the whole group's gradient without atomics.
@@ -255,6 +262,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lds_barrier();
 
   char* pbase = smem + NS * STAGE + grp * PGRP;
+  auto rowop = [&](int tofs, int row0, int c) __attribute__((always_inline)) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(smem + ofs.k[c] + (tofs + row0 * (2 * D)));
+  };
+  auto trop = [&](int tofs, int row0, int db) __attribute__((always_inline)) -> bf16x8 {
+    const int o = tofs + row0 * (2 * D);
+    return join_tr(ds_read_tr16(smem + ofs.v[db][0] + o), ds_read_tr16(smem + ofs.v[db][1] + o));
+  };
+  // The dV wave reads the stage of tile vt, the dK wave the stage of tile vt - 1.
+  auto ofs_add = [&](int delta) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c) ofs.k[c] += delta;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      ofs.v[db][0] += delta;
+      ofs.v[db][1] += delta;
+    }
+  };
+  if (role == 1) ofs_add((NS - 1) * STAGE);
   auto dv_tile_plain = [&](int vt, int t) __attribute__((always_inline)) {
     // dV wave, virtual tile vt (query tile t): S = Q K^T, P = 2^(S scale log2 e - LSE2)
     // (masked), P to LDS, dV += P^T dO.
@@ -270,7 +295,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) sv[qb][r] = 0.f;
 #pragma unroll
       for (int c = 0; c < DC; ++c)
-        sv[qb] = mfma32(*reinterpret_cast<const bf16x8*>(qs + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], sv[qb]);
+        sv[qb] = mfma32(rowop(0, qb * 32, c), kreg[c], sv[qb]);
     }
     bf16x8 pa[NQB][2];
 #pragma unroll
@@ -302,7 +327,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int sh = 0; sh < 2; ++sh)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc[db] = mfma32(pa[qb][sh], ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+          acc[db] = mfma32(pa[qb][sh], trop(T::BYTES, qb * 32 + 16 * sh, db), acc[db]);
   };
   auto dk_tile_plain = [&](int tt) __attribute__((always_inline)) {
     // dK wave, tile t-1: dP = dO V^T, dS = P (dP - D) with P from LDS, dK += dS^T Q.
@@ -317,7 +342,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
 #pragma unroll
       for (int c = 0; c < DC; ++c)
-        dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dos + swz<D>(qb * 32 + l32, 2 * c + h32)), kreg[c], dp[qb]);
+        dp[qb] = mfma32(rowop(T::BYTES, qb * 32, c), kreg[c], dp[qb]);
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -339,7 +364,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bf16x8 dsa = pack8(dp[qb], sh);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc[db] = mfma32(dsa, ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane), acc[db]);
+          acc[db] = mfma32(dsa, trop(0, qb * 32 + 16 * sh, db), acc[db]);
       }
     }
   };
@@ -350,6 +375,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int LA = XATTN_DKDV_LOOKAHEAD;
   constexpr bool kIlv = XATTN_DKDV_ILV && D == 128;  // the slot plan assumes 8 chunks, 4 blocks
   auto dv_tile_ilv = [&](int vt, int cvt, int ch, int ct) __attribute__((always_inline)) {
+   if constexpr (kIlv) {  // only instantiated where the slot plan applies
     const char* qs = smem + (vt % NS) * STAGE;
     const char* dos = qs + T::BYTES;
     const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
@@ -359,10 +385,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto opnd = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
       constexpr int j = decltype(jc)::value;
       if constexpr (j < 16) {
-        return *reinterpret_cast<const bf16x8*>(qs + swz<D>((j / 8) * 32 + l32, 2 * (j % 8) + h32));
+        return rowop(0, (j / 8) * 32, j % 8);
       } else {
         constexpr int jj = j - 16, qb = jj / 8, sh = (jj / 4) % 2, db = jj % 4;
-        return ld_tr_operand<D>(dos, qb * 32 + 16 * sh, db * 32, lane);
+        return trop(T::BYTES, qb * 32 + 16 * sh, db);
       }
     };
     f32x16 sv[NQB];
@@ -408,8 +434,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
       sched_fence();
     });
+   }
   };
+
   auto dk_tile_ilv = [&](int tt, int cvt, int ch, int ct) __attribute__((always_inline)) {
+   if constexpr (kIlv) {  // only instantiated where the slot plan applies
     const char* qs = smem + (tt % NS) * STAGE;
     const char* dos = qs + T::BYTES;
     const float* dls = reinterpret_cast<const float*>(qs + 2 * T::BYTES) + BQ;
@@ -417,10 +446,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto opnd = [&](auto jc) __attribute__((always_inline)) -> bf16x8 {
       constexpr int j = decltype(jc)::value;
       if constexpr (j < 16) {
-        return *reinterpret_cast<const bf16x8*>(dos + swz<D>((j / 8) * 32 + l32, 2 * (j % 8) + h32));
+        return rowop(T::BYTES, (j / 8) * 32, j % 8);
       } else {
         constexpr int jj = j - 16, qb = jj / 8, sh = (jj / 4) % 2, db = jj % 4;
-        return ld_tr_operand<D>(qs, qb * 32 + 16 * sh, db * 32, lane);
+        return trop(0, qb * 32 + 16 * sh, db);
       }
     };
     f32x16 dp[NQB];
@@ -468,6 +497,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
       sched_fence();
     });
+   }
   };
 
   // Virtual tile vt+1 is copied during iteration vt: up front, or, with XATTN_DKDV_SPREAD, one
@@ -500,6 +530,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (more) wait_vmem();  // virtual tile vt+1 has landed
     lds_barrier();
+    ofs_add(((role == 0 ? vt : vt + NS - 1) % NS) == NS - 1 ? -(NS - 1) * STAGE : STAGE);
     h_cur = h_nxt;
     t_cur = t_nxt;
     if constexpr (SPARSE) {
