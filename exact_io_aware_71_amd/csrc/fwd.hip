@@ -522,6 +522,13 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   const int wblk = (qw0 - q0) / kSparseBlock;  // the wave's query block within the workgroup
   TileOffsets<D> ofs;
   ofs.init(lane);
+  // The V ring sits above the K ring; its base goes into the per-lane V offsets so that the
+  // constant part of every V address fits the 16-bit offset field of the LDS reads.
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    ofs.v[db][0] += NS * TILE;
+    ofs.v[db][1] += NS * TILE;
+  }
 
   // Copies: tile i of K (V) lives in stage i % 4 of the K (V) ring.  Wave copy j covers tile
   // rows RPC*j .. RPC*j + RPC-1; lane l fills physical chunk l of that 1 KB block (row
@@ -552,8 +559,8 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   auto kblk = [&](int u) __attribute__((always_inline)) {
     return smem + ((u >> SPT_SH) & (NS - 1)) * TILE + (u & (SPT - 1)) * 32 * (2 * D);
   };
-  auto vblk = [&](int u) __attribute__((always_inline)) {
-    return smem + NS * TILE + ((u >> SPT_SH) & (NS - 1)) * TILE + (u & (SPT - 1)) * 32 * (2 * D);
+  auto vblk = [&](int u) __attribute__((always_inline)) {  // relative to the V ring (see ofs.v)
+    return smem + ((u >> SPT_SH) & (NS - 1)) * TILE + (u & (SPT - 1)) * 32 * (2 * D);
   };
   // Operand j of a step: j < NPV are V^T operands (sh, db), db fastest; then the K operands c.
   auto operand = [&](const char* ks, const char* vs, auto jc) __attribute__((always_inline)) -> bf16x8 {
@@ -641,8 +648,8 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   // copied too, clamped to the last key, into stages nobody reads any more, so every step
   // issues the same copies and the wait counts stay fixed.  kcur is the key tile of S_u and
   // keep whether the wave's query block keeps it (block-sparse).
-  auto step = [&](int u, auto phc, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2], u32x4(&pc)[RB][2],
-                  int t, int kcur, bool keep) __attribute__((always_inline)) {
+  auto step = [&](int u, auto phc, auto stc, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2],
+                  u32x4(&pc)[RB][2], int t, int kcur, bool keep) __attribute__((always_inline)) {
     if (active(u)) {
       if constexpr (RB > 1 && XATTN_ILV_QKASM != 0) qk_result_fence();  // S_u came from asm MFMAs
       const int u0 = kcur * BN + (u & (SPT - 1)) * 32;  // first key of S_u
@@ -658,8 +665,13 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
           }
         }
       }
-      const char* ks = kblk(u + 1);
-      const char* vs = vblk(u - 1);
+      // K block u+1 and V block u-1 at offsets known at compile time from the ring stage of
+      // tile t (the tile loop is unrolled over the four stages).
+      constexpr int st = decltype(stc)::value, ph = decltype(phc)::value;
+      constexpr int kst = SPT == 2 ? (st + ph) % NS : (st + 1) % NS, khalf = SPT == 2 ? 1 - ph : 0;
+      constexpr int vst = SPT == 2 ? (st + NS - 1 + ph) % NS : (st + NS - 1) % NS, vhalf = SPT == 2 ? 1 - ph : 0;
+      const char* ks = smem + (kst * TILE + khalf * 32 * (2 * D));
+      const char* vs = smem + (vst * TILE + vhalf * 32 * (2 * D));  // V ring base is in ofs.v
       float m4[RB][2];
       float alpha[RB];
       float rs[RB][2];
@@ -810,27 +822,35 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     }
   };
 
-  for (int t = 0; t < T; ++t) {
-    int kc = t, keep = 1;
-    if constexpr (SPARSE) {
-      const int e = entry(t);
-      kc = e & 0x3fff;
-      keep = (e >> (14 + wblk)) & 1;
-    }
-    if constexpr (SPT == 2) {
-      step(2 * t, std::integral_constant<int, 0>{}, sA, sB, pA, pB, t, kc, keep != 0);
-      step(2 * t + 1, std::integral_constant<int, 1>{}, sB, sA, pB, pA, t, kc, keep != 0);
-    } else {  // two 32-key tiles per pass (T is even), so the register roles stay fixed
-      step(t, std::integral_constant<int, 0>{}, sA, sB, pA, pB, t, kc, keep != 0);
-      wait_vmem_n<2 * CPW>();
-      lds_barrier();
-      ++t;
-      step(t, std::integral_constant<int, 0>{}, sB, sA, pB, pA, t, t, true);
-    }
-    // Everything copied before this tile's steps must have landed (64-key tiles: K_{t+2} and
-    // V_{t+1}; 32-key tiles: K_{t+2} and V_t); this tile's copies may stay in flight.
-    wait_vmem_n<2 * CPW>();
-    lds_barrier();
+  // Four tiles per pass, one per ring stage, so that every LDS operand address is a per-lane
+  // offset plus a constant; the pass stops after the last tile.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  for (int t = 0; t < T;) {
+    static_for<NS>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      if (t < T) {
+        if constexpr (SPT == 2) {
+          int kc = t, keep = 1;
+          if constexpr (SPARSE) {
+            const int e = entry(t);
+            kc = e & 0x3fff;
+            keep = (e >> (14 + wblk)) & 1;
+          }
+          step(2 * t, I0{}, stc, sA, sB, pA, pB, t, kc, keep != 0);
+          step(2 * t + 1, I1{}, stc, sB, sA, pB, pA, t, kc, keep != 0);
+        } else if constexpr (st % 2 == 0) {  // 32-key tiles: S/P register roles alternate per tile
+          step(t, I0{}, stc, sA, sB, pA, pB, t, t, true);
+        } else {
+          step(t, I0{}, stc, sB, sA, pB, pA, t, t, true);
+        }
+        // Everything copied before this tile's steps must have landed (64-key tiles: K_{t+2}
+        // and V_{t+1}; 32-key tiles: K_{t+2} and V_t); this tile's copies may stay in flight.
+        wait_vmem_n<2 * CPW>();
+        lds_barrier();
+        ++t;
+      }
+    });
   }
   wait_vmem();
 
