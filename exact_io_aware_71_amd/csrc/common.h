@@ -197,6 +197,27 @@ __device__ __forceinline__ void dma16_m0(const void* base, uint32_t voff, uint32
                : "memory");
 }
 
+// Raw buffer resource (stride 0) over `bytes` bytes at the wave-uniform address `base`: a
+// load through it at a byte offset at or past `bytes` returns zeros, dword by dword (no memory
+// access), so a copy of rows past the end of a tensor needs no clamping.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes) {
+  const uintptr_t u = (uintptr_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)u;
+  r[1] = (int)((uint32_t)(u >> 32) & 0xffffu);  // address bits 47:32; stride 0
+  r[2] = bytes > 0 ? bytes : 0;
+  r[3] = 0x00020000;  // 32-bit data format, no swizzle
+  return r;
+}
+
+// As dma16_m0 through a buffer resource: lane i's 16 bytes at byte offset voff of the buffer
+// (zeros where out of range) land at lds_addr + 16 * i.
+__device__ __forceinline__ void bdma16_m0(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_addr)
+               : "memory");
+}
+
 // As dma16_m0 with 4 bytes per lane.
 __device__ __forceinline__ void dma4_m0(const void* base, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr) : "memory");

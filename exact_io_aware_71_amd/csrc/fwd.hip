@@ -533,25 +533,27 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   // Copies: tile i of K (V) lives in stage i % 4 of the K (V) ring.  Wave copy j covers tile
   // rows RPC*j .. RPC*j + RPC-1; lane l fills physical chunk l of that 1 KB block (row
   // RPC*j + l/(D/8), chunk l%(D/8)), so it reads logical chunk (l%(D/8)) ^ swizzle(row).
-  // Rows past the last key read the last key (finite data whose probabilities are zero).
+  // Each copy goes through a buffer resource over the key rows from the tile's first row on,
+  // so the per-lane byte offset within the tile is a constant and rows past the last key
+  // arrive as zeros (finite data whose probabilities are zero); the resource and the LDS
+  // destination are scalar work.  Byte counts stay below 2^31: the API bounds the key rows
+  // times 2d under that.
   const int lrow = lane / (D / 8);
   uint32_t loff[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int r = RPC * (wave * CPW + i) + lrow;
-    loff[i] = lrow * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(r, 0) >> 4) & (D / 8 - 1)));
+    loff[i] = r * (2 * D) + 16 * ((lane % (D / 8)) ^ ((swz<D>(r, 0) >> 4) & (D / 8 - 1)));
   }
-  // Branch-free (it sits inside the interleaved MFMA sequence): rows are clamped per lane.
-  // Byte offsets stay below 2^31: the API bounds the key rows times 2d under that.  The LDS
-  // destination is computed in scalar registers from a wave index made uniform once.
-  const void* kbase = wave_uniform(kp);
-  const void* vbase = wave_uniform(vp);
+  const char* kbase = reinterpret_cast<const char*>(wave_uniform(kp));
+  const char* vbase = reinterpret_cast<const char*>(wave_uniform(vp));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const uint32_t wdst = lds0 + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (CPW * 1024);
   auto copy = [&](int tile, int ktile, bool is_k, int i) __attribute__((always_inline)) {
-    const int row = min(ktile * BN + RPC * (wave * CPW + i) + lrow, Nk - 1);
+    const int first = ktile * BN;  // first key row of the tile
+    const i32x4 rsrc = buffer_rsrc((is_k ? kbase : vbase) + (size_t)first * (2 * D), (Nk - first) * (2 * D));
     const uint32_t m0v = wdst + (is_k ? 0 : NS * TILE) + (tile & (NS - 1)) * TILE + 1024 * i;
-    dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff[i] - lrow * (2 * D)), m0v);
+    bdma16_m0(rsrc, loff[i], m0v);
   };
   // LDS base of 32-key block u of K (V): tile u/SPT, rows 32*(u%SPT) ..  (u = -1 at the
   // first step: the zeroed last stage.)
