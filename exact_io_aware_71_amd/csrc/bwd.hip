@@ -214,20 +214,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // Branch-free single pieces, for issue between the MFMAs of the interleaved tiles: piece i
-  // of this wave (rows clamped per lane), and the statistics (even waves copy LSE2, odd waves
-  // D; the copies of one kind write the same bytes).
+  // of this wave, and the statistics (even waves copy LSE2, odd waves D; the copies of one
+  // kind write the same bytes).
   const void* qbase = wave_uniform(qp);
   const void* dobase = wave_uniform(dop);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // The piece goes through a buffer resource that starts at its first row, so the per-lane
+  // offset is the constant loff0 and rows past the last query arrive as zeros (their LSE2 is
+  // +inf and D is 0, so they contribute nothing); the address work is scalar.
   auto copy_piece = [&](int vt, int h, int t, int i) __attribute__((always_inline)) {
     const int j = wv + NW * i;
     const bool is_q = j < CPTT;
     const int jt = is_q ? j : j - CPTT;
-    const int row = min(t * BQ + RPC * jt + lrow, Nq - 1);
+    const int first = t * BQ + RPC * jt;
     const uint32_t m0v = lds0 + (vt % NS) * STAGE + (is_q ? 0 : T::BYTES) + 1024 * jt;
-    const char* base = reinterpret_cast<const char*>(is_q ? qbase : dobase) + (size_t)h * geo.nq * D * 2;
-    dma16_m0(base, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
+    const char* base = reinterpret_cast<const char*>(is_q ? qbase : dobase) + ((size_t)h * geo.nq + first) * (2 * D);
+    bdma16_m0(buffer_rsrc(base, (Nq - first) * (2 * D)), loff0, m0v);
   };
   auto copy_stats = [&](int vt, int h, int t) __attribute__((always_inline)) {
     const uint32_t m0v = lds0 + (vt % NS) * STAGE + 2 * T::BYTES + (wv & 1) * BQ * 4;
@@ -665,19 +668,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // Branch-free single pieces of tile t (rows clamped per lane), issued between the MFMAs of
-  // the first key block so that the workgroups' copies do not all queue at the tile start.
+  // Branch-free single pieces of tile t, issued between the MFMAs of the first key blocks so
+  // that the workgroups' copies do not all queue at the tile start.
   const void* kbase = wave_uniform(kp);
   const void* vbase = wave_uniform(vp);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // Through a buffer resource that starts at the piece's first row: constant per-lane offset
+  // loff0, rows past the last key read as zeros (masked), scalar address work.
   auto copy_piece = [&](int t, int ktile, int i) __attribute__((always_inline)) {
     const int j = wv + NW * i;
     const bool is_k = j < CPTT;
     const int jt = is_k ? j : j - CPTT;
-    const int row = min(ktile * BN + RPC * jt + lrow, Nk - 1);
+    const int first = ktile * BN + RPC * jt;
     const uint32_t m0v = lds0 + (t & 1) * STAGE + (is_k ? 0 : T::BYTES) + 1024 * jt;
-    dma16_m0(is_k ? kbase : vbase, (uint32_t)row * (2 * D) + (loff0 - lrow * (2 * D)), m0v);
+    const char* base = reinterpret_cast<const char*>(is_k ? kbase : vbase) + (size_t)first * (2 * D);
+    bdma16_m0(buffer_rsrc(base, (Nk - first) * (2 * D)), loff0, m0v);
   };
 
   uint16_t* dqp = dq + sr.q * D;
