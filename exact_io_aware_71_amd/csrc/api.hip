@@ -185,11 +185,18 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void*
 // dense layout, per sequence (64 spare rows each) in the packed one.
 int bwd_npad(int N) { return (N + 63) / 64 * 64; }
 
-size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
-  (void)Hkv;
-  (void)d;
-  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+static size_t bwd_stats_bytes(int B, int Hq, int N) {
   return align_up(2 * (size_t)B * Hq * bwd_npad(N) * sizeof(float), 256);
+}
+// fp32 partial dK/dV of the split grouped-query backward (see kBwdSplitGrid), after the statistics.
+static size_t bwd_part_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (!xattn::bwd_split_possible(B, Hq, Hkv, N) || d <= 0) return 0;
+  return align_up(4 * (size_t)B * Hkv * N * d * sizeof(float), 256);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  return bwd_stats_bytes(B, Hq, N) + bwd_part_bytes(B, Hq, Hkv, N, d);
 }
 
 size_t attn_bwd_varlen_workspace_bytes(int B, int Hq, int total_q) {
@@ -228,9 +235,12 @@ static attn_status_t bwd_impl(const void* q, const void* k, const void* v, const
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const long long stride = cu_q ? (long long)Nq + 64LL * B : bwd_npad(Nq);
   const long long half = cu_q ? (long long)Hq * stride : (long long)B * Hq * stride;
+  float* part = nullptr;  // dense causal grouped-query backward with few key blocks: split dK/dV
+  if (!cu_q && causal && bwd_part_bytes(B, Hq, Hkv, Nq, d) > 0)
+    part = (float*)((char*)workspace + bwd_stats_bytes(B, Hq, Nq));
   xattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, B, Hq, Hkv, Nq, Nk, max_q, max_k, d,
                    causal ? 1 : 0, scale, (float*)workspace, stride, half, (hipStream_t)stream, block_mask, mask_sb,
-                   mask_sh};
+                   mask_sh, part};
   return from_hip(xattn::launch_bwd(a), "attn_bwd launch");
 }
 

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ stats, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, SeqGeo geo, BlockMask bm, long long stat_stride, long long stat_half, float scale,
-    float scale_log2, int BHkv, int Hq, int Hkv) {
+    float scale_log2, int BHkv, int Hq, int Hkv, float* __restrict__ part, int nsplit) {
   constexpr int NW = 8, NG = 4, BK = NG * 32, BQ = kBwdBQ, DC = D / 16, DB = D / 32, NQB = BQ / 32;
   using T = BwdTile<D>;
   constexpr int STAGE = (2 * T::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // Q, dO, LSE2, D
@@ -142,13 +142,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   ofs.init(lane);
   // One workgroup per (batch, KV head, 128 keys).  With grouped-query heads the g query heads
   // sharing the KV head are visited one after the other ([OPT] §5.3 mapping kv = h / g), so
-  // dK and dV accumulate the whole group's gradient without atomics.
+  // dK and dV accumulate the whole group's gradient without atomics.  Split (nsplit = 2, part
+  // non-null): two workgroups per key block take half of the group's heads each and write fp32
+  // partial sums, which bwd_dkdv_sum_kernel adds.
   const int bkv = blockIdx.x % BHkv, b = bkv / Hkv, hk = bkv - b * Hkv;
-  const int g = Hq / Hkv, h0 = hk * g;  // the group's first query head
+  const int kbs = blockIdx.x / BHkv, kblk = kbs / nsplit, half_ = kbs - kblk * nsplit;
+  const int g = Hq / Hkv / nsplit, h0 = hk * (Hq / Hkv) + half_ * g;  // this workgroup's first query head
   const SeqRows sr = seq_rows(geo, b, h0, Hq, hk, Hkv);
   const int Nq = sr.lq, Nk = sr.lk, doff = Nk - Nq;  // query i sees keys j <= i + doff (causal)
   // Causal: early key blocks see the most queries and are dispatched first.
-  const int k0 = (blockIdx.x / BHkv) * BK;
+  const int k0 = kblk * BK;
   if (k0 >= Nk) return;  // key block past the end of a shorter sequence
   const int kw0 = k0 + grp * 32;
   // Query head h0 + i of the group: rows + i * geo.nq (the head stride of both layouts).
@@ -172,13 +175,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return __builtin_amdgcn_readfirstlane((int)tlist[min(i, nvt - 1)]);
   };
   uint16_t* outp = (role == 0 ? dv : dk) + sr.k * D;
+  // Split: fp32 partial of (role, half) at the key's row of [B*Hkv*Nk, D].
+  float* partp = part ? part + ((size_t)(role * nsplit + half_) * BHkv * geo.nk + sr.k) * D : nullptr;
   if (nvt <= 0) {  // no query sees these keys: dK = dV = 0
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kr = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        if (kr < Nk) outp[(size_t)kr * D + db * 32 + l32] = 0;
+        if (kr < Nk) {
+          if (partp) partp[(size_t)kr * D + db * 32 + l32] = 0.f;
+          else outp[(size_t)kr * D + db * 32 + l32] = 0;
+        }
       }
     return;
   }
@@ -553,8 +561,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      if (kr < Nk) outp[(size_t)kr * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(acc[db][r] * oscale, 0.f) & 0xffffu);
+      if (kr < Nk) {
+        if (partp) partp[(size_t)kr * D + db * 32 + l32] = acc[db][r] * oscale;
+        else outp[(size_t)kr * D + db * 32 + l32] = (uint16_t)(pack_bf16x2(acc[db][r] * oscale, 0.f) & 0xffffu);
+      }
     }
+}
+
+// Split dK/dV: out = bf16(partial of the first half + partial of the second half), four
+// elements per thread; n4 = B*Hkv*N*d/4 per tensor, grid over both tensors (dV, then dK).
+__global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(const float* __restrict__ part, uint16_t* __restrict__ dv,
+                                                           uint16_t* __restrict__ dk, long long n4) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const int role = i >= n4;
+  const long long j = i - role * n4;
+  const f32x4 a = reinterpret_cast<const f32x4*>(part + (size_t)(2 * role) * n4 * 4)[j];
+  const f32x4 c = reinterpret_cast<const f32x4*>(part + (size_t)(2 * role + 1) * n4 * 4)[j];
+  u32x2 w;
+  w[0] = pack_bf16x2(a[0] + c[0], a[1] + c[1]);
+  w[1] = pack_bf16x2(a[2] + c[2], a[3] + c[3]);
+  reinterpret_cast<u32x2*>(role ? dk : dv)[j] = w;
 }
 
 // ------------------------------------------------------------------ dQ
@@ -886,11 +913,24 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   const int n_kt = (a.max_k + 127) / 128;
-  if (n_kt > 0)
-    hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL, SPARSE>), dim3(n_kt * BHkv), dim3(512), 0, a.stream,
+  if (n_kt > 0) {
+    // The caller hands over the partial buffer only where the split applies (dense causal
+    // grouped-query heads, even group size, fewer than kBwdSplitGrid workgroups).
+    const bool split = CAUSAL && a.part != nullptr && a.cu_q == nullptr && bwd_split_possible(a.B, a.Hq, a.Hkv, a.Nk) &&
+                       a.Nq == a.Nk;
+    const int nsplit = split ? 2 : 1;
+    hipLaunchKernelGGL((bwd_dkdv_lag_kernel<D, CAUSAL, SPARSE>), dim3(n_kt * nsplit * BHkv), dim3(512), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const float*)a.stats,
                        (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, geo, bm, a.stat_stride,
-                       a.stat_half, a.scale, sl2, BHkv, a.Hq, a.Hkv);
+                       a.stat_half, a.scale, sl2, BHkv, a.Hq, a.Hkv, split ? a.part : nullptr, nsplit);
+    if (split) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const long long n4 = (long long)BHkv * a.Nk * D / 4;
+      hipLaunchKernelGGL(bwd_dkdv_sum_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, a.stream,
+                         (const float*)a.part, (uint16_t*)a.dv, (uint16_t*)a.dk, n4);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -38,7 +38,20 @@ struct BwdArgs {
   hipStream_t stream;
   const unsigned char* block_mask;  // optional [B, Hq, ceil(N/128), ceil(N/128)] keep bytes (dense layout only)
   long long mask_sb, mask_sh;       // batch and head strides of block_mask in bytes
+  float* part;                      // fp32 [2 (dV, dK)][2 halves][B*Hkv*N][d] for the split dK/dV, or null
 };
+
+// Causal grouped-query backward with few key blocks: when the dK/dV grid has fewer workgroups
+// than this, the query heads of each group are split over two workgroups per key block (their
+// causal work differs by up to the number of key blocks, and one round of workgroups would run
+// as long as the heaviest); each writes fp32 partial sums that a second pass adds in a fixed
+// order.  Dense layout (with or without a block mask), even group size.
+constexpr int kBwdSplitGrid = 512;
+inline bool bwd_split_possible(int B, int Hq, int Hkv, int N) {
+  if (B <= 0 || Hkv <= 0 || N <= 0 || Hq % Hkv != 0) return false;
+  const int g = Hq / Hkv;
+  return g >= 2 && g % 2 == 0 && (long long)B * Hkv * ((N + 127) / 128) < kBwdSplitGrid;
+}
 
 struct DecodeArgs {
   const void* q; const void* k; const void* v; void* o; float* lse;

@@ -136,7 +136,11 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void*
 
 /* Bytes of device workspace attn_bwd needs: fp32 per-row statistics (LSE * log2(e) and
  * D = rowsum(dO * O)) for every query row padded to a multiple of 64, i.e.
- * 2 * B * Hq * roundup(N, 64) * 4 bytes, rounded up to 256. */
+ * 2 * B * Hq * roundup(N, 64) * 4 bytes, rounded up to 256; plus, when Hq/Hkv is even and
+ * above 1 and B * Hkv * ceil(N/128) < 512, 4 * B * Hkv * N * d * 4 bytes (rounded up to 256)
+ * of fp32 partial dK/dV: a causal backward of such a shape splits each group's query heads
+ * over two dK/dV workgroups (the causal work of the key blocks differs too much for one round
+ * of workgroups) and adds their two partial sums in a fixed order. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /*

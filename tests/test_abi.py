@@ -110,6 +110,17 @@ def bwd(ws=P, ws_bytes=1 << 30, Hq=2, Hkv=2, d=128, dt=1, scale=0.1, dq=P):
                         ws, ws_bytes, None)
 
 
+def test_bwd_workspace_split():
+    """Causal grouped-query backward with few key blocks splits each group's query heads over two
+    dK/dV workgroups; their fp32 partial sums follow the statistics in the workspace."""
+    stats = 2 * 1 * 32 * 4096 * 4
+    part = 4 * 1 * 8 * 4096 * 128 * 4            # [dV, dK] x [two halves] x B*Hkv*N x d, fp32
+    assert lib.attn_bwd_workspace_bytes(1, 32, 8, 4096, 128) == stats + part
+    assert lib.attn_bwd_workspace_bytes(1, 32, 32, 4096, 128) == stats             # no groups
+    assert lib.attn_bwd_workspace_bytes(1, 6, 2, 4096, 128) == 2 * 6 * 4096 * 4    # odd group size
+    assert lib.attn_bwd_workspace_bytes(4, 32, 8, 4096, 128) == 2 * 4 * 32 * 4096 * 4  # 1024 key blocks
+
+
 def test_bwd_validation():
     need = lib.attn_bwd_workspace_bytes(1, 2, 2, 64, 128)
     assert need == 1024                      # LSE2 and D rows, padded to 64 queries

@@ -319,6 +319,21 @@ def test_bwd_grouped_query(gpu_lib, heads, d, causal):
     check_bwd(grads, inp, scale, causal, tag=f"gqa {Hq}/{Hkv} d={d}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 8, 4, 1000, 128), (1, 16, 2, 777, 64), (2, 8, 1, 640, 128),
+                                         (1, 6, 2, 500, 128)])
+def test_bwd_grouped_query_split(gpu_lib, B, Hq, Hkv, N, d):
+    """Causal grouped-query backward on few key blocks: the group's query heads are split over
+    two dK/dV workgroups whose fp32 partial sums are added in a fixed order (group sizes 2, 8 and
+    4; the odd group of 3 takes the unsplit path).  Matches the oracle and repeats bit for bit."""
+    inp = make_prefill(B, Hq, Hkv, N, d, "bf16", seed=900 + Hq + Hkv + N, with_dout=True)
+    scale = default_scale(d)
+    grads = run_fwd_bwd(gpu_lib, inp, True, scale)
+    check_bwd(grads, inp, scale, True, tag=f"split {Hq}/{Hkv} N={N} d={d}")
+    again = run_fwd_bwd(gpu_lib, inp, True, scale)
+    for a, b in zip(grads, again):
+        assert np.array_equal(a, b)
+
+
 def test_bwd_from_oracle_forward(gpu_lib):
     """Feed the oracle's O (as bf16) and LSE into attn_bwd: isolates the backward kernels."""
     import torch
