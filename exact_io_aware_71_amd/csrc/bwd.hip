@@ -40,10 +40,7 @@
 #ifndef XATTN_DKDV_SPREAD
 #define XATTN_DKDV_SPREAD 1
 #endif
-// dQ: slot-interleaved tile body (0: block by block) and its LDS operand lookahead.
-#ifndef XATTN_DQ_ILV
-#define XATTN_DQ_ILV 1
-#endif
+// dQ: LDS operand lookahead of the slot-interleaved tile body.
 #ifndef XATTN_DQ_LOOKAHEAD
 #define XATTN_DQ_LOOKAHEAD 4
 #endif
@@ -728,7 +725,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wait_vmem();  // also covers the Q/dO loads
   lds_barrier();
   // Tile t+1 is copied during tile t (past the end: rows clamped, into the idle stage).
-#if XATTN_DQ_ILV
   // Interleaved tile: the MFMAs of one 64-key tile run in fixed slots and the vector work of
   // each key block sits between the MFMAs that do not depend on it.  Slot phases (one MFMA
   // per slot, DC = D/16 slots for a score block, 2*DB for a dQ block):
@@ -834,56 +830,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vmem();  // tile t+1 has landed
     lds_barrier();
   }
-#else
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = kt(t) * BN, kn = kt(t + 1);
-    const char* ks = smem + (t & 1) * STAGE;
-    const char* vs = ks + T::BYTES;
-    if (CAUSAL && t0 > qd0 + 31) {
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) copy_piece(t + 1, kn, i);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const int off = swz<D>(kb * 32 + l32, 2 * c + h32);
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(ks + off);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + off);
-          s = mfma32(ak, qreg[c], s);
-          dp = mfma32(av, doreg[c], dp);
-          if (kb == 0 && c < CPW) copy_piece(t + 1, kn, c);
-        }
-        // Lane owns query qi; register r holds key t0 + kb*32 + 8(r/4) + 4*h32 + r%4.
-        const int kb0 = t0 + kb * 32;
-        const bool need_mask = (kb0 + 32 > Nk) || (CAUSAL && kb0 + 31 > qd0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
-          if (need_mask) {
-            const int kj = kb0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            if (kj >= Nk || (CAUSAL && kj > kmax)) p = 0.f;
-          }
-          dp[r] = p * (dp[r] - dl);
-        }
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const bf16x8 dsa = pack8(dp, sh);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 bk = ld_tr_operand<D>(ks, kb * 32 + 16 * sh, db * 32, lane);
-            dq_acc[db] = mfma32(dsa, bk, dq_acc[db]);
-          }
-        }
-      }
-    }
-    wait_vmem();  // tile t+1 has landed
-    lds_barrier();
-  }
-#endif
   // C layout: lane holds feature db*32 + l32 of queries qw0 + 8(r/4) + 4*h32 + r%4.
 #pragma unroll
   for (int db = 0; db < DB; ++db)
