@@ -44,13 +44,16 @@
 #ifndef XATTN_FWD128_WPE
 #define XATTN_FWD128_WPE 2
 #endif
-// d = 64 through the interleaved kernel (256-row tiles): measured 5-15% faster at N = 4096 but
-// 13% slower on 4 x 16 heads of N = 1024 (half as many workgroups), so off by default.
+// d = 64 through the interleaved kernel with four waves (128-row tiles, 64 KB of LDS, two
+// workgroups per CU): 4-7% faster than fwd_bf16_kernel at N = 1024 and 4096, causal or not
+// (10-12% before its matrix-core row sum, which the error bound needs; see kMfmaSum).
+// With eight waves (256-row tiles) it lost 13% on 4 x 16 heads of N = 1024 (half as many
+// workgroups).
 #ifndef XATTN_FWD64_ILV
-#define XATTN_FWD64_ILV 0
+#define XATTN_FWD64_ILV 1
 #endif
 #ifndef XATTN_FWD64_ILV_NW
-#define XATTN_FWD64_ILV_NW 8
+#define XATTN_FWD64_ILV_NW 4
 #endif
 #ifndef XATTN_FWD64_NQ
 #define XATTN_FWD64_NQ 1
@@ -475,6 +478,21 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][db][r] = 0.f;
+  // d = 64: O is divided by the sum of the same bf16 probabilities its P V product used, formed
+  // on the matrix cores against an operand of ones (every row of lsum holds it, for the lane's
+  // query), so that a row dominated by one key gets that key's V row exactly; the fp32 sum
+  // l_run still gives the LSE.  Dividing by the fp32 sum instead leaves the bf16 rounding of the
+  // dominant probability (up to 2^-9 relative) in O.  d = 128 keeps the fp32 sum: its matrix
+  // cores have no slack for the two extra products per step.  At d = 64 they cost 5-7% against
+  // dividing by the fp32 sum (which misses the error bound by one bf16 step on a peaky row);
+  // the same sum by eight v_dot2_f32_bf16 per step measured within 2% of them.
+  constexpr bool kMfmaSum = D == 64;
+  f32x16 lsum[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lsum[rb][r] = 0.f;
+  const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   float m_run[RB], l_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) { m_run[rb] = kMaxInit; l_run[rb] = 0.f; }
@@ -486,7 +504,9 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float lt = sum_xor32(l_run[rb]);
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      // A row with keys has lsum >= 1: its largest probability is at least 1 against the
+      // reference max, which never exceeds the row's running max.
+      const float inv = lt > 0.f ? 1.f / (kMfmaSum ? lsum[rb][0] : lt) : 0.f;
       const int qi = qw0 + 32 * rb + l32;
       if (qi < Nq) {
 #pragma unroll
@@ -689,6 +709,7 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
         if constexpr (j < NPV) {
           constexpr int db = j % DB, sh = j / DB;
           acc[rb][db] = mfma32(buf[j % L], as_bf16x8(pp[rb][sh]), acc[rb][db]);
+          if constexpr (kMfmaSum && db == 0) lsum[rb] = mfma32(ones, as_bf16x8(pp[rb][sh]), lsum[rb]);
         } else {
           constexpr int c = j - NPV;
           if constexpr (RB == 1) {
@@ -801,6 +822,12 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
           for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
+        if constexpr (kMfmaSum) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lsum[rb][r] *= alpha[rb];
+        }
         sched_fence();
       }
 #else
@@ -812,6 +839,12 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
           for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
+        if constexpr (kMfmaSum) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lsum[rb][r] *= alpha[rb];
+        }
         sched_fence();
       }
 #endif
@@ -863,7 +896,10 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       constexpr int j = decltype(jc)::value, db = j % DB, sh = j / DB;
       const bf16x8 a = operand(vs, vs, jc);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc[rb][db] = mfma32(a, as_bf16x8(pA[rb][sh]), acc[rb][db]);
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb][db] = mfma32(a, as_bf16x8(pA[rb][sh]), acc[rb][db]);
+        if constexpr (kMfmaSum && db == 0) lsum[rb] = mfma32(ones, as_bf16x8(pA[rb][sh]), lsum[rb]);
+      }
     });
   }
 
