@@ -478,15 +478,24 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][db][r] = 0.f;
-  // d = 64: O is divided by the sum of the same bf16 probabilities its P V product used, formed
-  // on the matrix cores against an operand of ones (every row of lsum holds it, for the lane's
-  // query), so that a row dominated by one key gets that key's V row exactly; the fp32 sum
-  // l_run still gives the LSE.  Dividing by the fp32 sum instead leaves the bf16 rounding of the
-  // dominant probability (up to 2^-9 relative) in O.  d = 128 keeps the fp32 sum: its matrix
-  // cores have no slack for the two extra products per step.  At d = 64 they cost 5-7% against
-  // dividing by the fp32 sum (which misses the error bound by one bf16 step on a peaky row);
-  // the same sum by eight v_dot2_f32_bf16 per step measured within 2% of them.
+  // O is divided by the sum of the same bf16 probabilities its P V product used, so that a row
+  // dominated by one key gets that key's V row exactly; the fp32 sum l_run still gives the LSE.
+  // Dividing by the fp32 sum instead leaves the bf16 rounding of the dominant probability (up
+  // to 2^-9 relative: under the lazy reference max it lies in (1, 2^8], not at 1) in O, which
+  // with the final rounding of O can exceed the 2e-2 error bound on peaky rows.
+  //   d = 64 forms the sum on the matrix cores, two products per step against an operand of
+  //   ones (every row of lsum holds it, for the lane's query): its vector ALU is the busier
+  //   pipe.  d = 128 forms it on the vector ALU, v_dot2_f32_bf16 of each packed pair against
+  //   (1, 1), eight per step (lane-partial, added across the lane pair at the end like l_run):
+  //   its matrix cores are the busier pipe.  (Measured: at d = 128 the two forms cost the same,
+  //   3-5% against the fp32 division; at d = 64 the matrix-core form is the cheaper.)
   constexpr bool kMfmaSum = D == 64;
+  constexpr bool kDotSum = D == 128;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  float lb[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) lb[rb] = 0.f;
   f32x16 lsum[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -506,7 +515,7 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       const float lt = sum_xor32(l_run[rb]);
       // A row with keys has lsum >= 1: its largest probability is at least 1 against the
       // reference max, which never exceeds the row's running max.
-      const float inv = lt > 0.f ? 1.f / (kMfmaSum ? lsum[rb][0] : lt) : 0.f;
+      const float inv = lt > 0.f ? 1.f / (kMfmaSum ? lsum[rb][0] : kDotSum ? sum_xor32(lb[rb]) : lt) : 0.f;
       const int qi = qw0 + 32 * rb + l32;
       if (qi < Nq) {
 #pragma unroll
@@ -699,6 +708,9 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       float rs[RB][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) { rs[rb][0] = 0.f; rs[rb][1] = 0.f; alpha[rb] = 1.f; }
+      float rsb[RB];  // kDotSum: this step's lane-partial sum of the bf16 probabilities
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) rsb[rb] = 0.f;
       bool resc = false;
       bf16x8 buf[L];
       static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(ks, vs, jc); });
@@ -765,6 +777,11 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
             // fp32 row sums (summing the bf16-rounded values would cost the LSE up to 2^-9).
             rs[erb][0] += p[0] + p[2];
             rs[erb][1] += p[1] + p[3];
+            if constexpr (kDotSum) {
+              rsb[erb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones2, rsb[erb], false);
+              rsb[erb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones2, rsb[erb], false);
+              asm volatile("" : "+v"(rsb[erb]));
+            }
             // Keeps this step's vector work in its slot (the compiler would otherwise sink it).
             asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs[erb][0]), "+v"(rs[erb][1]));
             pc[erb][jq / 2][2 * (jq % 2)] = w0;
@@ -802,8 +819,10 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
           alpha[rb] = fast_exp2(m_run[rb] - m_new);
           m_run[rb] = m_new;
           l_run[rb] *= alpha[rb];
+          lb[rb] *= alpha[rb];
           rs[rb][0] = 0.f;
           rs[rb][1] = 0.f;
+          rsb[rb] = 0.f;
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq) {
             float pv[4];
@@ -812,6 +831,10 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
             const uint32_t w0 = pack_bf16x2(pv[0], pv[1]), w1 = pack_bf16x2(pv[2], pv[3]);
             rs[rb][0] += pv[0] + pv[2];
             rs[rb][1] += pv[1] + pv[3];
+            if constexpr (kDotSum) {
+              rsb[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones2, rsb[rb], false);
+              rsb[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones2, rsb[rb], false);
+            }
             pc[rb][jq / 2][2 * (jq % 2)] = w0;
             pc[rb][jq / 2][2 * (jq % 2) + 1] = w1;
           }
@@ -850,7 +873,10 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
 #endif
       // One branch only: a second one on the same condition costs the allocator ~40 registers.
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
+      for (int rb = 0; rb < RB; ++rb) {
+        l_run[rb] += rs[rb][0] + rs[rb][1];
+        if constexpr (kDotSum) lb[rb] += rsb[rb];
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < CPS; ++i) step_copy(t, phc, i);

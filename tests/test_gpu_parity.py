@@ -65,16 +65,29 @@ def test_fwd_long_prefill_sampled_rows(gpu_lib, name, causal):
     assert_fwd_ok(fwd_errors(o[:, :, rows], o_ref, lse[:, :, rows], lse_ref), name)
 
 
-def test_fwd_long4k_full_heads(gpu_lib):
+def test_fwd_long4k_every_element(gpu_lib):
+    """Long prefill at N = 4096 (logits x2): every element of O and every LSE row of all 32
+    heads, causal and not.  A kernel that divided O by the fp32 row sum while P V used the
+    bf16 probabilities had one element of the causal case at 0.025 here."""
     w = WORKLOADS["long4k"]
     inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed, qk_mult=w.qk_mult)
     scale = default_scale(w.d)
     for causal in (True, False):
         o, lse = run_fwd(gpu_lib, inp, causal, scale)
-        for h in (0, 31):
+        for h in range(w.Hq):
             sl = {kk: inp[kk][:, h:h + 1] for kk in ("q", "k", "v")}
             o_ref, lse_ref = oracle.forward(sl["q"], sl["k"], sl["v"], scale, causal)
             assert_fwd_ok(fwd_errors(o[:, h:h + 1], o_ref, lse[:, h:h + 1], lse_ref), f"h{h} causal={causal}")
+
+
+def test_fwd_peaky_grouped_rows(gpu_lib):
+    """d = 128, grouped heads, logits x2, N = 511, non-causal: a shape on which dividing O by
+    the fp32 row sum put one element at 0.0225 (found by a randomised sweep)."""
+    inp = make_prefill(1, 16, 2, 511, 128, "bf16", seed=7076, qk_mult=2.0)
+    scale = default_scale(128)
+    o, lse = run_fwd(gpu_lib, inp, False, scale)
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], scale, False)
+    assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), "peaky grouped")
 
 
 @pytest.mark.parametrize("causal", [True, False])
