@@ -755,6 +755,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return join_tr(ds_read_tr16(smem + ofs.v[db][0] + roff), ds_read_tr16(smem + ofs.v[db][1] + roff));
     }
   };
+  if (!SPARSE && ntiles == 1) {
+    // The tile's keys are all the keys of these rows: D = sum_j P_ij dP_ij, its definition,
+    // replaces rowsum(dO * O) here and in the statistics the dK/dV kernel reads.  O is stored in
+    // bf16 and D inherits its rounding; on rows dominated by one key dP - D nearly cancels, and
+    // on such short rows that rounding alone moved dQ and dK by up to a few percent.
+    const int t0 = kt(0) * BN;
+    f32x16 sv[2], dpv[2];
+    static_for<2>([&](auto kc) {
+      constexpr int kb = decltype(kc)::value;
+      static_for<DC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const bf16x8 ak = opnd(std::integral_constant<int, (2 * kb) * DC + c>{});
+        const bf16x8 av = opnd(std::integral_constant<int, (2 * kb + 1) * DC + c>{});
+        if constexpr (c == 0) {
+          sv[kb] = mfma32(ak, qreg[0], f32x16{});
+          dpv[kb] = mfma32(av, doreg[0], f32x16{});
+        } else {
+          sv[kb] = mfma32(ak, qreg[c], sv[kb]);
+          dpv[kb] = mfma32(av, doreg[c], dpv[kb]);
+        }
+      });
+    });
+    float dpart = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        float pr = fast_exp2(fmaf(sv[kb][r], scale_log2, -lse2));
+        if (kj >= Nk || (CAUSAL && kj > kmax)) pr = 0.f;
+        sv[kb][r] = pr;
+        dpart += pr * dpv[kb][r];
+      }
+    const float dex = sum_xor32(dpart);
+    if (h32 == 0 && qi < Nq) stats[stat_row(geo, stat_stride, b, hq, Hq) + stat_half + qi] = dex;
+    bf16x8 dsv[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpv[kb][r] = sv[kb][r] * (dpv[kb][r] - dex);
+      dsv[kb][0] = pack8(dpv[kb], 0);
+      dsv[kb][1] = pack8(dpv[kb], 1);
+    }
+    static_for<4 * DB>([&](auto jc) {
+      constexpr int jj = decltype(jc)::value, kb = jj / (2 * DB), sh = (jj % (2 * DB)) / DB, db = jj % DB;
+      dq_acc[db] = mfma32(dsv[kb][sh], opnd(std::integral_constant<int, PE + jj>{}), dq_acc[db]);
+    });
+  } else
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = kt(t) * BN, kn = kt(t + 1);
     if (CAUSAL && t0 > qd0 + 31) {

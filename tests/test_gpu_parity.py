@@ -347,6 +347,18 @@ def test_bwd_grouped_query_split(gpu_lib, B, Hq, Hkv, N, d):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,seed", [(2, 4, 2, 2, 128, True, 7129), (1, 3, 1, 2, 64, True, 7132),
+                                                    (1, 2, 2, 2, 128, False, 7007), (2, 2, 2, 33, 64, True, 7200)])
+def test_bwd_short_peaky_rows(gpu_lib, B, Hq, Hkv, N, d, causal, seed):
+    """Rows whose keys fit one 64-key tile, logits x2 (rows dominated by one key): D is formed
+    as sum_j P_ij dP_ij rather than from the stored bf16 O, whose rounding alone moved dQ and
+    dK past the bound on these shapes."""
+    inp = make_prefill(B, Hq, Hkv, N, d, "bf16", seed=seed, with_dout=True, qk_mult=2.0)
+    scale = default_scale(d)
+    grads = run_fwd_bwd(gpu_lib, inp, causal, scale)
+    check_bwd(grads, inp, scale, causal, tag=f"short peaky N={N} d={d}")
+
+
 def test_bwd_from_oracle_forward(gpu_lib):
     """Feed the oracle's O (as bf16) and LSE into attn_bwd: isolates the backward kernels."""
     import torch

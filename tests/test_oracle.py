@@ -723,11 +723,12 @@ def test_backward_blocksparse_pins():
 
 
 def test_bwd_bound_needs_more_than_bf16_o_on_tiny_peaky_rows():
-    """The backward takes O as the forward stored it (bf16) and forms D = rowsum(dO * O) from
-    it.  On a tiny causal case with doubled logits (N = 2: the second row is dominated by one
-    key, so dP - D nearly cancels) that rounding alone moves dQ and dK by about 2% in relative
-    L2, beyond the 1e-2 bound, while the same fp64 backward with the exact O reproduces the
-    oracle: the bound is out of reach there for any backward that consumes the stored O."""
+    """A backward that forms D = rowsum(dO * O) from O as the forward stored it (bf16): on a
+    tiny causal case with doubled logits (N = 2: the second row is dominated by one key, so
+    dP - D nearly cancels) that rounding alone moves dQ and dK by about 2% in relative L2,
+    beyond the 1e-2 bound, while the same fp64 backward with the exact O reproduces the oracle.
+    Hence the dQ kernel forms D from its definition, sum_j P_ij dP_ij, wherever a query tile's
+    keys fit one key tile."""
     B, Hq, Hkv, N, d = 2, 4, 2, 2, 128
     inp = make_prefill(B, Hq, Hkv, N, d, "bf16", seed=7129, with_dout=True, qk_mult=2.0)
     scale = default_scale(d)
