@@ -482,26 +482,26 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   // dominated by one key gets that key's V row exactly; the fp32 sum l_run still gives the LSE.
   // Dividing by the fp32 sum instead leaves the bf16 rounding of the dominant probability (up
   // to 2^-9 relative: under the lazy reference max it lies in (1, 2^8], not at 1) in O, which
-  // with the final rounding of O can exceed the 2e-2 error bound on peaky rows.
-  //   d = 64 forms the sum on the matrix cores, two products per step against an operand of
-  //   ones (every row of lsum holds it, for the lane's query): its vector ALU is the busier
-  //   pipe.  d = 128 forms it on the vector ALU, v_dot2_f32_bf16 of each packed pair against
-  //   (1, 1), eight per step (lane-partial, added across the lane pair at the end like l_run):
-  //   its matrix cores are the busier pipe.  (Measured: at d = 128 the two forms cost the same,
-  //   3-5% against the fp32 division; at d = 64 the matrix-core form is the cheaper.)
-  constexpr bool kMfmaSum = D == 64;
-  constexpr bool kDotSum = D == 128;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  float lb[RB];
+  // with the final rounding of O can exceed the 2e-2 error bound on peaky rows.  The sum comes
+  // from the matrix cores at half the cost of one 32x32x16 product per 32 keys: one
+  // v_mfma_f32_16x16x32_bf16 per 16 keys reads the P^T operand as its B (32 k x 16 n; column n,
+  // k-groups 0..3 = query n keys 0-7, query n+16 keys 0-7, query n keys 8-15, query n+16 keys
+  // 8-15) against a 0/1 selector A (row 0 picks groups 0 and 2, row 1 groups 1 and 3), so that
+  // C row 0 accumulates the sum of query n and row 1 that of query n+16, in lanes 0-15.
+  // (Measured against eight v_dot2_f32_bf16 per step, and two 32x32x16 products against ones:
+  // 2.5-5% faster at d = 128, 3-13% at d = 64.)
+  f32x4 lsum[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) lb[rb] = 0.f;
-  f32x16 lsum[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lsum[rb][r] = 0.f;
-  const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  for (int rb = 0; rb < RB; ++rb) lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool sel_on = ((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1);
+  const bf16x8 sel16 = sel_on ? as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u})
+                              : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  // Rescale of lsum by the per-row factor a: row 1 of lanes 0-15 belongs to query lane + 16.
+  auto lsum_scale = [&](int rb, float a) __attribute__((always_inline)) {
+    const float a_hi = __shfl(a, (lane & 15) + 16);
+    lsum[rb][0] *= a;
+    lsum[rb][1] *= a_hi;
+  };
   float m_run[RB], l_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) { m_run[rb] = kMaxInit; l_run[rb] = 0.f; }
@@ -513,9 +513,10 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float lt = sum_xor32(l_run[rb]);
-      // A row with keys has lsum >= 1: its largest probability is at least 1 against the
+      // A row with keys has a bf16 sum >= 1: its largest probability is at least 1 against the
       // reference max, which never exceeds the row's running max.
-      const float inv = lt > 0.f ? 1.f / (kMfmaSum ? lsum[rb][0] : kDotSum ? sum_xor32(lb[rb]) : lt) : 0.f;
+      const float r0 = __shfl(lsum[rb][0], l32 & 15), r1 = __shfl(lsum[rb][1], l32 & 15);
+      const float inv = lt > 0.f ? 1.f / (l32 < 16 ? r0 : r1) : 0.f;
       const int qi = qw0 + 32 * rb + l32;
       if (qi < Nq) {
 #pragma unroll
@@ -708,9 +709,6 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       float rs[RB][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) { rs[rb][0] = 0.f; rs[rb][1] = 0.f; alpha[rb] = 1.f; }
-      float rsb[RB];  // kDotSum: this step's lane-partial sum of the bf16 probabilities
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) rsb[rb] = 0.f;
       bool resc = false;
       bf16x8 buf[L];
       static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(ks, vs, jc); });
@@ -721,7 +719,7 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
         if constexpr (j < NPV) {
           constexpr int db = j % DB, sh = j / DB;
           acc[rb][db] = mfma32(buf[j % L], as_bf16x8(pp[rb][sh]), acc[rb][db]);
-          if constexpr (kMfmaSum && db == 0) lsum[rb] = mfma32(ones, as_bf16x8(pp[rb][sh]), lsum[rb]);
+          if constexpr (db == 0) lsum[rb] = mfma16(sel16, as_bf16x8(pp[rb][sh]), lsum[rb]);
         } else {
           constexpr int c = j - NPV;
           if constexpr (RB == 1) {
@@ -777,11 +775,6 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
             // fp32 row sums (summing the bf16-rounded values would cost the LSE up to 2^-9).
             rs[erb][0] += p[0] + p[2];
             rs[erb][1] += p[1] + p[3];
-            if constexpr (kDotSum) {
-              rsb[erb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones2, rsb[erb], false);
-              rsb[erb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones2, rsb[erb], false);
-              asm volatile("" : "+v"(rsb[erb]));
-            }
             // Keeps this step's vector work in its slot (the compiler would otherwise sink it).
             asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs[erb][0]), "+v"(rs[erb][1]));
             pc[erb][jq / 2][2 * (jq % 2)] = w0;
@@ -819,10 +812,8 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
           alpha[rb] = fast_exp2(m_run[rb] - m_new);
           m_run[rb] = m_new;
           l_run[rb] *= alpha[rb];
-          lb[rb] *= alpha[rb];
           rs[rb][0] = 0.f;
           rs[rb][1] = 0.f;
-          rsb[rb] = 0.f;
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq) {
             float pv[4];
@@ -831,10 +822,6 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
             const uint32_t w0 = pack_bf16x2(pv[0], pv[1]), w1 = pack_bf16x2(pv[2], pv[3]);
             rs[rb][0] += pv[0] + pv[2];
             rs[rb][1] += pv[1] + pv[3];
-            if constexpr (kDotSum) {
-              rsb[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones2, rsb[rb], false);
-              rsb[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones2, rsb[rb], false);
-            }
             pc[rb][jq / 2][2 * (jq % 2)] = w0;
             pc[rb][jq / 2][2 * (jq % 2) + 1] = w1;
           }
@@ -845,12 +832,8 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
           for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
-        if constexpr (kMfmaSum) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) lsum[rb][r] *= alpha[rb];
-        }
+        for (int rb = 0; rb < RB; ++rb) lsum_scale(rb, alpha[rb]);
         sched_fence();
       }
 #else
@@ -862,21 +845,14 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
           for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
-        if constexpr (kMfmaSum) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) lsum[rb][r] *= alpha[rb];
-        }
+        for (int rb = 0; rb < RB; ++rb) lsum_scale(rb, alpha[rb]);
         sched_fence();
       }
 #endif
       // One branch only: a second one on the same condition costs the allocator ~40 registers.
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        l_run[rb] += rs[rb][0] + rs[rb][1];
-        if constexpr (kDotSum) lb[rb] += rsb[rb];
-      }
+      for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
     } else {
 #pragma unroll
       for (int i = 0; i < CPS; ++i) step_copy(t, phc, i);
@@ -924,7 +900,7 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         acc[rb][db] = mfma32(a, as_bf16x8(pA[rb][sh]), acc[rb][db]);
-        if constexpr (kMfmaSum && db == 0) lsum[rb] = mfma32(ones, as_bf16x8(pA[rb][sh]), lsum[rb]);
+        if constexpr (db == 0) lsum[rb] = mfma16(sel16, as_bf16x8(pA[rb][sh]), lsum[rb]);
       }
     });
   }
