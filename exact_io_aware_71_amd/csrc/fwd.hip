@@ -22,9 +22,14 @@
 //     trip for P.
 //   * V^T, the A operand of that product, is read from the row-major V tile with the
 //     transposing ds_read_b64_tr_b16, so the tile is stored exactly as it arrives.
-//   * K/V tiles are double buffered: the global loads for tile t+1 are issued before the
-//     MFMA work on tile t and written to the other LDS stage afterwards (one barrier per
-//     tile), hiding HBM/L2 latency behind compute ([OPT] §5.2).
+//   * K/V tiles arrive ahead of use, so HBM/L2 latency hides behind compute ([OPT] §5.2):
+//     fwd_ilv_kernel (bf16, the default for d = 64 and 128) copies them straight into LDS
+//     rings of four stages (buffer_load ... lds, no registers), K three tiles and V two tiles
+//     ahead, one barrier per tile; fwd_bf16_kernel (behind a switch) stages the next tile
+//     through registers into a second LDS buffer; fwd_f32_kernel (fp32 inputs) is
+//     single-buffered.
+//   * fwd_ilv_kernel software-pipelines each wave: the MFMAs of P_{u-1} V_{u-1} and of S_{u+1}
+//     interleave with the vector work of the softmax of S_u in fixed slots.
 //   * Causal: tiles past the diagonal are never loaded, waves whose rows all precede a tile
 //     skip its MFMA work, and only diagonal tiles evaluate the mask.  Heavy (late) query
 //     tiles are dispatched first; all query tiles of one head land on one XCD when the
