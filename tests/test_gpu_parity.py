@@ -80,6 +80,20 @@ def test_fwd_long4k_every_element(gpu_lib):
             assert_fwd_ok(fwd_errors(o[:, h:h + 1], o_ref, lse[:, h:h + 1], lse_ref), f"h{h} causal={causal}")
 
 
+def test_fwd_long8k_every_element(gpu_lib):
+    """Long prefill at N = 8192 (logits x2): every element of O and every LSE row of all 32
+    heads, causal and not (about 20 s of oracle time)."""
+    w = WORKLOADS["long8k"]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed, qk_mult=w.qk_mult)
+    scale = default_scale(w.d)
+    for causal in (True, False):
+        o, lse = run_fwd(gpu_lib, inp, causal, scale)
+        for h in range(w.Hq):
+            sl = {kk: inp[kk][:, h:h + 1] for kk in ("q", "k", "v")}
+            o_ref, lse_ref = oracle.forward(sl["q"], sl["k"], sl["v"], scale, causal)
+            assert_fwd_ok(fwd_errors(o[:, h:h + 1], o_ref, lse[:, h:h + 1], lse_ref), f"h{h} causal={causal}")
+
+
 def test_fwd_peaky_grouped_rows(gpu_lib):
     """d = 128, grouped heads, logits x2, N = 511, non-causal: a shape on which dividing O by
     the fp32 row sum put one element at 0.0225 (found by a randomised sweep)."""
