@@ -35,21 +35,11 @@
 #include "common.h"
 #include "launch.h"
 
-#ifndef XATTN_DKDV_ILV
-#define XATTN_DKDV_ILV 1
-#endif
-#ifndef XATTN_DKDV_LOOKAHEAD
-#define XATTN_DKDV_LOOKAHEAD 4
-#endif
-#ifndef XATTN_DKDV_SPREAD
-#define XATTN_DKDV_SPREAD 1
-#endif
-// dQ: LDS operand lookahead of the slot-interleaved tile body.
-#ifndef XATTN_DQ_LOOKAHEAD
-#define XATTN_DQ_LOOKAHEAD 4
-#endif
-
 namespace xattn {
+
+// MFMA operands read from LDS run this many MFMA slots ahead of their use (dK/dV and dQ).
+constexpr int kDkdvLookahead = 4;
+constexpr int kDqLookahead = 4;
 
 // ------------------------------------------------------------------ D = rowsum(dO * O), LSE2
 // First statistics row of (b, h) in each half of the workspace (see BwdArgs).
@@ -383,9 +373,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Interleaved versions (no mask needed): 32 MFMA slots per tile.  dV wave: S of block 0,
   // then S of block 1 while the vector ALU forms P of block 0, then dV of block 0 while it
   // forms P of block 1, then dV of block 1.  The dK wave does the same with dP, dS and dK.
-  // MFMA operands read from LDS run XATTN_DKDV_LOOKAHEAD slots ahead.
-  constexpr int LA = XATTN_DKDV_LOOKAHEAD;
-  constexpr bool kIlv = XATTN_DKDV_ILV && D == 128;  // the slot plan assumes 8 chunks, 4 blocks
+  constexpr int LA = kDkdvLookahead;
+  constexpr bool kIlv = D == 128;  // the interleaved slot plan assumes 8 chunks, 4 blocks
   auto dv_tile_ilv = [&](int vt, int cvt, int ch, int ct) __attribute__((always_inline)) {
    if constexpr (kIlv) {  // only instantiated where the slot plan applies
     const char* qs = smem + (vt % NS) * STAGE;
@@ -442,8 +431,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         pa[qb][r4 / 2] = as_bf16x8(u);
         if constexpr (r4 % 2 == 1) *reinterpret_cast<bf16x8*>(pw + (qb * 2 + r4 / 2) * 1024 + 16 * lane) = pa[qb][r4 / 2];
       }
-      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(cvt, ch, ct, i / 3);
-      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
+      if constexpr (i % 3 == 1 && i / 3 < CPW) copy_piece(cvt, ch, ct, i / 3);
+      if constexpr (i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
       sched_fence();
     });
    }
@@ -505,15 +494,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         asm volatile("" : "+v"(u));  // keeps this slot's vector work in place
         dsa[qb][sh] = as_bf16x8(u);
       }
-      if constexpr (XATTN_DKDV_SPREAD && i % 3 == 1 && i / 3 < CPW) copy_piece(cvt, ch, ct, i / 3);
-      if constexpr (XATTN_DKDV_SPREAD && i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
+      if constexpr (i % 3 == 1 && i / 3 < CPW) copy_piece(cvt, ch, ct, i / 3);
+      if constexpr (i == 3 * CPW + 1) copy_stats(cvt, ch, ct);
       sched_fence();
     });
    }
   };
 
-  // Virtual tile vt+1 is copied during iteration vt: up front, or, with XATTN_DKDV_SPREAD, one
-  // piece every third MFMA of the first half of an interleaved tile.  Past the end the last
+  // Virtual tile vt+1 is copied during iteration vt: one piece every third MFMA of the first
+  // half of an interleaved tile, else up front.  Past the end the last
   // head's tile qt_end is copied, its rows and statistics clamped to the last ones, into the
   // stage nobody reads in this iteration.
   int h_nxt = nt == 1 ? 1 : 0, t_nxt = nt == 1 ? qt_begin : qt_begin + 1;  // of vt + 1
@@ -530,7 +519,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int ch = more ? h_nxt : h_end, ct = more ? t_nxt : t_end;
     const bool ilv_dv = kIlv && role == 0 && vt < nvt && !(CAUSAL && t_cur * BQ + doff < kw0 + 31);
     const bool ilv_dk = kIlv && role == 1 && vt > 0;
-    if (!(XATTN_DKDV_SPREAD && (ilv_dv || ilv_dk)) && more) copy_tile(vt + 1, h_nxt, t_nxt);
+    if (!(ilv_dv || ilv_dk) && more) copy_tile(vt + 1, h_nxt, t_nxt);
     if (role == 0) {
       if (vt < nvt) {
         if (ilv_dv) dv_tile_ilv(vt, vt + 1, ch, ct);
@@ -741,7 +730,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // blocks that hold such a key.  Per accumulator the products are summed in the same order
   // as block by block, so the result does not depend on this schedule.  The next tile's copy
   // pieces go out on the odd slots of phases A and B; LDS operands are read LA slots ahead.
-  constexpr int LA = XATTN_DQ_LOOKAHEAD;
+  constexpr int LA = kDqLookahead;
   constexpr int PA = 0, PB = DC, PC = 2 * DC, PD = 3 * DC, PE = 4 * DC, PF = 4 * DC + 2 * DB, NSLOT = 4 * DC + 4 * DB;
   static_assert(CPW <= DC, "copy pieces fit the odd slots of phases A and B");
   static_assert((STAGE & (STAGE - 1)) == 0 && STAGE >= 2 * T::BYTES, "stage toggled by XOR");

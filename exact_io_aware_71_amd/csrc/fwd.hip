@@ -23,11 +23,9 @@
 //   * V^T, the A operand of that product, is read from the row-major V tile with the
 //     transposing ds_read_b64_tr_b16, so the tile is stored exactly as it arrives.
 //   * K/V tiles arrive ahead of use, so HBM/L2 latency hides behind compute ([OPT] §5.2):
-//     fwd_ilv_kernel (bf16, the default for d = 64 and 128) copies them straight into LDS
-//     rings of four stages (buffer_load ... lds, no registers), K three tiles and V two tiles
-//     ahead, one barrier per tile; fwd_bf16_kernel (behind a switch) stages the next tile
-//     through registers into a second LDS buffer; fwd_f32_kernel (fp32 inputs) is
-//     single-buffered.
+//     fwd_ilv_kernel (bf16, d = 64 and 128) copies them straight into LDS rings of four
+//     stages (buffer_load ... lds, no registers), K three tiles and V two tiles ahead, one
+//     barrier per tile; fwd_f32_kernel (fp32 inputs) is single-buffered.
 //   * fwd_ilv_kernel software-pipelines each wave: the MFMAs of P_{u-1} V_{u-1} and of S_{u+1}
 //     interleave with the vector work of the softmax of S_u in fixed slots.
 //   * Causal: tiles past the diagonal are never loaded, waves whose rows all precede a tile
@@ -38,51 +36,10 @@
 #include "common.h"
 #include "launch.h"
 
-// Tile shape per head size: query blocks of 32 per wave (NQ), waves per workgroup (NW) and
-// the waves-per-SIMD occupancy target (WPE) the register budget is sized for.
-#ifndef XATTN_FWD128_NQ
-#define XATTN_FWD128_NQ 1
-#endif
-#ifndef XATTN_FWD128_NW
-#define XATTN_FWD128_NW 8
-#endif
-#ifndef XATTN_FWD128_WPE
-#define XATTN_FWD128_WPE 2
-#endif
-// d = 64 through the interleaved kernel with four waves (128-row tiles, 64 KB of LDS, two
-// workgroups per CU): 4-7% faster than fwd_bf16_kernel at N = 1024 and 4096, causal or not
-// (10-12% before its matrix-core row sum, which the error bound needs; see kMfmaSum).
-// With eight waves (256-row tiles) it lost 13% on 4 x 16 heads of N = 1024 (half as many
-// workgroups).
-#ifndef XATTN_FWD64_ILV
-#define XATTN_FWD64_ILV 1
-#endif
-#ifndef XATTN_FWD64_ILV_NW
-#define XATTN_FWD64_ILV_NW 4
-#endif
-#ifndef XATTN_FWD64_NQ
-#define XATTN_FWD64_NQ 1
-#endif
-#ifndef XATTN_FWD64_NW
-#define XATTN_FWD64_NW 4
-#endif
-#ifndef XATTN_FWD64_WPE
-#define XATTN_FWD64_WPE 2
-#endif
-
 namespace xattn {
 
 constexpr int kFwdBN = 64;  // keys per tile
 static_assert((kMaxSparseTiles - 1) * kFwdBN == kMaxSparseKeys, "block-sparse tile list size");
-constexpr float kLazy = 8.f; // log2 of the largest un-normalised probability allowed
-
-template <int D>
-struct FwdLds {
-  static constexpr int KBYTES = kFwdBN * D * 2;  // swizzled K tile
-  static constexpr int VBYTES = kFwdBN * D * 2;  // swizzled V tile
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int TOTAL = 2 * STAGE;
-};
 
 // Work-item -> (head, query tile): heavy-first for causal, head index fastest.
 __device__ __forceinline__ void fwd_tile_of(int id, int BH, int n_qtiles, bool causal, int& bh, int& qt) {
@@ -91,280 +48,24 @@ __device__ __forceinline__ void fwd_tile_of(int id, int BH, int n_qtiles, bool c
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
-template <int D, int NQ, int NW, int WPE, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask bm,
-    float scale_log2, int n_qtiles, int BH) {
-  constexpr int BM = NW * NQ * 32;
-  constexpr int BN = kFwdBN;
-  constexpr int KB = BN / 32;             // 32-key blocks per tile
-  constexpr int DC = D / 16;              // k-chunks of the QK^T product
-  constexpr int DB = D / 32;              // 32-row blocks of O^T
-  constexpr int CHUNKS = BN * D / 8;      // 16-byte chunks per K (or V) tile
-  constexpr int CPT = CHUNKS / (NW * 64); // chunks per thread per tensor
-  static_assert(CHUNKS % (NW * 64) == 0, "tile must split evenly over the workgroup");
-  using Lds = FwdLds<D>;
-  __shared__ __attribute__((aligned(16))) char smem[Lds::TOTAL];
-  __shared__ uint16_t tlist[SPARSE ? kMaxSparseTiles : 1];  // kept key tiles (block-sparse)
-  static_assert(!SPARSE || BM % kSparseBlock == 0, "query tile must cover whole mask blocks");
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int h32 = lane >> 5;
-
-  int bh, qt;
-  fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
-  const SeqRows sr = seq_rows(geo, b, hq, Hq, hk, Hkv);
-  const int Nq = sr.lq, Nk = sr.lk;
-  const int q0 = qt * BM;
-  if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
-  const uint16_t* qp = q + sr.q * D;
-  const uint16_t* kp = k + sr.k * D;
-  const uint16_t* vp = v + sr.k * D;
-  const int qw0 = q0 + wave * NQ * 32;
-  // Causal masks align the last query with the last key: query i sees keys j <= i + Nk - Nq.
-  const int qd0 = qw0 + (Nk - Nq);
-
-  // Q^T operand: lane holds query qw0 + qb*32 + l32, features 16c + 8*h32 .. +7.
-  bf16x8 qreg[NQ][DC];
-#pragma unroll
-  for (int qb = 0; qb < NQ; ++qb) {
-    const int qi = qw0 + qb * 32 + l32;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (qi < Nq) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
-      qreg[qb][c] = as_bf16x8(u);
-    }
-  }
-
-  f32x16 acc[DB][NQ];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < NQ; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.f;
-  float m_run[NQ], l_run[NQ];
-#pragma unroll
-  for (int qb = 0; qb < NQ; ++qb) { m_run[qb] = kMaxInit; l_run[qb] = 0.f; }
-
-  const int kv_end = CAUSAL ? min(Nk, q0 + BM + (Nk - Nq)) : Nk;
-  int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-  // Block-sparse: walk only the tiles one of the workgroup's query blocks keeps; walk position
-  // t holds key tile kt(t) and the wave skips tiles its own block drops.  Dense: kt(t) = t.
-  if constexpr (SPARSE)
-    ntiles = build_tile_list<SPARSE ? BM / kSparseBlock : 1>(bm, b, hq, q0 / kSparseBlock, ntiles, tlist);
-  auto entry = [&](int t) __attribute__((always_inline)) -> int {
-    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tlist[t]);
-    else return t;
-  };
-  auto ktile = [&](int e) __attribute__((always_inline)) -> int { return SPARSE ? (e & 0x3fff) : e; };
-
-  u32x4 pk[CPT], pv[CPT];
-  auto load_tile = [&](int t) {
-    const int t0 = t * BN;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NW * 64;
-      const int row = c / (D / 8);
-      const int col = c % (D / 8);
-      const int key = t0 + row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (key < Nk) {
-        zk = ld_global16(kp + (size_t)key * D + col * 8);
-        zv = ld_global16(vp + (size_t)key * D + col * 8);
-      }
-      pk[i] = zk;
-      pv[i] = zv;
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* ks = smem + stage * Lds::STAGE;
-    char* vs = ks + Lds::KBYTES;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NW * 64;
-      const int row = c / (D / 8);
-      const int col = c % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + swz<D>(row, col)) = pk[i];
-      *reinterpret_cast<u32x4*>(vs + swz<D>(row, col)) = pv[i];
-    }
-  };
-
-  load_tile(ntiles > 0 ? ktile(entry(0)) : 0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_tile(ktile(entry(t + 1)));
-    const int e = entry(t);
-    const int t0 = ktile(e) * BN;
-    const char* ks = smem + (t & 1) * Lds::STAGE;
-    const char* vs = ks + Lds::KBYTES;
-    // A wave whose queries all precede this tile has nothing to add (causal skip), nor one whose
-    // query block drops it.
-    const bool keep = !SPARSE || ((e >> (14 + (qw0 - q0) / kSparseBlock)) & 1) != 0;
-    const bool active = keep && qw0 < Nq && (!CAUSAL || (t0 <= qd0 + NQ * 32 - 1));
-    if (active) {
-      f32x16 s[KB][NQ];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < NQ; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + swz<D>(kb * 32 + l32, 2 * c + h32));
-#pragma unroll
-          for (int qb = 0; qb < NQ; ++qb) s[kb][qb] = mfma32(a, qreg[qb][c], s[kb][qb]);
-        }
-      }
-      // Mask keys past the end and, on diagonal tiles, keys after the query.
-      const bool need_mask = (t0 + BN > Nk) || (CAUSAL && t0 + BN - 1 > qd0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < NQ; ++qb) {
-            const int kmax = qd0 + qb * 32 + l32;  // last key of this lane's row
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-              if (kj >= Nk || (CAUSAL && kj > kmax)) s[kb][qb][r] = -INFINITY;
-            }
-          }
-      }
-      // Online softmax ([OPT] §3.2.1) in the base-2 domain, t = s * scale * log2(e).
-      // The reference max m_run moves only when a row's tile max exceeds it by more than
-      // kLazy (i.e. p could exceed 2^kLazy); otherwise p = 2^(t - m_run) <= 2^kLazy is
-      // accumulated against the stale reference.  Final O = acc / l and LSE = m + log2 l
-      // are identical in exact arithmetic, and the O rescale is skipped on most tiles.
-#pragma unroll
-      for (int qb = 0; qb < NQ; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = max_xor32(mx) * scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kLazy) != 0) {  // wave-uniform branch
-          const float m_new = fmaxf(m_run[qb], mx);
-          const float alpha = fast_exp2(m_run[qb] - m_new);  // both finite (m starts at kMaxInit)
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[db][qb][r] *= alpha;
-        }
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(s[kb][qb][r], scale_log2, -m_run[qb]));
-            s[kb][qb][r] = p;
-            rs += p;
-          }
-        l_run[qb] += rs;
-      }
-      // O^T += V^T P^T over the tile's keys, 16 keys per MFMA.
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          bf16x8 pb[NQ];
-#pragma unroll
-          for (int qb = 0; qb < NQ; ++qb) {
-            u32x4 u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(s[kb][qb][8 * sh + 2 * e], s[kb][qb][8 * sh + 2 * e + 1]);
-            pb[qb] = as_bf16x8(u);
-          }
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 a = ld_tr_operand<D>(vs, kb * 32 + 16 * sh, db * 32, lane);
-#pragma unroll
-            for (int qb = 0; qb < NQ; ++qb) acc[db][qb] = mfma32(a, pb[qb], acc[db][qb]);
-          }
-        }
-      }
-    }
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
-    __syncthreads();
-  }
-
-  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l); a row without keys (l = 0) gets O = 0
-  // and LSE = -inf.
-  uint16_t* op = o + sr.q * D;
-#pragma unroll
-  for (int qb = 0; qb < NQ; ++qb) {
-    const float lt = sum_xor32(l_run[qb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int qi = qw0 + qb * 32 + l32;
-    if (qi < Nq) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d = db * 32 + 8 * jj + 4 * h32;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[db][qb][4 * jj + 0] * inv, acc[db][qb][4 * jj + 1] * inv);
-          w[1] = pack_bf16x2(acc[db][qb][4 * jj + 2] * inv, acc[db][qb][4 * jj + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
-        }
-      if (lse != nullptr && h32 == 0) lse[sr.q + qi] = (m_run[qb] + fast_log2(lt)) * kLn2;
-    }
-  }
-}
-
-// Interleaved forward (bf16, d = 128).  Eight waves, two per SIMD, each owning 32 query rows
-// of a 256-row block (XATTN_ILV_RB = 2: four waves of 64 rows, one per SIMD).  Each wave
-// software-pipelines its own work over 32-key blocks u: in step u it issues
+// Interleaved forward (bf16, d = 64 and 128).  Each wave owns 32 query rows of the
+// workgroup's block and software-pipelines its own work over 32-key blocks u: in step u it
+// issues
 //   O^T += V_{u-1}^T P_{u-1}^T  and  S_{u+1}^T = K_{u+1} Q^T        (MFMAs)
 // and, between those MFMAs, the online softmax of S_u into P_u       (vector ALU),
 // which are independent of each other, so the matrix core and the vector ALU of the SIMD
-// work at the same time within one wave.  The S and P register sets alternate roles between
-// even and odd steps.  K and V arrive in 64-key tiles through direct global -> LDS copies
-// into two rings of four stages (128 KB); the two steps of tile t read K_t, K_{t+1}, V_{t-1},
-// V_t, copy K_{t+3} and V_{t+2}, and end with one barrier.  With 32-key tiles (64 KB, four
-// waves: two workgroups per CU) each step is a tile of its own: step t reads K_{t+1} and
-// V_{t-1}, copies K_{t+3} and V_{t+2}, and ends with the barrier.  A rescale of O forced by a
-// moved running max is applied after the step's MFMAs, before P_u is added.
-#ifndef XATTN_FWD_ILV
-#define XATTN_FWD_ILV 1
-#endif
-#ifndef XATTN_ILV_LOOKAHEAD
-#define XATTN_ILV_LOOKAHEAD 4
-#endif
-#ifndef XATTN_ILV_COPY_SLOT
-#define XATTN_ILV_COPY_SLOT 6
-#endif
-#ifndef XATTN_ILV_PRIO
-#define XATTN_ILV_PRIO 0
-#endif
-
-// S^T = K Q^T block products for the interleaved kernel, written to vector registers (the
-// softmax reads them there), while O^T accumulates in accumulation registers.  Issued from inline
-// assembly because the compiler picks one register file for all MFMA results of a kernel.
-// The hardware chains back-to-back MFMAs on the same accumulator; a vector-ALU read of the
-// result must follow the last MFMA by at least 19 wait states (qk_result_fence).
-#ifndef XATTN_ILV_QKASM
-#define XATTN_ILV_QKASM 0
-#endif
-#ifndef XATTN_ILV_RB
-#define XATTN_ILV_RB 1
-#endif
+// work at the same time within one wave; two waves share each SIMD.  The S and P register
+// sets alternate roles between even and odd steps.  K and V arrive in 64-key tiles through
+// direct global -> LDS copies into two rings of four stages; the two steps of tile t read
+// K_t, K_{t+1}, V_{t-1}, V_t, copy K_{t+3} and V_{t+2}, and end with one barrier.  With
+// 32-key tiles each step is a tile of its own: step t reads K_{t+1} and V_{t-1}, copies
+// K_{t+3} and V_{t+2}, and ends with the barrier.  A rescale of O forced by a moved running
+// max is applied after the step's MFMAs, before P_u is added.
+//
+// LDS operands of the MFMAs are read this many MFMA slots ahead of their use.
+constexpr int kIlvLookahead = 4;
+// MFMA slot (modulo the copy spacing) at which a step issues each of its copies.
+constexpr int kIlvCopySlot = 6;
 // Dense and packed d = 128 inputs come in two shapes.  Wide: 8 waves (256 query rows) with
 // 64-key tiles, one workgroup per CU (128 KB of LDS).  Narrow: 4 waves (128 rows) with 32-key
 // tiles (64 KB), two workgroups per CU, so that one's prologue (Q loads, first copies) and
@@ -374,48 +75,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // N = 512, +10% on packed batches of 256-4096 tokens), ties at 2048 keys (N = 4096 causal)
 // and loses 2-5% on long walks (non-causal N = 4096, causal N = 16384, a 1024-query chunk
 // onto 8192 keys).  Both give bit-identical results (same 32-key block order and arithmetic).
-// The narrow shape is taken below XATTN_FWD128_NARROW_KEYS average keys per query tile
-// (0: never), or when the wide grid would leave CUs idle.
-#ifndef XATTN_FWD128_NARROW_KEYS
-#define XATTN_FWD128_NARROW_KEYS 2048
-#endif
-// 1: the running max is checked through the row sums of the new probabilities instead of a
-// per-step row max (see the step below).
-#ifndef XATTN_ILV_SUMCHECK
-#define XATTN_ILV_SUMCHECK 1
-#endif
+// The narrow shape is taken below this many average keys per query tile, or when the wide
+// grid would leave CUs idle.
+constexpr double kFwd128NarrowKeys = 2048.0;
 // Largest lane-partial row sum of one 32-key step accepted without moving the reference max
 // (so every probability stays below it).
 constexpr float kSumMax = 256.f;
 
-__device__ __forceinline__ void mfma_qk_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
-#if XATTN_ILV_QKASM == 1
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "a"(b));
-#elif XATTN_ILV_QKASM == 2
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
-#else
-  f32x16 z;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) z[r] = 0.f;
-  c = mfma32(a, b, z);
-#endif
-}
-__device__ __forceinline__ void mfma_qk_next(f32x16& c, const bf16x8& a, const bf16x8& b) {
-#if XATTN_ILV_QKASM == 1
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
-#elif XATTN_ILV_QKASM == 2
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-#else
-  c = mfma32(a, b, c);
-#endif
-}
-__device__ __forceinline__ void qk_result_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
-template <int D, int RB_, int NW_ = 8 / RB_, int BN_ = kFwdBN>
+template <int D, int NW_, int BN_>
 struct IlvShape {
   static constexpr int BN = BN_, DC = D / 16, DB = D / 32;
   static constexpr int SPT = BN / 32;              // 32-key steps per tile
-  static constexpr int RB = RB_, NW = NW_, BM = NW * RB * 32;
+  static constexpr int NW = NW_, BM = NW * 32;     // waves, query rows per workgroup
   static constexpr int TILE = BN * D * 2;          // bytes of one K or V tile
   static constexpr int NS = 4;                     // stages per ring
   static constexpr int RPC = 1024 / (2 * D);       // tile rows per 1 KB wave copy
@@ -426,15 +97,15 @@ struct IlvShape {
   static constexpr int NQK = DC;                   // K operands per 32-key block
 };
 
-template <int D, int RB_, int NW_, int BN_, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB_, 2 / RB_))) void fwd_ilv_kernel(
+template <int D, int NW_, int BN_, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_ilv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask bm,
     float scale_log2, int n_qtiles, int BH) {
-  using S = IlvShape<D, RB_, NW_, BN_>;
-  constexpr int BN = S::BN, SPT = S::SPT, DC = S::DC, DB = S::DB, RB = S::RB, NS = S::NS, NW = S::NW;
+  using S = IlvShape<D, NW_, BN_>;
+  constexpr int BN = S::BN, SPT = S::SPT, DC = S::DC, DB = S::DB, NS = S::NS, NW = S::NW;
   constexpr int TILE = S::TILE, CPW = S::CPW, CPS = S::CPS, RPC = S::RPC, NPV = S::NPV, NQK = S::NQK;
-  constexpr int NOPS = NPV + NQK, NMF = RB * NOPS, L = XATTN_ILV_LOOKAHEAD;
+  constexpr int NMF = NPV + NQK, L = kIlvLookahead;
   static_assert(NS == 4 && CPS <= 4, "copy schedule");
   static_assert(!SPARSE || BN == 64, "the block-sparse tile list counts 64-key tiles");
   constexpr int CSP = NMF / CPS;  // MFMA slots per copy
@@ -457,32 +128,29 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   const uint16_t* qp = q + sr.q * D;
   const uint16_t* kp = k + sr.k * D;
   const uint16_t* vp = v + sr.k * D;
-  const int qw0 = q0 + wave * (RB * 32);  // rows qw0 + 32 rb + l32
+  const int qw0 = q0 + wave * 32;  // rows qw0 + l32
   // Causal masks align the last query with the last key: query i sees keys j <= i + Nk - Nq.
   // A wave without query rows (past the end of a shorter sequence) skips all its MFMA work:
   // under the causal test its limit lies before every key.
   const bool has_rows = qw0 < Nq;
   const int qd0 = has_rows ? qw0 + (Nk - Nq) : -(1 << 29);  // last key visible to the wave's first row
 
-  // Q^T operands: lane holds query qw0 + 32 rb + l32, features 16c + 8*h32 .. +7.
-  bf16x8 qreg[RB][DC];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int qi = qw0 + 32 * rb + l32;
+  // Q^T operands: lane holds query qw0 + l32, features 16c + 8*h32 .. +7.
+  bf16x8 qreg[DC];
+  {
+    const int qi = qw0 + l32;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       u32x4 u = {0u, 0u, 0u, 0u};
       if (qi < Nq) u = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
-      qreg[rb][c] = as_bf16x8(u);
+      qreg[c] = as_bf16x8(u);
     }
   }
-  f32x16 acc[RB][DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][db][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   // O is divided by the sum of the same bf16 probabilities its P V product used, so that a row
   // dominated by one key gets that key's V row exactly; the fp32 sum l_run still gives the LSE.
   // Dividing by the fp32 sum instead leaves the bf16 rounding of the dominant probability (up
@@ -495,47 +163,40 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   // C row 0 accumulates the sum of query n and row 1 that of query n+16, in lanes 0-15.
   // (Measured against eight v_dot2_f32_bf16 per step, and two 32x32x16 products against ones:
   // 2.5-5% faster at d = 128, 3-13% at d = 64.)
-  f32x4 lsum[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
   const bool sel_on = ((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1);
   const bf16x8 sel16 = sel_on ? as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u})
                               : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   // Rescale of lsum by the per-row factor a: row 1 of lanes 0-15 belongs to query lane + 16.
-  auto lsum_scale = [&](int rb, float a) __attribute__((always_inline)) {
+  auto lsum_scale = [&](float a) __attribute__((always_inline)) {
     const float a_hi = __shfl(a, (lane & 15) + 16);
-    lsum[rb][0] *= a;
-    lsum[rb][1] *= a_hi;
+    lsum[0] *= a;
+    lsum[1] *= a_hi;
   };
-  float m_run[RB], l_run[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) { m_run[rb] = kMaxInit; l_run[rb] = 0.f; }
+  float m_run = kMaxInit, l_run = 0.f;
 
   // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l); a row without keys (l = 0) gets O = 0
   // and LSE = -inf.
   auto epilogue = [&]() __attribute__((always_inline)) {
     uint16_t* op = o + sr.q * D;
+    const float lt = sum_xor32(l_run);
+    // A row with keys has a bf16 sum >= 1: its largest probability is at least 1 against the
+    // reference max, which never exceeds the row's running max.
+    const float r0 = __shfl(lsum[0], l32 & 15), r1 = __shfl(lsum[1], l32 & 15);
+    const float inv = lt > 0.f ? 1.f / (l32 < 16 ? r0 : r1) : 0.f;
+    const int qi = qw0 + l32;
+    if (qi < Nq) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float lt = sum_xor32(l_run[rb]);
-      // A row with keys has a bf16 sum >= 1: its largest probability is at least 1 against the
-      // reference max, which never exceeds the row's running max.
-      const float r0 = __shfl(lsum[rb][0], l32 & 15), r1 = __shfl(lsum[rb][1], l32 & 15);
-      const float inv = lt > 0.f ? 1.f / (l32 < 16 ? r0 : r1) : 0.f;
-      const int qi = qw0 + 32 * rb + l32;
-      if (qi < Nq) {
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int d = db * 32 + 8 * jj + 4 * h32;
-            u32x2 w;
-            w[0] = pack_bf16x2(acc[rb][db][4 * jj + 0] * inv, acc[rb][db][4 * jj + 1] * inv);
-            w[1] = pack_bf16x2(acc[rb][db][4 * jj + 2] * inv, acc[rb][db][4 * jj + 3] * inv);
-            *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
-          }
-        if (lse != nullptr && h32 == 0) lse[sr.q + qi] = (m_run[rb] + fast_log2(lt)) * kLn2;
-      }
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = db * 32 + 8 * jj + 4 * h32;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv);
+          w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + (size_t)qi * D + d) = w;
+        }
+      if (lse != nullptr && h32 == 0) lse[sr.q + qi] = (m_run + fast_log2(lt)) * kLn2;
     }
   };
 
@@ -590,13 +251,10 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     const uint32_t m0v = wdst + (is_k ? 0 : NS * TILE) + (tile & (NS - 1)) * TILE + 1024 * i;
     bdma16_m0(rsrc, loff[i], m0v);
   };
-  // LDS base of 32-key block u of K (V): tile u/SPT, rows 32*(u%SPT) ..  (u = -1 at the
-  // first step: the zeroed last stage.)
+  // LDS base of 32-key block u of V (relative to the V ring, see ofs.v): tile u/SPT, rows
+  // 32*(u%SPT) ..
   constexpr int SPT_SH = SPT == 2 ? 1 : 0;
-  auto kblk = [&](int u) __attribute__((always_inline)) {
-    return smem + ((u >> SPT_SH) & (NS - 1)) * TILE + (u & (SPT - 1)) * 32 * (2 * D);
-  };
-  auto vblk = [&](int u) __attribute__((always_inline)) {  // relative to the V ring (see ofs.v)
+  auto vblk = [&](int u) __attribute__((always_inline)) {
     return smem + ((u >> SPT_SH) & (NS - 1)) * TILE + (u & (SPT - 1)) * 32 * (2 * D);
   };
   // Operand j of a step: j < NPV are V^T operands (sh, db), db fastest; then the K operands c.
@@ -615,7 +273,7 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   // probability 0).
   auto active = [&](int u) __attribute__((always_inline)) {
     if constexpr (SPARSE || !CAUSAL) return has_rows;
-    else return (u - 1) * 32 <= qd0 + RB * 32 - 1;
+    else return (u - 1) * 32 <= qd0 + 31;
   };
   auto kt = [&](int i) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) return entry(i) & 0x3fff;
@@ -646,36 +304,24 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   }
   for (int i = tid; i < TILE / 16; i += NW * 64)
     *reinterpret_cast<u32x4*>(smem + NS * TILE + (NS - 1) * TILE + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-  f32x16 sA[RB], sB[RB];
-  u32x4 pA[RB][2], pB[RB][2];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh) pA[rb][sh] = u32x4{0u, 0u, 0u, 0u};
+  f32x16 sA, sB;
+  u32x4 pA[2], pB[2];
+  pA[0] = u32x4{0u, 0u, 0u, 0u};
+  pA[1] = u32x4{0u, 0u, 0u, 0u};
   wait_vmem();  // also covers the Q loads
   lds_barrier();
   // S_0.
   {
-    const char* ks = kblk(0);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ofs.k[c]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + ofs.k[c]);
+      if (c == 0) {
+        f32x16 z;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if constexpr (RB == 1) {
-          if (c == 0) {
-            f32x16 z;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = 0.f;
-            sA[rb] = mfma32(a, qreg[rb][0], z);
-          } else {
-            sA[rb] = mfma32(a, qreg[rb][c], sA[rb]);
-          }
-        } else if (c == 0) {
-          mfma_qk_first(sA[rb], a, qreg[rb][0]);
-        } else {
-          mfma_qk_next(sA[rb], a, qreg[rb][c]);
-        }
+        for (int r = 0; r < 16; ++r) z[r] = 0.f;
+        sA = mfma32(a, qreg[0], z);
+      } else {
+        sA = mfma32(a, qreg[c], sA);
       }
     }
   }
@@ -685,21 +331,17 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
   // copied too, clamped to the last key, into stages nobody reads any more, so every step
   // issues the same copies and the wait counts stay fixed.  kcur is the key tile of S_u and
   // keep whether the wave's query block keeps it (block-sparse).
-  auto step = [&](int u, auto phc, auto stc, f32x16(&sc)[RB], f32x16(&sn)[RB], u32x4(&pp)[RB][2],
-                  u32x4(&pc)[RB][2], int t, int kcur, bool keep) __attribute__((always_inline)) {
+  auto step = [&](int u, auto phc, auto stc, f32x16& sc, f32x16& sn, u32x4(&pp)[2], u32x4(&pc)[2], int t, int kcur,
+                  bool keep) __attribute__((always_inline)) {
     if (active(u)) {
-      if constexpr (RB > 1 && XATTN_ILV_QKASM != 0) qk_result_fence();  // S_u came from asm MFMAs
       const int u0 = kcur * BN + (u & (SPT - 1)) * 32;  // first key of S_u
       const bool drop = SPARSE && !keep;
       if (drop || (u0 + 32 > Nk) || (CAUSAL && u0 + 31 > qd0)) {
+        const int kmax = qd0 + l32;  // last key of this lane's row
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int kmax = qd0 + 32 * rb + l32;  // last key of this lane's row
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kj = u0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            if (drop || kj >= Nk || (CAUSAL && kj > kmax)) sc[rb][r] = -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int kj = u0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          if (drop || kj >= Nk || (CAUSAL && kj > kmax)) sc[r] = -INFINITY;
         }
       }
       // K block u+1 and V block u-1 at offsets known at compile time from the ring stage of
@@ -709,89 +351,51 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       constexpr int vst = SPT == 2 ? (st + NS - 1 + ph) % NS : (st + NS - 1) % NS, vhalf = SPT == 2 ? 1 - ph : 0;
       const char* ks = smem + (kst * TILE + khalf * 32 * (2 * D));
       const char* vs = smem + (vst * TILE + vhalf * 32 * (2 * D));  // V ring base is in ofs.v
-      float m4[RB][2];
-      float alpha[RB];
-      float rs[RB][2];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) { rs[rb][0] = 0.f; rs[rb][1] = 0.f; alpha[rb] = 1.f; }
-      bool resc = false;
+      float rs0 = 0.f, rs1 = 0.f;
       bf16x8 buf[L];
       static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(ks, vs, jc); });
-      if (XATTN_ILV_PRIO) __builtin_amdgcn_s_setprio(1);
       sched_fence();
       static_for<NMF>([&](auto ic) {
-        constexpr int i = decltype(ic)::value, j = i / RB, rb = i % RB;
+        constexpr int j = decltype(ic)::value;
         if constexpr (j < NPV) {
           constexpr int db = j % DB, sh = j / DB;
-          acc[rb][db] = mfma32(buf[j % L], as_bf16x8(pp[rb][sh]), acc[rb][db]);
-          if constexpr (db == 0) lsum[rb] = mfma16(sel16, as_bf16x8(pp[rb][sh]), lsum[rb]);
+          acc[db] = mfma32(buf[j % L], as_bf16x8(pp[sh]), acc[db]);
+          if constexpr (db == 0) lsum = mfma16(sel16, as_bf16x8(pp[sh]), lsum);
         } else {
           constexpr int c = j - NPV;
-          if constexpr (RB == 1) {
-            if constexpr (c == 0) {
-              f32x16 z;
+          if constexpr (c == 0) {
+            f32x16 z;
 #pragma unroll
-              for (int r = 0; r < 16; ++r) z[r] = 0.f;
-              sn[rb] = mfma32(buf[j % L], qreg[rb][0], z);
-            } else {
-              sn[rb] = mfma32(buf[j % L], qreg[rb][c], sn[rb]);
-            }
-          } else if constexpr (c == 0) {
-            mfma_qk_first(sn[rb], buf[j % L], qreg[rb][0]);
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            sn = mfma32(buf[j % L], qreg[0], z);
           } else {
-            mfma_qk_next(sn[rb], buf[j % L], qreg[rb][c]);
+            sn = mfma32(buf[j % L], qreg[c], sn);
           }
         }
-        if constexpr (rb == RB - 1 && j + L < NOPS) buf[j % L] = operand(ks, vs, std::integral_constant<int, j + L>{});
-        // Vector work.  With the sum check: only the exponentials, spread evenly over slots
-        // 1 .. NMF-2.  Otherwise: row maxima (slots 0 .. 2RB-1), then the exponentials over
-        // slots 2RB+1 .. NMF-2.
-        if constexpr (!XATTN_ILV_SUMCHECK && i < RB) {
-          // Two chains of v_max3 over the lane's 16 scores of row block i.
-#pragma unroll
-          for (int ch = 0; ch < 2; ++ch) {
-            float m = fmaxf(sc[i][8 * ch], sc[i][8 * ch + 1]);
-#pragma unroll
-            for (int e = 2; e < 8; e += 2) m = fmaxf(fmaxf(m, sc[i][8 * ch + e]), sc[i][8 * ch + e + 1]);
-            m4[i][ch] = m;
-          }
-        } else if constexpr (!XATTN_ILV_SUMCHECK && i < 2 * RB) {
-          constexpr int vrb = i - RB;
-          float mx = fmaxf(m4[vrb][0], m4[vrb][1]);
-          mx = max_xor32(mx) * scale_log2;
-          // Lazy reference max ([OPT] §3.2.1 with a deferred rescale): it moves only when a
-          // row's block max exceeds it by more than 2^kLazy; it starts at kMaxInit (finite).
-          const bool up = __builtin_amdgcn_ballot_w64(mx > m_run[vrb] + kLazy) != 0;
-          const float m_new = up ? fmaxf(m_run[vrb], mx) : m_run[vrb];
-          alpha[vrb] = fast_exp2(m_run[vrb] - m_new);
-          m_run[vrb] = m_new;
-          l_run[vrb] *= alpha[vrb];
-          resc = resc || up;
-        }
-        constexpr int E0 = XATTN_ILV_SUMCHECK ? 1 : 2 * RB + 1, NE = RB * 4, ESPAN = NMF - 2 - E0;
+        if constexpr (j + L < NMF) buf[j % L] = operand(ks, vs, std::integral_constant<int, j + L>{});
+        // Vector work: the exponentials of S_u, four per group, spread evenly over slots
+        // 1 .. NMF-2.
+        constexpr int E0 = 1, NE = 4, ESPAN = NMF - 2 - E0;
         static_for<NE>([&](auto ec) {
-          constexpr int e = decltype(ec)::value;
-          if constexpr (E0 + e * ESPAN / NE == i) {
-            constexpr int erb = e / 4, jq = e % 4;
+          constexpr int jq = decltype(ec)::value;
+          if constexpr (E0 + jq * ESPAN / NE == j) {
             float p[4];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) p[w] = fast_exp2(fmaf(sc[erb][4 * jq + w], scale_log2, -m_run[erb]));
+            for (int w = 0; w < 4; ++w) p[w] = fast_exp2(fmaf(sc[4 * jq + w], scale_log2, -m_run));
             uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
             // fp32 row sums (summing the bf16-rounded values would cost the LSE up to 2^-9).
-            rs[erb][0] += p[0] + p[2];
-            rs[erb][1] += p[1] + p[3];
+            rs0 += p[0] + p[2];
+            rs1 += p[1] + p[3];
             // Keeps this step's vector work in its slot (the compiler would otherwise sink it).
-            asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs[erb][0]), "+v"(rs[erb][1]));
-            pc[erb][jq / 2][2 * (jq % 2)] = w0;
-            pc[erb][jq / 2][2 * (jq % 2) + 1] = w1;
+            asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs0), "+v"(rs1));
+            pc[jq / 2][2 * (jq % 2)] = w0;
+            pc[jq / 2][2 * (jq % 2) + 1] = w1;
           }
         });
         // The step's CPS copies, one every CSP slots (slots 6 and 14 with 64-key tiles at d = 128).
-        if constexpr (i % CSP == XATTN_ILV_COPY_SLOT % CSP && i / CSP < CPS) step_copy(t, phc, i / CSP);
+        if constexpr (j % CSP == kIlvCopySlot % CSP && j / CSP < CPS) step_copy(t, phc, j / CSP);
         sched_fence();
       });
-      if (XATTN_ILV_PRIO) __builtin_amdgcn_s_setprio(0);
-#if XATTN_ILV_SUMCHECK
       // Reference max check ([OPT] §3.2.1, lazily): the step's probabilities were formed
       // against the current reference m.  If every lane-partial row sum stays at or below
       // kSumMax (so does every probability; the first visible key of a row overflows against
@@ -799,65 +403,38 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
       // redoes the step with m moved to the running max (at least kMaxInit, so finite) and
       // rescales O and l by 2^(m_old - m_new); the P V products already issued this step used
       // the old m, as O did.  Masked scores (-inf) give probability 0 against any finite m.
-      {
-        bool bad = false;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) bad = bad || !(rs[rb][0] + rs[rb][1] <= kSumMax);
-        resc = __builtin_amdgcn_ballot_w64(bad) != 0;
-      }
-      if (resc) {
+      if (__builtin_amdgcn_ballot_w64(!(rs0 + rs1 <= kSumMax)) != 0) {
         sched_fence();
+        float mx = sc[0];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          float mx = sc[rb][0];
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        mx = max_xor32(mx) * scale_log2;
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        rs0 = 0.f;
+        rs1 = 0.f;
 #pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[rb][r]);
-          mx = max_xor32(mx) * scale_log2;
-          const float m_new = fmaxf(m_run[rb], mx);
-          alpha[rb] = fast_exp2(m_run[rb] - m_new);
-          m_run[rb] = m_new;
-          l_run[rb] *= alpha[rb];
-          rs[rb][0] = 0.f;
-          rs[rb][1] = 0.f;
+        for (int jq = 0; jq < 4; ++jq) {
+          float pv[4];
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            float pv[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) pv[w] = fast_exp2(fmaf(sc[rb][4 * jq + w], scale_log2, -m_new));
-            const uint32_t w0 = pack_bf16x2(pv[0], pv[1]), w1 = pack_bf16x2(pv[2], pv[3]);
-            rs[rb][0] += pv[0] + pv[2];
-            rs[rb][1] += pv[1] + pv[3];
-            pc[rb][jq / 2][2 * (jq % 2)] = w0;
-            pc[rb][jq / 2][2 * (jq % 2) + 1] = w1;
-          }
+          for (int w = 0; w < 4; ++w) pv[w] = fast_exp2(fmaf(sc[4 * jq + w], scale_log2, -m_new));
+          const uint32_t w0 = pack_bf16x2(pv[0], pv[1]), w1 = pack_bf16x2(pv[2], pv[3]);
+          rs0 += pv[0] + pv[2];
+          rs1 += pv[1] + pv[3];
+          pc[jq / 2][2 * (jq % 2)] = w0;
+          pc[jq / 2][2 * (jq % 2) + 1] = w1;
         }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) lsum_scale(rb, alpha[rb]);
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        lsum_scale(alpha);
         sched_fence();
       }
-#else
-      if (resc) {  // rare: a real branch (the fence keeps it from being flattened into selects)
-        sched_fence();
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha[rb];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) lsum_scale(rb, alpha[rb]);
-        sched_fence();
-      }
-#endif
       // One branch only: a second one on the same condition costs the allocator ~40 registers.
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
+      l_run += rs0 + rs1;
     } else {
 #pragma unroll
       for (int i = 0; i < CPS; ++i) step_copy(t, phc, i);
@@ -902,11 +479,8 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2 / RB
     static_for<NPV>([&](auto jc) {
       constexpr int j = decltype(jc)::value, db = j % DB, sh = j / DB;
       const bf16x8 a = operand(vs, vs, jc);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        acc[rb][db] = mfma32(a, as_bf16x8(pA[rb][sh]), acc[rb][db]);
-        if constexpr (db == 0) lsum[rb] = mfma16(sel16, as_bf16x8(pA[rb][sh]), lsum[rb]);
-      }
+      acc[db] = mfma32(a, as_bf16x8(pA[sh]), acc[db]);
+      if constexpr (db == 0) lsum = mfma16(sel16, as_bf16x8(pA[sh]), lsum);
     });
   }
 
@@ -1026,41 +600,26 @@ static hipError_t launch_fwd_grid(FwdKernel<T> kern, int BM, int threads, const 
 hipError_t launch_fwd(const FwdArgs& a) {
   if (a.dtype == 0)  // fp32, d = 64 (dense only)
     return launch_fwd_grid<float>(a.causal ? fwd_f32_kernel<true> : fwd_f32_kernel<false>, 128, 256, a);
-#if XATTN_FWD_ILV
-  if (a.d == 128) {
-    if (a.block_mask) {  // the block-sparse tile list counts 64-key tiles
-      using S = IlvShape<128, XATTN_ILV_RB>;
-      return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, XATTN_ILV_RB, S::NW, S::BN), S::BM,
-                                       S::NW * 64, a);
-    }
-    // Average keys walked by one query tile (packed: per-sequence averages).
-    const double nq = a.cu_q ? (double)a.Nq / a.B : (double)a.Nq;
-    const double nk = a.cu_q ? (double)a.Nk / a.B : (double)a.Nk;
-    const double walk = a.causal ? (nk > nq ? nk - nq : 0.0) + 0.5 * (nq < nk ? nq : nk) : nk;
-    using W = IlvShape<128, 1, 8, 64>;
-    using N = IlvShape<128, 1, 4, 32>;
-    const long long wide_grid = (long long)((a.max_q + W::BM - 1) / W::BM) * a.B * a.Hq;
-    if (walk < XATTN_FWD128_NARROW_KEYS || wide_grid < 256)
-      return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, 1, N::NW, N::BN, true, false>
-                                                : fwd_ilv_kernel<128, 1, N::NW, N::BN, false, false>,
-                                       N::BM, N::NW * 64, a);
-    return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, 1, W::NW, W::BN, true, false>
-                                              : fwd_ilv_kernel<128, 1, W::NW, W::BN, false, false>,
-                                     W::BM, W::NW * 64, a);
+  if (a.d == 64) {  // four waves, 128-row tiles, 64-key tiles: two workgroups per CU
+    using S = IlvShape<64, 4, 64>;
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, S::NW, S::BN), S::BM, S::NW * 64, a);
   }
-#endif
-#if XATTN_FWD64_ILV
-  if (a.d == 64) {
-    using S = IlvShape<64, 1, XATTN_FWD64_ILV_NW>;
-    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, 1, S::NW, S::BN), S::BM, S::NW * 64, a);
-  }
-#endif
-  if (a.d == 128) {
-    constexpr int NQ = XATTN_FWD128_NQ, NW = XATTN_FWD128_NW, WPE = XATTN_FWD128_WPE;
-    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_bf16_kernel, 128, NQ, NW, WPE), NW * NQ * 32, NW * 64, a);
-  }
-  constexpr int NQ = XATTN_FWD64_NQ, NW = XATTN_FWD64_NW, WPE = XATTN_FWD64_WPE;
-  return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_bf16_kernel, 64, NQ, NW, WPE), NW * NQ * 32, NW * 64, a);
+  using W = IlvShape<128, 8, 64>;
+  using N = IlvShape<128, 4, 32>;
+  if (a.block_mask)  // the block-sparse tile list counts 64-key tiles
+    return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 128, W::NW, W::BN), W::BM, W::NW * 64, a);
+  // Average keys walked by one query tile (packed: per-sequence averages).
+  const double nq = a.cu_q ? (double)a.Nq / a.B : (double)a.Nq;
+  const double nk = a.cu_q ? (double)a.Nk / a.B : (double)a.Nk;
+  const double walk = a.causal ? (nk > nq ? nk - nq : 0.0) + 0.5 * (nq < nk ? nq : nk) : nk;
+  const long long wide_grid = (long long)((a.max_q + W::BM - 1) / W::BM) * a.B * a.Hq;
+  if (walk < kFwd128NarrowKeys || wide_grid < 256)
+    return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, N::NW, N::BN, true, false>
+                                              : fwd_ilv_kernel<128, N::NW, N::BN, false, false>,
+                                     N::BM, N::NW * 64, a);
+  return launch_fwd_grid<uint16_t>(a.causal ? fwd_ilv_kernel<128, W::NW, W::BN, true, false>
+                                            : fwd_ilv_kernel<128, W::NW, W::BN, false, false>,
+                                   W::BM, W::NW * 64, a);
 }
 #undef XATTN_PICK
 

@@ -70,16 +70,14 @@ struct DecodeArgs {
 // Longest key sequence the block-sparse forward walks (its tile list holds 8191 tiles of 64).
 constexpr int kMaxSparseKeys = 8191 * 64;
 
-// Decode path: rows = T * (Hq/Hkv) (token, head) pairs per KV head.  Up to XATTN_DEC_VALU_ROWS
+// Decode path: rows = T * (Hq/Hkv) (token, head) pairs per KV head.  Up to kDecValuRows
 // rows the vector-ALU kernel (one partial per workgroup), above it the matrix-core kernel
 // (one partial per wave: four per workgroup; 32 rows per workgroup) up to kDecMaxRows.  Measured on the 2 GiB decode
 // cache: at 4 and 8 rows the vector-ALU kernel is 3-6% faster, at 16 rows the matrix-core one
 // 1.7x (its P V no longer scales with the row count).
-#ifndef XATTN_DEC_VALU_ROWS
-#define XATTN_DEC_VALU_ROWS 8
-#endif
+constexpr int kDecValuRows = 8;
 constexpr int kDecMaxRows = 4096;
-inline bool decode_uses_mma(int T, int g) { return T * g > XATTN_DEC_VALU_ROWS; }
+inline bool decode_uses_mma(int T, int g) { return T * g > kDecValuRows; }
 inline int decode_partials_per_split(int T, int g) { return decode_uses_mma(T, g) ? 4 : 1; }
 
 hipError_t launch_fwd(const FwdArgs& a);
