@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 thread_local char g_err[512] = "";
 
 attn_status_t fail(attn_status_t s, const char* fmt, ...) {
@@ -188,7 +188,15 @@ int bwd_npad(int N) { return (N + 63) / 64 * 64; }
 static size_t bwd_stats_bytes(int B, int Hq, int N) {
   return align_up(2 * (size_t)B * Hq * bwd_npad(N) * sizeof(float), 256);
 }
-// fp32 partial dK/dV of the split grouped-query backward (see kBwdSplitGrid), after the statistics.
+static size_t bwd_varlen_stats_bytes(int B, int Hq, int total_q) {
+  return align_up(2 * (size_t)Hq * ((size_t)total_q + 64 * (size_t)B) * sizeof(float), 256);
+}
+// One word per wave of each dQ workgroup of 128 queries (its "walk again with the exact D"
+// flag), after the statistics; the packed layout bounds the longest sequence by the total.
+static size_t bwd_flag_bytes(int B, int Hq, int max_q) {
+  return align_up((size_t)B * Hq * (size_t)((max_q + 127) / 128) * 4 * sizeof(unsigned), 256);
+}
+// fp32 partial dK/dV of the split grouped-query backward (see kBwdSplitGrid), after the flags.
 static size_t bwd_part_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (!xattn::bwd_split_possible(B, Hq, Hkv, N) || d <= 0) return 0;
   return align_up(4 * (size_t)B * Hkv * N * d * sizeof(float), 256);
@@ -196,12 +204,12 @@ static size_t bwd_part_bytes(int B, int Hq, int Hkv, int N, int d) {
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (B <= 0 || Hq <= 0 || N <= 0) return 0;
-  return bwd_stats_bytes(B, Hq, N) + bwd_part_bytes(B, Hq, Hkv, N, d);
+  return bwd_stats_bytes(B, Hq, N) + bwd_flag_bytes(B, Hq, N) + bwd_part_bytes(B, Hq, Hkv, N, d);
 }
 
 size_t attn_bwd_varlen_workspace_bytes(int B, int Hq, int total_q) {
   if (B <= 0 || Hq <= 0 || total_q < 0) return 0;
-  return align_up(2 * (size_t)Hq * ((size_t)total_q + 64 * (size_t)B) * sizeof(float), 256);
+  return bwd_varlen_stats_bytes(B, Hq, total_q) + bwd_flag_bytes(B, Hq, total_q);
 }
 
 // Shared by attn_bwd (dense, cu_q == nullptr) and attn_bwd_varlen (packed).
@@ -235,12 +243,14 @@ static attn_status_t bwd_impl(const void* q, const void* k, const void* v, const
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const long long stride = cu_q ? (long long)Nq + 64LL * B : bwd_npad(Nq);
   const long long half = cu_q ? (long long)Hq * stride : (long long)B * Hq * stride;
+  const size_t stats_bytes = cu_q ? bwd_varlen_stats_bytes(B, Hq, Nq) : bwd_stats_bytes(B, Hq, Nq);
+  unsigned* flags = (unsigned*)((char*)workspace + stats_bytes);
   float* part = nullptr;  // dense causal grouped-query backward with few key blocks: split dK/dV
   if (!cu_q && causal && bwd_part_bytes(B, Hq, Hkv, Nq, d) > 0)
-    part = (float*)((char*)workspace + bwd_stats_bytes(B, Hq, Nq));
+    part = (float*)((char*)workspace + stats_bytes + bwd_flag_bytes(B, Hq, Nq));
   xattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, B, Hq, Hkv, Nq, Nk, max_q, max_k, d,
                    causal ? 1 : 0, scale, (float*)workspace, stride, half, (hipStream_t)stream, block_mask, mask_sb,
-                   mask_sh, part};
+                   mask_sh, part, flags};
   return from_hip(xattn::launch_bwd(a), "attn_bwd launch");
 }
 

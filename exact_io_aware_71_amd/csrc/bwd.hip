@@ -579,14 +579,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(const float* __restri
 constexpr int dq_vslot(int L, int g) { return 1 + g * (L - 2) / 3; }
 
 // Also forms the per-row statistics the dK/dV kernel reads (it runs first): LSE2 = LSE*log2(e)
-// and D = rowsum(dO * O) for its 128 rows, padding rows up to the sequence's multiple of 64
-// getting +inf and 0.
-template <int D, bool CAUSAL, bool SPARSE>
+// and D for its 128 rows, padding rows up to the sequence's multiple of 64 getting +inf and 0.
+//
+// D.  dS = P (dP - D) takes D = rowsum(dO * O), known before the key walk, but O is stored in
+// bf16 and that D carries O's rounding, up to 2^-9 relative.  On the key that dominates a row
+// dP - D nearly cancels, and there the rounding moves dQ_i by about scale * dD_i * sum_j P_ij K_j,
+// as large as dQ_i itself once the row's largest probability nears 1 (relative error about
+// 2^-9 / sqrt(1 - P_max)).  Each wave therefore notes the largest probability it meets (one
+// v_max3 per two) and flags itself when that exceeds 1/2.  A second launch (REDO) exits at once
+// in workgroups without a flagged wave; in the others it forms D from its definition,
+// sum_j P_ij dP_ij (fp32), in a walk that computes only S and dP, writes it for the dK/dV kernel
+// (launched after both), and walks the key tiles once more, last first (the last two are still
+// in LDS), for dQ with that D.  On N(0,1) inputs only the first rows of a causal sequence (few
+// keys) trigger it; rows whose keys all fit one tile get the exact D in the first launch.
+template <int D, bool CAUSAL, bool SPARSE, bool REDO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const float* __restrict__ lse, float* __restrict__ stats,
     const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, SeqGeo geo, BlockMask bm, long long stat_stride,
-    long long stat_half, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv) {
+    long long stat_half, float scale, float scale_log2, int n_qtiles, int BH, int Hq, int Hkv,
+    unsigned* __restrict__ flags) {
   constexpr int NW = 4, BM = NW * 32, BN = kBwdBK, KB = BN / 32, DC = D / 16, DB = D / 32;
   static_assert(!SPARSE || BM == kSparseBlock, "a workgroup's queries form one mask block");
   using T = BwdTile<D>;
@@ -604,6 +616,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const SeqRows sr = seq_rows(geo, b, hq, Hq, hk, Hkv);
   const int Nq = sr.lq, Nk = sr.lk;
   if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
+  if constexpr (REDO) {  // one flag word per wave of the first launch
+    const u32x4 f = *reinterpret_cast<const u32x4*>(flags + 4 * (size_t)blockIdx.x);
+    if (__builtin_amdgcn_readfirstlane(f[0] | f[1] | f[2] | f[3]) == 0) return;
+  }
   const int qd0 = qw0 + (Nk - Nq), kmax = qi + (Nk - Nq);  // causal: query i sees keys <= i + Nk - Nq
   const uint16_t* qp = q + sr.q * D;
   const uint16_t* kp = k + sr.k * D;
@@ -619,7 +635,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (qi < Nq) {
       a = ld_global16(qp + (size_t)qi * D + 16 * c + 8 * h32);
       g = ld_global16(dop + (size_t)qi * D + 16 * c + 8 * h32);
-      w = ld_global16(op + (size_t)qi * D + 16 * c + 8 * h32);
+      if constexpr (!REDO) w = ld_global16(op + (size_t)qi * D + 16 * c + 8 * h32);
     }
     qreg[c] = as_bf16x8(a);
     doreg[c] = as_bf16x8(g);
@@ -630,14 +646,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // row's features sits in lane qi + 32).  Rows past the sequence up to its multiple of 64 are
   // padding (+inf, 0) so that the dK/dV kernel's 64-row tile copies need no bounds check.
   const float dtot = sum_xor32(dsum);
-  const float dl = qi < Nq ? dtot : 0.f;
+  float* st = stats + stat_row(geo, stat_stride, b, hq, Hq);
+  float dl = qi < Nq ? dtot : 0.f;  // D_O = rowsum(dO * O); the redo launch forms the exact D
   const float lse2 = qi < Nq ? lse[sr.q + qi] * kLog2e : INFINITY;
-  {
-    float* st = stats + stat_row(geo, stat_stride, b, hq, Hq);
-    if (h32 == 0 && qi < (Nq + 63) / 64 * 64) {
-      st[qi] = lse2;
-      st[stat_half + qi] = dl;
-    }
+  if (!REDO && h32 == 0 && qi < (Nq + 63) / 64 * 64) {
+    st[qi] = lse2;
+    st[stat_half + qi] = dl;
   }
 
   f32x16 dq_acc[DB];
@@ -704,6 +718,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   uint16_t* dqp = dq + sr.q * D;
+  if (!REDO && lane == 0 && (ntiles == 0 || (!SPARSE && ntiles == 1))) flags[4 * blockIdx.x + wave] = 0u;
   if (ntiles == 0) {  // no key for any row of the tile: dQ = 0
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -748,6 +763,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return join_tr(ds_read_tr16(smem + ofs.v[db][0] + roff), ds_read_tr16(smem + ofs.v[db][1] + roff));
     }
   };
+  if constexpr (REDO) {
+    // D_i = sum_j P_ij dP_ij over the rows' keys, from S and dP alone (tile t+1 copied during
+    // tile t), then dQ with it, walking the tiles last first: the last two are still in the two
+    // stages, and tile t-2 is copied into the stage of tile t during tile t-1.
+    float dpart = 0.f;
+    auto tile_sdp = [&](auto kc, int t0, f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
+      constexpr int kb = decltype(kc)::value;
+      static_for<DC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const bf16x8 ak = opnd(std::integral_constant<int, (2 * kb) * DC + c>{});
+        const bf16x8 av = opnd(std::integral_constant<int, (2 * kb + 1) * DC + c>{});
+        if constexpr (c == 0) {
+          sv = mfma32(ak, qreg[0], f32x16{});
+          dpv = mfma32(av, doreg[0], f32x16{});
+        } else {
+          sv = mfma32(ak, qreg[c], sv);
+          dpv = mfma32(av, doreg[c], dpv);
+        }
+      });
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        const float pr = fast_exp2(fmaf(sv[r], scale_log2, -lse2));
+        sv[r] = (kj >= Nk || (CAUSAL && kj > kmax)) ? 0.f : pr;
+      }
+    };
+    for (int t = 0; t < ntiles; ++t) {
+      const int t0 = kt(t) * BN;
+      if (t + 1 < ntiles) copy_tile(kt(t + 1), (t + 1) & 1);
+      if (!(CAUSAL && t0 > qd0 + 31)) {
+        static_for<2>([&](auto kc) {
+          f32x16 sv, dpv;
+          tile_sdp(kc, t0, sv, dpv);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dpart = fmaf(sv[r], dpv[r], dpart);
+        });
+      }
+      wait_vmem();
+      lds_barrier();
+      if (t + 1 < ntiles) ofs.toggle(STAGE);
+    }
+    dl = qi < Nq ? sum_xor32(dpart) : 0.f;
+    if (h32 == 0 && qi < Nq) st[stat_half + qi] = dl;
+    // ofs is on the stage of tile ntiles-1 and tile ntiles-2 is still in the other stage.  At
+    // tile t <= ntiles-2 the stage of tile t+1 is free again and takes tile t-1.
+    for (int t = ntiles - 1; t >= 0; --t) {
+      const int t0 = kt(t) * BN;
+      if (t <= ntiles - 2 && t >= 1) copy_tile(kt(t - 1), (t - 1) & 1);
+      if (!(CAUSAL && t0 > qd0 + 31)) {
+        bf16x8 dsv[2][2];
+        static_for<2>([&](auto kc) {
+          constexpr int kb = decltype(kc)::value;
+          f32x16 sv, dpv;
+          tile_sdp(kc, t0, sv, dpv);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dpv[r] = sv[r] * (dpv[r] - dl);
+          dsv[kb][0] = pack8(dpv, 0);
+          dsv[kb][1] = pack8(dpv, 1);
+        });
+        static_for<4 * DB>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value, kb = jj / (2 * DB), sh = (jj % (2 * DB)) / DB, db = jj % DB;
+          dq_acc[db] = mfma32(dsv[kb][sh], opnd(std::integral_constant<int, PE + jj>{}), dq_acc[db]);
+        });
+      }
+      wait_vmem();  // tile t-1 has landed
+      lds_barrier();
+      ofs.toggle(STAGE);
+    }
+  } else
   if (!SPARSE && ntiles == 1) {
     // The tile's keys are all the keys of these rows: D = sum_j P_ij dP_ij, its definition,
     // replaces rowsum(dO * O) here and in the statistics the dK/dV kernel reads.  O is stored in
@@ -782,7 +866,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dpart += pr * dpv[kb][r];
       }
     const float dex = sum_xor32(dpart);
-    if (h32 == 0 && qi < Nq) stats[stat_row(geo, stat_stride, b, hq, Hq) + stat_half + qi] = dex;
+    if (h32 == 0 && qi < Nq) st[stat_half + qi] = dex;
     bf16x8 dsv[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -795,7 +879,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       constexpr int jj = decltype(jc)::value, kb = jj / (2 * DB), sh = (jj % (2 * DB)) / DB, db = jj % DB;
       dq_acc[db] = mfma32(dsv[kb][sh], opnd(std::integral_constant<int, PE + jj>{}), dq_acc[db]);
     });
-  } else
+  } else {
+  float pmx = 0.f;  // largest probability this lane meets (first launch)
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = kt(t) * BN, kn = kt(t + 1);
     if (CAUSAL && t0 > qd0 + 31) {
@@ -823,6 +908,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         asm volatile("" : "+v"(x[4 * g]), "+v"(x[4 * g + 1]), "+v"(x[4 * g + 2]), "+v"(x[4 * g + 3]));
       };
       auto ds_group = [&](const f32x16& p, f32x16& dp, bf16x8 (&ds)[2], int g) __attribute__((always_inline)) {
+        if constexpr (!REDO) pmx = fmaxf(fmaxf(pmx, p[4 * g]), fmaxf(fmaxf(p[4 * g + 1], p[4 * g + 2]), p[4 * g + 3]));
 #pragma unroll
         for (int e = 0; e < 4; ++e) dp[4 * g + e] = p[4 * g + e] * (dp[4 * g + e] - dl);
         if (g % 2 == 1) {
@@ -871,6 +957,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vmem();  // tile t+1 has landed
     lds_barrier();
   }
+  if constexpr (!REDO) {
+    // The wave's flag for the redo launch (rows past the sequence have P = 0, so a flagged
+    // lane holds a real row).
+    const bool dom = __builtin_amdgcn_ballot_w64(pmx > 0.5f) != 0;
+    if (lane == 0) flags[4 * blockIdx.x + wave] = dom ? 1u : 0u;
+  }
+  }
   // C layout: lane holds feature db*32 + l32 of queries qw0 + 8(r/4) + 4*h32 + r%4.
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -892,11 +985,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   // dQ first: it also writes the row statistics the dK/dV kernel reads.
   const int n_qt = (a.max_q + 127) / 128;
   if (n_qt > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(n_qt * BH), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE, false>), dim3(n_qt * BH), dim3(256), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o, a.lse,
                        a.stats, (const uint16_t*)a.dout, (uint16_t*)a.dq, geo, bm, a.stat_stride, a.stat_half, a.scale,
-                       sl2, n_qt, BH, a.Hq, a.Hkv);
+                       sl2, n_qt, BH, a.Hq, a.Hkv, a.flags);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // Workgroups that met a probability above 1/2 walk again for dQ with the exact D; the
+    // others exit at once.
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE, true>), dim3(n_qt * BH), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o, a.lse,
+                       a.stats, (const uint16_t*)a.dout, (uint16_t*)a.dq, geo, bm, a.stat_stride, a.stat_half, a.scale,
+                       sl2, n_qt, BH, a.Hq, a.Hkv, a.flags);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int n_kt = (a.max_k + 127) / 128;

@@ -39,6 +39,7 @@ struct BwdArgs {
   const unsigned char* block_mask;  // optional [B, Hq, ceil(N/128), ceil(N/128)] keep bytes (dense layout only)
   long long mask_sb, mask_sh;       // batch and head strides of block_mask in bytes
   float* part;                      // fp32 [2 (dV, dK)][2 halves][B*Hkv*N][d] for the split dK/dV, or null
+  unsigned* flags;                  // [ceil(max_q/128) * B * Hq][4]: per dQ wave, walk again with the exact D
 };
 
 // Causal grouped-query backward with few key blocks: when the dK/dV grid has fewer workgroups

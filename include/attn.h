@@ -134,13 +134,16 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void*
                               int Hkv, int total_q, int total_k, int max_seqlen_q, int d,
                               attn_dtype_t dtype, int causal, float scale, void* stream);
 
-/* Bytes of device workspace attn_bwd needs: fp32 per-row statistics (LSE * log2(e) and
- * D = rowsum(dO * O)) for every query row padded to a multiple of 64, i.e.
- * 2 * B * Hq * roundup(N, 64) * 4 bytes, rounded up to 256; plus, when Hq/Hkv is even and
- * above 1 and B * Hkv * ceil(N/128) < 512, 4 * B * Hkv * N * d * 4 bytes (rounded up to 256)
- * of fp32 partial dK/dV: a causal backward of such a shape splits each group's query heads
- * over two dK/dV workgroups (the causal work of the key blocks differs too much for one round
- * of workgroups) and adds their two partial sums in a fixed order. */
+/* Bytes of device workspace attn_bwd needs:
+ *   - fp32 per-row statistics (LSE * log2(e) and D, see attn_bwd) for every query row padded
+ *     to a multiple of 64: 2 * B * Hq * roundup(N, 64) * 4 bytes, rounded up to 256;
+ *   - one 4-byte flag per wave of 32 query rows, B * Hq * ceil(N/128) * 4 * 4 bytes rounded up
+ *     to 256 (a wave that meets a probability above 1/2 asks for D from its definition);
+ *   - when Hq/Hkv is even and above 1 and B * Hkv * ceil(N/128) < 512, 4 * B * Hkv * N * d * 4
+ *     bytes (rounded up to 256) of fp32 partial dK/dV: a causal backward of such a shape splits
+ *     each group's query heads over two dK/dV workgroups (the causal work of the key blocks
+ *     differs too much for one round of workgroups) and adds their two partial sums in a fixed
+ *     order. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /*
@@ -153,6 +156,11 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  *                                    aligned; contents on entry are ignored
  * Supported: BF16, d in {64, 128}.  Grouped-query heads ([OPT] §5.3, kv = h / (Hq/Hkv)): dk and
  * dv of a KV head are the sums of the gradients of the Hq/Hkv query heads sharing it.
+ * D_i = sum_j P_ij dP_ij enters dS = P (dP - D).  It is taken as rowsum(dO * O) from the stored
+ * O, except for the 128-query blocks that hold a row whose largest probability exceeds 1/2:
+ * there the bf16 rounding of O would dominate the nearly cancelling dP - D of the dominant key,
+ * so a second dQ launch forms D from its definition and computes dQ of the block again with it
+ * (dK and dV use that D too).
  * Deterministic (no atomics).
  */
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -180,7 +188,8 @@ attn_status_t attn_bwd_blocksparse(const void* q, const void* k, const void* v, 
 
 /* Bytes of device workspace attn_bwd_varlen needs: the same two fp32 statistics per query
  * row, each sequence padded by up to 64 rows, i.e. 2 * Hq * (total_q + 64 * B) * 4 bytes,
- * rounded up to 256. */
+ * rounded up to 256, then the flags of attn_bwd for B * Hq * ceil(total_q/128) workgroups
+ * (B * Hq * ceil(total_q/128) * 16 bytes, rounded up to 256). */
 size_t attn_bwd_varlen_workspace_bytes(int B, int Hq, int total_q);
 
 /*

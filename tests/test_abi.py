@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     assert lib.attn_status_str(0) == b"ok"
     assert lib.attn_status_str(3) == b"workspace too small"
 
@@ -110,21 +110,30 @@ def bwd(ws=P, ws_bytes=1 << 30, Hq=2, Hkv=2, d=128, dt=1, scale=0.1, dq=P):
                         ws, ws_bytes, None)
 
 
+def r256(x):
+    return (x + 255) // 256 * 256
+
+
+def flags(B, Hq, N):
+    """One 4-byte flag per wave (four per 128-query dQ workgroup), rounded up to 256 bytes."""
+    return r256(B * Hq * ((N + 127) // 128) * 4 * 4)
+
+
 def test_bwd_workspace_split():
     """Causal grouped-query backward with few key blocks splits each group's query heads over two
-    dK/dV workgroups; their fp32 partial sums follow the statistics in the workspace."""
+    dK/dV workgroups; their fp32 partial sums follow the statistics and the dQ flags."""
     stats = 2 * 1 * 32 * 4096 * 4
     part = 4 * 1 * 8 * 4096 * 128 * 4            # [dV, dK] x [two halves] x B*Hkv*N x d, fp32
-    assert lib.attn_bwd_workspace_bytes(1, 32, 8, 4096, 128) == stats + part
-    assert lib.attn_bwd_workspace_bytes(1, 32, 32, 4096, 128) == stats             # no groups
-    assert lib.attn_bwd_workspace_bytes(1, 6, 2, 4096, 128) == 2 * 6 * 4096 * 4    # odd group size
-    assert lib.attn_bwd_workspace_bytes(4, 32, 8, 4096, 128) == 2 * 4 * 32 * 4096 * 4  # 1024 key blocks
+    assert lib.attn_bwd_workspace_bytes(1, 32, 8, 4096, 128) == stats + flags(1, 32, 4096) + part
+    assert lib.attn_bwd_workspace_bytes(1, 32, 32, 4096, 128) == stats + flags(1, 32, 4096)  # no groups
+    assert lib.attn_bwd_workspace_bytes(1, 6, 2, 4096, 128) == 2 * 6 * 4096 * 4 + flags(1, 6, 4096)  # odd group
+    assert lib.attn_bwd_workspace_bytes(4, 32, 8, 4096, 128) == 2 * 4 * 32 * 4096 * 4 + flags(4, 32, 4096)
 
 
 def test_bwd_validation():
     need = lib.attn_bwd_workspace_bytes(1, 2, 2, 64, 128)
-    assert need == 1024                      # LSE2 and D rows, padded to 64 queries
-    assert lib.attn_bwd_workspace_bytes(1, 2, 2, 65, 128) == 2 * 2 * 128 * 4
+    assert need == 1024 + 256                # LSE2 and D rows padded to 64 queries; dQ flags
+    assert lib.attn_bwd_workspace_bytes(1, 2, 2, 65, 128) == 2 * 2 * 128 * 4 + flags(1, 2, 65)
     assert bwd(dq=None) == 1
     assert bwd(Hq=3, Hkv=2) == 1           # Hq must be a multiple of Hkv
     assert bwd(dt=0) == 2
@@ -136,7 +145,7 @@ def test_bwd_validation():
 
 def test_bwd_varlen_validation():
     need = lib.attn_bwd_varlen_workspace_bytes(3, 4, 100)
-    assert need == 2 * 4 * (100 + 64 * 3) * 4 // 256 * 256 + (256 if (2 * 4 * (100 + 192) * 4) % 256 else 0)
+    assert need == r256(2 * 4 * (100 + 64 * 3) * 4) + flags(3, 4, 100)
 
     def bv(cu_q=P, cu_k=P, ws=P, ws_bytes=need, max_q=40, max_k=50, total_k=200, dt=1):
         return lib.attn_bwd_varlen(P, P, P, P, P, P, P, P, P, cu_q, cu_k, 3, 4, 2, 100, total_k, max_q, max_k, 128, dt,

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from synth import default_scale, make_prefill
-from tests._util import to_dev, to_host64
+from tests._util import Guarded, to_dev, to_host64
 from tests.test_gpu_kv_varlen import check_rows
 
 pytestmark = pytest.mark.gpu
@@ -22,8 +22,10 @@ def run_sparse(lib, inp, mask, causal, scale):
     import torch
     q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
     m = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda()
-    o, lse = lib.attn_fwd_blocksparse(q, k, v, m, causal, scale)
-    torch.cuda.synchronize()
+    g = Guarded()
+    o, lse = g.like(q), g.empty(q.shape[:3], torch.float32)
+    lib.attn_fwd_blocksparse(q, k, v, m, causal, scale, o=o, lse=lse)
+    g.check("attn_fwd_blocksparse")
     return to_host64(o), lse.cpu().numpy().astype(np.float64)
 
 
@@ -99,9 +101,14 @@ def run_sparse_fwd_bwd(lib, inp, mask, causal, scale):
     q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "dout"))
     m = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda()
     o, lse = lib.attn_fwd_blocksparse(q, k, v, m, causal, scale)
-    grads = lib.attn_bwd_blocksparse(q, k, v, o, lse, do, m, causal, scale)
-    torch.cuda.synchronize()
-    return [to_host64(g) for g in grads]
+    g = Guarded()
+    grads = (g.like(q), g.like(k), g.like(v))
+    B, Hq, N, d = q.shape
+    ws = g.empty((max(lib.attn_bwd_workspace_bytes(B, Hq, k.shape[1], N, d), 1),), torch.uint8)
+    lib.attn_bwd_blocksparse(q, k, v, o, lse, do, m, causal, scale, dq=grads[0], dk=grads[1], dv=grads[2],
+                             workspace=ws)
+    g.check("attn_bwd_blocksparse")
+    return [to_host64(t) for t in grads]
 
 
 @pytest.mark.parametrize("N", [300, 1000])

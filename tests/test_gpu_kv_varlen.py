@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from synth import default_scale, make_prefill, make_varlen
-from tests._util import BWD_REL_L2, assert_fwd_ok, fwd_errors, rel_l2, to_dev, to_host64
+from tests._util import BWD_REL_L2, Guarded, assert_fwd_ok, fwd_errors, rel_l2, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -28,8 +28,10 @@ def check_rows(o, lse, o_ref, lse_ref, tag):
 def run_kv(lib, inp, causal, scale):
     import torch
     q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
-    o, lse = lib.attn_fwd_kv(q, k, v, causal, scale)
-    torch.cuda.synchronize()
+    g = Guarded()
+    o, lse = g.like(q), g.empty(q.shape[:3], torch.float32)
+    lib.attn_fwd_kv(q, k, v, causal, scale, o=o, lse=lse)
+    g.check("attn_fwd_kv")
     return to_host64(o), lse.cpu().numpy().astype(np.float64)
 
 
@@ -109,8 +111,10 @@ def run_varlen(lib, x, causal, scale):
     q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
     cq, ck = torch.from_numpy(x["cu_q"]).cuda(), torch.from_numpy(x["cu_k"]).cuda()
     max_q = int(np.diff(x["cu_q"]).max())
-    o, lse = lib.attn_fwd_varlen(q, k, v, cq, ck, max_q, causal, scale)
-    torch.cuda.synchronize()
+    g = Guarded()
+    o, lse = g.like(q), g.empty(q.shape[:2], torch.float32)
+    lib.attn_fwd_varlen(q, k, v, cq, ck, max_q, causal, scale, o=o, lse=lse)
+    g.check("attn_fwd_varlen")
     return to_host64(o), lse.cpu().numpy().astype(np.float64)
 
 
@@ -168,9 +172,13 @@ def run_varlen_fwd_bwd(lib, x, causal, scale):
     cq, ck = torch.from_numpy(x["cu_q"]).cuda(), torch.from_numpy(x["cu_k"]).cuda()
     max_q, max_k = int(np.diff(x["cu_q"]).max()), int(np.diff(x["cu_k"]).max())
     o, lse = lib.attn_fwd_varlen(q, k, v, cq, ck, max_q, causal, scale)
-    grads = lib.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, max_q, max_k, causal, scale)
-    torch.cuda.synchronize()
-    return [to_host64(g) for g in grads]
+    g = Guarded()
+    grads = (g.like(q), g.like(k), g.like(v))
+    ws = g.empty((lib.attn_bwd_varlen_workspace_bytes(len(x["cu_q"]) - 1, q.shape[0], q.shape[1]),), torch.uint8)
+    lib.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, max_q, max_k, causal, scale, dq=grads[0], dk=grads[1],
+                        dv=grads[2], workspace=ws)
+    g.check("attn_bwd_varlen")
+    return [to_host64(t) for t in grads]
 
 
 @pytest.mark.parametrize("case", sorted(VARLEN_CASES))

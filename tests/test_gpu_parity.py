@@ -12,16 +12,19 @@ import pytest
 
 import oracle
 from synth import WORKLOADS, default_scale, make_decode, make_prefill
-from tests._util import assert_fwd_ok, fwd_errors, rel_l2, to_dev, to_host64, BWD_REL_L2
+from tests._util import Guarded, assert_fwd_ok, fwd_errors, rel_l2, to_dev, to_host64, BWD_REL_L2
 
 pytestmark = pytest.mark.gpu
 
 
 def run_fwd(lib, inp, causal, scale):
-    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
-    o, lse = lib.attn_fwd(q, k, v, causal, scale)
+    """Outputs in guarded buffers: a write outside O or LSE fails the test."""
     import torch
-    torch.cuda.synchronize()
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    g = Guarded()
+    o, lse = g.like(q), g.empty(q.shape[:3], torch.float32)
+    lib.attn_fwd(q, k, v, causal, scale, o=o, lse=lse)
+    g.check("attn_fwd")
     return to_host64(o), lse.cpu().numpy().astype(np.float64)
 
 
@@ -47,7 +50,20 @@ def test_fwd_batched_prefill(gpu_lib, seed_off):
     assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), "prefill")
 
 
-def sample_rows(N, seed, extra=120):
+_LONG_INPUTS = {}
+
+
+def long_inputs(name):
+    """Seeded inputs of a long-prefill workload, drawn once per module (the N = 16384 draw
+    takes seconds)."""
+    if name not in _LONG_INPUTS:
+        _LONG_INPUTS.clear()
+        w = WORKLOADS[name]
+        _LONG_INPUTS[name] = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed, qk_mult=w.qk_mult)
+    return _LONG_INPUTS[name]
+
+
+def sample_rows(N, seed, extra=248):
     fixed = {0, 1, 63, 64, 127, 128, N // 2, N - 1}
     rng = np.random.default_rng(seed)
     return np.array(sorted(fixed | set(rng.integers(0, N, extra).tolist())))
@@ -57,12 +73,28 @@ def sample_rows(N, seed, extra=120):
 @pytest.mark.parametrize("causal", [True, False])
 def test_fwd_long_prefill_sampled_rows(gpu_lib, name, causal):
     w = WORKLOADS[name]
-    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed, qk_mult=w.qk_mult)
+    inp = long_inputs(name)
     scale = default_scale(w.d)
     o, lse = run_fwd(gpu_lib, inp, causal, scale)
     rows = sample_rows(w.N, w.seed + int(causal))
     o_ref, lse_ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], scale, causal, rows)
     assert_fwd_ok(fwd_errors(o[:, :, rows], o_ref, lse[:, :, rows], lse_ref), name)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("h", [0, 31])
+def test_fwd_long16k_full_heads(gpu_lib, causal, h):
+    """Long prefill at N = 16384 (logits x2): every element of O and every LSE row of two whole
+    heads, causal and not, besides the 256 sampled rows of every head above (the oracle holds
+    the 16384 x 16384 score matrix of one head at a time)."""
+    w = WORKLOADS["long16k"]
+    print(f"long16k full head h={h} causal={causal}", flush=True)
+    inp = long_inputs("long16k")
+    scale = default_scale(w.d)
+    o, lse = run_fwd(gpu_lib, inp, causal, scale)
+    sl = {kk: inp[kk][:, h:h + 1] for kk in ("q", "k", "v")}
+    o_ref, lse_ref = oracle.forward(sl["q"], sl["k"], sl["v"], scale, causal)
+    assert_fwd_ok(fwd_errors(o[:, h:h + 1], o_ref, lse[:, h:h + 1], lse_ref), f"h{h} causal={causal}")
 
 
 def test_fwd_long4k_every_element(gpu_lib):
@@ -228,7 +260,22 @@ def decode_inputs():
     return w, make_decode(w.B, w.Hq, w.Hkv, w.L, w.d, seed=w.seed)
 
 
-@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+def test_decode_full_size_every_sequence(gpu_lib, decode_inputs):
+    """The decode workload with the automatic split count: all 64 sequences against the oracle."""
+    import torch
+    w, inp = decode_inputs
+    scale = default_scale(w.d)
+    q, kc, vc = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = gpu_lib.attn_decode(q, kc, vc, scale, num_splits=0)
+    torch.cuda.synchronize()
+    o, lse = to_host64(o), lse.cpu().numpy().astype(np.float64)
+    del q, kc, vc
+    torch.cuda.empty_cache()
+    o_ref, lse_ref = oracle.decode(inp["q"], inp["k"], inp["v"], scale)
+    assert_fwd_ok(fwd_errors(o, o_ref, lse, lse_ref), "decode every sequence")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
 def test_decode_full_size_sampled_batches(gpu_lib, decode_inputs, splits):
     import torch
     w, inp = decode_inputs
@@ -249,13 +296,18 @@ def test_decode_full_size_sampled_batches(gpu_lib, decode_inputs, splits):
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_small(gpu_lib, L, g, d):
     import torch
+    g_ = g
     inp = make_decode(3, 2 * g, 2, L, d, seed=L + g + d)
     scale = default_scale(d)
+    q, kc, vc = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
     for splits in (0, 2, 7):
-        o, lse = gpu_lib.attn_decode(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), scale, num_splits=splits)
-        torch.cuda.synchronize()
+        g = Guarded()
+        o, lse = g.like(q), g.empty(q.shape[:2], torch.float32)
+        ws = g.empty((gpu_lib.attn_decode_workspace_bytes(3, 2 * g_, 2, L, d, splits),), torch.uint8)
+        gpu_lib.attn_decode(q, kc, vc, scale, num_splits=splits, o=o, lse=lse, workspace=ws)
+        g.check(f"decode L={L} g={g_} s={splits}")
         o_ref, lse_ref = oracle.decode(inp["q"], inp["k"], inp["v"], scale)
-        assert_fwd_ok(fwd_errors(to_host64(o), o_ref, lse.cpu().numpy(), lse_ref), f"L={L} g={g} s={splits}")
+        assert_fwd_ok(fwd_errors(to_host64(o), o_ref, lse.cpu().numpy(), lse_ref), f"L={L} g={g_} s={splits}")
 
 
 def test_decode_matches_forward_single_row(gpu_lib):
@@ -279,9 +331,13 @@ def test_decode_per_sequence_lengths(gpu_lib, d, splits):
     inp = make_decode(len(lens), 8, 2, L, d, seed=5 + d)
     scale = default_scale(d)
     sl = torch.from_numpy(lens).cuda()
-    o, lse = gpu_lib.attn_decode_varlen(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), sl, scale,
-                                        num_splits=splits)
-    torch.cuda.synchronize()
+    q = to_dev(inp["q"])
+    g = Guarded()
+    o, lse = g.like(q), g.empty(q.shape[:2], torch.float32)
+    ws = g.empty((gpu_lib.attn_decode_workspace_bytes(len(lens), 8, 2, L, d, splits),), torch.uint8)
+    gpu_lib.attn_decode_varlen(q, to_dev(inp["k"]), to_dev(inp["v"]), sl, scale, num_splits=splits, o=o, lse=lse,
+                               workspace=ws)
+    g.check(f"decode varlen d={d} splits={splits}")
     o_ref, lse_ref = oracle.decode(inp["q"], inp["k"], inp["v"], scale, seqlens=lens)
     o_h, lse_h = to_host64(o), lse.cpu().numpy().astype(np.float64)
     assert np.all(o_h[0] == 0.0) and np.all(lse_h[0] == -np.inf)
@@ -290,11 +346,16 @@ def test_decode_per_sequence_lengths(gpu_lib, d, splits):
 
 # ----------------------------------------------------------------------------- backward
 def run_fwd_bwd(lib, inp, causal, scale):
+    """Gradients and the backward workspace in guarded buffers."""
     import torch
     q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "dout"))
     o, lse = lib.attn_fwd(q, k, v, causal, scale)
-    dq, dk, dv = lib.attn_bwd(q, k, v, o, lse, do, causal, scale)
-    torch.cuda.synchronize()
+    g = Guarded()
+    dq, dk, dv = g.like(q), g.like(k), g.like(v)
+    B, Hq, N, d = q.shape
+    ws = g.empty((max(lib.attn_bwd_workspace_bytes(B, Hq, k.shape[1], N, d), 1),), torch.uint8)
+    lib.attn_bwd(q, k, v, o, lse, do, causal, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+    g.check("attn_bwd")
     return [to_host64(t) for t in (dq, dk, dv)]
 
 
@@ -311,17 +372,69 @@ def check_bwd(grads, inp, scale, causal, heads=None, tag=""):
         assert err <= BWD_REL_L2, (tag, name, err)
 
 
-@pytest.mark.parametrize("seed_off", [0, 1])
-def test_bwd_training_step_sampled_heads(gpu_lib, seed_off):
+@pytest.fixture(scope="module")
+def train_grads(gpu_lib):
+    """The training-step workload (B=2, H=16, N=4096, d=128, causal): GPU forward, then GPU
+    backward, once for the module."""
     w = WORKLOADS["train"]
-    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed + seed_off, with_dout=True)
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed, with_dout=True)
+    return w, inp, run_fwd_bwd(gpu_lib, inp, True, default_scale(w.d))
+
+
+@pytest.mark.parametrize("b", [0, 1])
+def test_bwd_training_step_every_head(gpu_lib, train_grads, b):
+    """Every head of the training step: dQ, dK, dV of each (b, h) against the oracle's fp64
+    backward (a head's gradients depend only on its own Q, K, V and dO)."""
+    w, inp, grads = train_grads
+    scale = default_scale(w.d)
+    for h in range(w.Hq):
+        sub = {x: inp[x][b:b + 1, h:h + 1] for x in inp}
+        check_bwd([g[b:b + 1, h:h + 1] for g in grads], sub, scale, True, tag=f"b{b}h{h}")
+
+
+def test_bwd_training_step_other_seed(gpu_lib):
+    """The training-step shape on a second seed: two heads per batch row."""
+    w = WORKLOADS["train"]
+    inp = make_prefill(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", seed=w.seed + 1, with_dout=True)
     scale = default_scale(w.d)
     grads = run_fwd_bwd(gpu_lib, inp, True, scale)
-    # Per-head gradients depend only on that head's Q, K, V, dO: check two heads per batch.
     for b in range(w.B):
-        for h in ([0, 15] if seed_off == 0 else [7]):
+        for h in (7, 12):
             sub = {x: inp[x][b:b + 1, h:h + 1] for x in inp}
             check_bwd([g[b:b + 1, h:h + 1] for g in grads], sub, scale, True, tag=f"b{b}h{h}")
+
+
+def dominated_inputs(N, trend, qk_mult, seed):
+    """Q, K, V, dO whose rows are dominated by one key over stretches longer than a key tile:
+    "spike" puts a few keys along the mean query with large norms, so every later row's softmax
+    is carried by the latest spike; "rising" grows the key norms along the sequence, so each
+    row's largest weights sit on its most recent keys."""
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    inp = make_prefill(1, 2, 2, N, 128, "bf16", seed=seed, with_dout=True, qk_mult=qk_mult)
+    q = bf16_bits_to_f32(inp["q"]).reshape(1, 2, N, 128)
+    k = bf16_bits_to_f32(inp["k"]).reshape(1, 2, N, 128)
+    if trend == "rising":
+        k = k * np.linspace(0.2, 3.0, N, dtype=np.float32)[None, None, :, None]
+    else:
+        pos = np.array(sorted({37, N // 7, N // 3, N // 3 + 1, N // 2 + 5, (5 * N) // 6}))
+        k = k * 0.3
+        k[:, :, pos] = (np.sign(q.mean(axis=2, keepdims=True)) * np.linspace(6.0, 16.0, len(pos),
+                        dtype=np.float32)[None, None, :, None] * 0.5)
+    return {"q": inp["q"], "k": f32_to_bf16_bits(k), "v": inp["v"], "dout": inp["dout"]}
+
+
+@pytest.mark.parametrize("N", [1000, 4096])
+@pytest.mark.parametrize("trend", ["spike", "rising"])
+@pytest.mark.parametrize("qk_mult", [1.0, 2.0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_dominated_rows_long(gpu_lib, N, trend, qk_mult, causal):
+    """Backward on rows dominated by one key over many key tiles: there dP - D nearly cancels
+    for the dominant key, so D must be accurate to well below the bf16 rounding of O."""
+    print(f"bwd dominated N={N} {trend} x{qk_mult} causal={causal}", flush=True)
+    inp = dominated_inputs(N, trend, qk_mult, seed=5100 + N + int(qk_mult))
+    scale = default_scale(128)
+    grads = run_fwd_bwd(gpu_lib, inp, causal, scale)
+    check_bwd(grads, inp, scale, causal, tag=f"dominated N={N} {trend} x{qk_mult} causal={causal}")
 
 
 @pytest.mark.parametrize("N", [1, 17, 64, 200, 333])
@@ -392,9 +505,15 @@ def test_bwd_from_oracle_forward(gpu_lib):
 def run_decode_multi(lib, q, kc, vc, lens, causal, splits, scale):
     import torch
     sl = None if lens is None else torch.tensor(np.asarray(lens, dtype=np.int32)).cuda()
-    o, lse = lib.attn_decode_multi(to_dev(q), to_dev(kc), to_dev(vc), scale, causal=causal, seqlens=sl,
-                                   num_splits=splits)
-    torch.cuda.synchronize()
+    qd = to_dev(q)
+    B, Hq, T, d = qd.shape
+    Hkv, L = kc.shape[1], kc.shape[2]
+    g = Guarded()
+    o, lse = g.like(qd), g.empty((B, Hq, T), torch.float32)
+    ws = g.empty((lib.attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, splits),), torch.uint8)
+    lib.attn_decode_multi(qd, to_dev(kc), to_dev(vc), scale, causal=causal, seqlens=sl, num_splits=splits, o=o,
+                          lse=lse, workspace=ws)
+    g.check("decode_multi")
     return to_host64(o), lse.cpu().numpy().astype(np.float64)
 
 
