@@ -23,7 +23,7 @@ EXPORTS = (
     "attn_fwd_blocksparse",
     "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
     "attn_bwd_blocksparse", "attn_decode_auto_splits",
-    "attn_decode_workspace_bytes", "attn_decode", "attn_decode_varlen",
+    "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc", "attn_decode_varlen",
     "attn_decode_multi_workspace_bytes", "attn_decode_multi",
 )
 
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_decode.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_decode_noalloc.restype = i
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.attn_decode_multi_workspace_bytes.restype = sz
     lib.attn_decode_multi_workspace_bytes.argtypes = [i] * 7
     lib.attn_decode_multi.restype = i
@@ -351,6 +353,30 @@ def attn_decode(q, k_cache, v_cache, scale: float, num_splits: int = 0, o=None, 
     _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d,
                            _dtype_code(q), float(scale), int(num_splits), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, lse
+
+
+# Scratch the library holds per GPU for attn_decode_noalloc (ATTN_DECODE_NOALLOC_SCRATCH_BYTES).
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, scale: float, num_splits: int = 0, o=None, lse=None, want_lse=True,
+                        stream=None):
+    """attn_decode with no workspace: the split partials go to the library's own scratch array.
+    With o (and lse) given, nothing is allocated on the device."""
+    import torch
+    lib = load()
+    _require(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4, "q [B,Hq,d], caches [B,Hkv,L,d]")
+    for t in (q, k_cache, v_cache):
+        _require(t.is_cuda and t.is_contiguous(), "inputs must be contiguous CUDA tensors")
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _require(tuple(k_cache.shape) == (B, Hkv, L, d) == tuple(v_cache.shape), "cache shape mismatch")
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq, Hkv, L, d,
+                                   _dtype_code(q), float(scale), int(num_splits), _stream(stream)))
     return o, lse
 
 

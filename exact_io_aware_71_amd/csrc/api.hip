@@ -2,11 +2,14 @@
 //
 // Every argument is validated on the host before any HIP call, so the validation paths are
 // exercised without a GPU.  The library allocates nothing: scratch space comes from the
-// caller's workspace, which keeps every call capturable in a HIP graph.
+// caller's workspace, which keeps every call capturable in a HIP graph.  The one exception,
+// attn_decode_noalloc, takes its scratch from a fixed device array of the library instead.
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "launch.h"
@@ -312,10 +315,41 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int num
   return attn_decode_multi_workspace_bytes(B, Hq, Hkv, 1, L, d, num_splits);
 }
 
+// ------------------------------------------------------------ scratch of attn_decode_noalloc
+// The split partials of attn_decode_noalloc live in this array instead of a caller workspace.
+// Each GPU the library runs on holds its own copy until the process ends; host code reaches
+// it only through the device address hipGetSymbolAddress returns on that device (the array's
+// name on the host is a stand-in, not a device address), looked up once per device.
+constexpr size_t kNoallocScratchBytes = ATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+static attn_status_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// use_scratch: take the partials from the library's scratch array (attn_decode_noalloc); the
+// workspace arguments are then ignored.
 static attn_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,
                                  void* o, float* lse, int B, int Hq, int Hkv, int L, int d, attn_dtype_t dtype,
                                  float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream,
-                                 int T = 1, int causal = 0) {
+                                 int T = 1, int causal = 0, bool use_scratch = false) {
   if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-null");
   if (T <= 0) return fail(ATTN_ERR_INVALID_ARG, "T must be positive (got %d)", T);
   RETURN_IF(check_heads(B, Hq, Hkv, L, d));
@@ -331,6 +365,14 @@ static attn_status_t decode_impl(const void* q, const void* k_cache, const void*
     return fail(ATTN_ERR_UNSUPPORTED, "decode supports at most %d (token, head) rows per KV head (T=%d, group %d)",
                 xattn::kDecMaxRows, T, Hq / Hkv);
   const size_t need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, L, d, num_splits);
+  if (use_scratch) {
+    if (need > kNoallocScratchBytes)
+      return fail(ATTN_ERR_UNSUPPORTED,
+                  "attn_decode_noalloc needs %zu scratch bytes for this shape, above the %zu the library holds "
+                  "(use attn_decode with a workspace)", need, kNoallocScratchBytes);
+    RETURN_IF(noalloc_scratch(&workspace));
+    workspace_bytes = kNoallocScratchBytes;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "attn_decode needs %zu workspace bytes (got %zu)", need, workspace ? workspace_bytes : 0);
   if (!aligned256(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -351,6 +393,13 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, nullptr, o, lse, B, Hq, Hkv, L, d, dtype, scale, num_splits, workspace,
                      workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                  int B, int Hq, int Hkv, int L, int d, attn_dtype_t dtype, float scale,
+                                  int num_splits, void* stream) {
+  return decode_impl(q, k_cache, v_cache, nullptr, o, lse, B, Hq, Hkv, L, d, dtype, scale, num_splits, nullptr, 0,
+                     stream, 1, 0, true);
 }
 
 attn_status_t attn_decode_multi(const void* q, const void* k_cache, const void* v_cache, const int* seqlens,

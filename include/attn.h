@@ -239,6 +239,29 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* stream);
 
 /*
+ * attn_decode without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * kernels and results as attn_decode with the same num_splits (bit for bit); the split
+ * partials go to a fixed scratch array inside the library instead of a caller workspace.
+ *   - The scratch holds ATTN_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, set aside on
+ *     every GPU the library runs on until the process ends.  A shape whose
+ *     attn_decode_workspace_bytes(...) exceeds it returns ATTN_ERR_UNSUPPORTED (nothing is
+ *     enqueued); the decode workload (B=64, Hq=32, Hkv=8, L=8192, d=128, automatic splits)
+ *     needs about 4.3 MB.
+ *   - The call allocates nothing: no hipMalloc, no hipFree, no library routine that
+ *     allocates.  Its first call on a device looks up the scratch's device address there once.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ *     streams, other threads, a graph replayed while another call runs) race and must be
+ *     ordered by the caller.  No state carries over between calls: every partial is written
+ *     before the merge reads it.
+ * Errors: as attn_decode (minus the workspace errors), plus ATTN_ERR_UNSUPPORTED above.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status_t attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                  float* lse, int B, int Hq, int Hkv, int L, int d,
+                                  attn_dtype_t dtype, float scale, int num_splits, void* stream);
+
+/*
  * attn_decode for a batch whose sequences hold different numbers of cached keys (caches of
  * one capacity L, each sequence b filled to its own length).  Sequence b attends to keys
  * [0, seqlens[b]) of its cache rows; everything else is as in attn_decode (same workspace

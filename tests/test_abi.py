@@ -196,6 +196,28 @@ def test_decode_plan_and_validation():
     assert decv(d=32) == 2
 
 
+def test_decode_noalloc_validation():
+    """attn_decode_noalloc: argument errors as attn_decode, and shapes whose partials exceed the
+    library's fixed 16 MiB scratch are refused before any HIP call."""
+    def decn(B=64, Hq=32, Hkv=8, L=8192, d=128, dt=1, splits=0, q=P, scale=0.1):
+        return lib.attn_decode_noalloc(q, P, P, P, P, B, Hq, Hkv, L, d, dt, ctypes.c_float(scale), splits, None)
+    assert binding.DECODE_NOALLOC_SCRATCH_BYTES == 16 << 20
+    # The decode workload fits (about 4.3 MB of partials).
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 8192, 128, 0) <= binding.DECODE_NOALLOC_SCRATCH_BYTES
+    big = lib.attn_decode_workspace_bytes(4096, 32, 8, 8192, 128, 0)
+    assert big > binding.DECODE_NOALLOC_SCRATCH_BYTES
+    assert decn(B=4096) == 2
+    assert b"scratch" in lib.attn_last_error()
+    assert decn(splits=64) == 2      # 64 splits of the decode workload: 67 MB of partials
+    assert decn(q=None) == 1
+    assert decn(q=P + 8) == 1        # misaligned
+    assert decn(d=32) == 2
+    assert decn(dt=0) == 2
+    assert decn(splits=-1) == 1
+    assert decn(scale=float("nan")) == 1
+    assert decn(Hq=30) == 1          # Hq not a multiple of Hkv
+
+
 def test_binding_raises_typed_error():
     with pytest.raises(binding.AttnError) as ei:
         binding._check(fwd(d=96))
