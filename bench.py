@@ -13,12 +13,24 @@ stream the kernels run on, over K steps after W untimed warm-up steps (default 5
 idle gap the shader clock needs some 25 ms of load to settle, and the timed steps should not
 include that ramp).  The fp64 CPU oracle is timed beside it on a bounded sample.
 
-Secondary lines, each timed on its own after the step (skipped with --no-extras): decode with
-per-sequence cache lengths, multi-token decode, chunked prefill (Nq != Nk), packed sequences of
-different lengths (forward and backward), a block-sparse mask (forward and backward) and the
-d=64 batched prefill.  Their FLOP counts are 4 d per (query, key) pair the mask keeps.
+Secondary lines, each timed on its own after the step (skipped with --no-extras):
+  * the other workload configurations: the tiny fp32 forward (B=1 H=1 N=256 d=64), the batched
+    d=64 prefill (B=4 H=16 N=1024, causal, with LSE; memory-side roofline) and the long-prefill
+    sweep (B=1 H=32 d=128, Q and K x2, N = 4096 / 8192 / 16384, causal and not);
+  * decode with per-sequence cache lengths, multi-token decode, chunked prefill (Nq != Nk),
+    packed sequences of different lengths (forward and backward), a block-sparse mask (forward
+    and backward).
+FLOP counts are 4 d per (query, key) pair the mask keeps.  Each line carries its fraction of
+the roofline: dense bf16 MFMA peak 2516.6 TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP per clock), HBM
+8000 GB/s (the published MI355X figures).
+
+Calibration modes (no step): --copy-calibration runs plain 1 GiB device copies (the reference
+for rocprofv3's FETCH_SIZE / WRITE_SIZE byte counters); --stream-read times a streaming read of
+a 4 GiB buffer (libexact_calib.so) at several grid sizes, the HBM read rate a kernel that only
+reads reaches on this GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+                       [--copy-calibration | --stream-read]
 """
 from __future__ import annotations
 
@@ -32,7 +44,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clock
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -126,6 +138,45 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
+def stream_read(nbytes=4 << 30):
+    """Streaming read of a device buffer with the calibration kernel at several grid sizes:
+    GB/s per grid (median of 5 timed batches of 10 reads, after 200 ms of warm-up reads)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_71_amd", "libexact_calib.so"))
+    lib.calib_stream_read.restype = ctypes.c_int
+    lib.calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(3)
+    out = torch.empty(1 << 16, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for blocks in (1024, 2048, 4096, 8192, 16384):
+        def run():
+            rc = lib.calib_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"calib_stream_read failed ({rc})")
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 10)
+        ms = sorted(times)[2]
+        res[blocks] = nbytes / (ms * 1e-3) / 1e9
+    best = max(res, key=res.get)
+    print(json.dumps({"stream_read_bytes": nbytes, "GBps_by_workgroups": res, "best_GBps": res[best],
+                      "best_workgroups": best}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,12 +188,17 @@ def main():
                          "variable-length decode) so that a profile holds the timed step only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (reference for HBM byte counters)")
+    ap.add_argument("--stream-read", action="store_true",
+                    help="only time a streaming read of a 4 GiB buffer (HBM read ceiling of a plain kernel)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.stream_read:
+        stream_read()
         return
 
     import numpy as np
@@ -309,7 +365,9 @@ def main():
                                                            workspace=mws))
         mdec_bytes = 2 * DB * DHkv * DL * d * 2 + 2 * DB * DHq * MT * d * 2 + DB * DHq * MT * 4
         del mq, mo, mlse, mws
-        # Batched prefill, d=64: B=4, H=16, N=1024, causal, with LSE (seed 1002).
+        # Batched prefill, d=64: B=4, H=16, N=1024, causal, with LSE (seed 1002).  Its
+        # arithmetic intensity (N/4 = 254 FLOP per byte) is below the ridge point (2516.6 TFLOP/s
+        # over 8000 GB/s = 315), so the roofline bound is the memory side: Q, K, V, O and LSE once.
         bp = make_prefill(4, 16, 16, 1024, 64, "bf16", seed=1002)
         bq, bk, bv = (to_dev(bp[x]) for x in ("q", "k", "v"))
         del bp
@@ -317,7 +375,30 @@ def main():
         blse = torch.empty((4, 16, 1024), dtype=torch.float32, device=dev)
         ms_pre64 = time_call(lambda: attn.attn_fwd(bq, bk, bv, True, default_scale(64), o=bo, lse=blse))
         f_pre64 = flops_fwd(4, 16, 1024, 64, True)
+        b_pre64 = 4 * 4 * 16 * 1024 * 64 * 2 + 4 * 16 * 1024 * 4
+        floor_pre64 = max(f_pre64 / (PEAK_BF16_TFLOPS * 1e12), b_pre64 / (PEAK_HBM_GBS * 1e9)) * 1e3
         del bq, bk, bv, bo, blse
+        # Tiny fp32 forward: B=1, H=1, N=256, d=64, non-causal (seed 1001); latency-bound.
+        tp = make_prefill(1, 1, 1, 256, 64, "f32", seed=1001)
+        tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(tp[x])).to(dev) for x in ("q", "k", "v"))
+        ms_tiny = time_call(lambda: attn.attn_fwd(tq, tk, tv, False, default_scale(64)))
+        f_tiny = flops_fwd(1, 1, 256, 64, False)
+        del tp, tq, tk, tv
+        # Long-prefill sweep: B=1, H=32, d=128, Q and K x2 (seed 1003), N = 4096, 8192, 16384,
+        # causal and not.
+        log("long-prefill sweep")
+        sweep = []
+        for LN in (4096, 8192, 16384):
+            lp = make_prefill(1, 32, 32, LN, d, "bf16", seed=1003, qk_mult=2.0)
+            lq, lk, lv = (to_dev(lp[x]) for x in ("q", "k", "v"))
+            del lp
+            lo = torch.empty_like(lq)
+            llse = torch.empty((1, 32, LN), dtype=torch.float32, device=dev)
+            for lc in (True, False):
+                ms_l = time_call(lambda: attn.attn_fwd(lq, lk, lv, lc, scale, o=lo, lse=llse), reps=10)
+                tf = flops_fwd(1, 32, LN, d, lc) / (ms_l * 1e-3) / 1e12
+                sweep.append({"N": LN, "causal": lc, "ms": ms_l, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS})
+            del lq, lk, lv, lo, llse
         extras = {
             "decode_varlen": {"GBps": vdec_bytes / (ms_vdec * 1e-3) / 1e9, "ms": ms_vdec,
                               "lengths": "uniform in [L/2, L], seed 1006, mean %.0f" % float(vlens.mean())},
@@ -334,8 +415,15 @@ def main():
                                        "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},
             "decode_multi": {"GBps": mdec_bytes / (ms_mdec * 1e-3) / 1e9, "ms": ms_mdec,
                          "workload": "attn_decode_multi B=64 Hq=32 Hkv=8 T=4 L=8192 d=128 causal"},
-        "fwd_prefill_d64": {"TFLOPs": f_pre64 / (ms_pre64 * 1e-3) / 1e12, "ms": ms_pre64,
-                                "workload": "attn_fwd B=4 H=16 N=1024 d=64 causal with LSE"},
+            "fwd_prefill_d64": {"TFLOPs": f_pre64 / (ms_pre64 * 1e-3) / 1e12, "ms": ms_pre64,
+                                "workload": "attn_fwd B=4 H=16 N=1024 d=64 causal with LSE",
+                                "roofline": {"bound": "hbm", "achieved": b_pre64 / (ms_pre64 * 1e-3) / 1e9,
+                                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                             "frac": floor_pre64 / ms_pre64, "floor_ms": floor_pre64,
+                                             "bytes": b_pre64}},
+            "fwd_tiny_f32": {"ms": ms_tiny, "TFLOPs": f_tiny / (ms_tiny * 1e-3) / 1e12,
+                             "workload": "attn_fwd B=1 H=1 N=256 d=64 fp32 non-causal (latency-bound)"},
+            "fwd_long_prefill": {"workload": "attn_fwd B=1 H=32 d=128, Q and K x2, with LSE", "lines": sweep},
         }
     f_fwd = flops_fwd(B, H, N, d, True)
     f_bwd = 2.5 * f_fwd
