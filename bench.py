@@ -9,9 +9,10 @@ One step = one pass of the whole path on synthetic inputs already resident in HB
 Reported value: forward+backward TFLOP/s with the algorithmic count 4 N^2 d per head
 (halved for causal) for the forward and 2.5x that for the backward.  Decode is reported as
 algorithmic HBM GB/s (K + V + Q + O + LSE bytes).  Phase times come from HIP events on the
-stream the kernels run on, over K steps after W untimed warm-up steps (default 50: after an
-idle gap the shader clock needs some 25 ms of load to settle, and the timed steps should not
-include that ramp).  The fp64 CPU oracle is timed beside it on a bounded sample.
+stream the kernels run on, over K steps after 0.3 s of untimed steps and then W untimed
+warm-up steps (default 50): after an idle gap the shader clock needs some 25 ms of load to
+settle, and the timed steps should not include that ramp.  The fp64 CPU oracle is timed beside
+it on a bounded sample.
 
 Secondary lines, each timed on its own after the step (skipped with --no-extras):
   * the other workload configurations: the tiny fp32 forward (B=1 H=1 N=256 d=64), the batched
@@ -27,10 +28,12 @@ the roofline: dense bf16 MFMA peak 2516.6 TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP
 Calibration modes (no step): --copy-calibration runs plain 1 GiB device copies (the reference
 for rocprofv3's FETCH_SIZE / WRITE_SIZE byte counters); --stream-read times a streaming read of
 a 4 GiB buffer (libexact_calib.so) at several grid sizes, the HBM read rate a kernel that only
-reads reaches on this GPU.
+reads reaches on this GPU; --mfma-ceiling times a plain loop of dense bf16 MFMAs on every SIMD
+and reads the shader clock it runs at (the matrix-core rate such a loop reaches on this GPU).
+--prefill-d64 times only the batched d=64 prefill, for a profile of its kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-                       [--copy-calibration | --stream-read]
+                       [--copy-calibration | --stream-read | --mfma-ceiling | --prefill-d64]
 """
 from __future__ import annotations
 
@@ -177,6 +180,81 @@ def stream_read(nbytes=4 << 30):
                       "best_workgroups": best}))
 
 
+def mfma_ceiling(blocks=1024, iters=4096):
+    """Dense bf16 matrix-core rate of a plain loop (four workgroups of four waves per CU, four
+    independent 32x32x16 products per wave in flight) and the shader clock it runs at, from the
+    ratio of the shader-clock counter to the 100 MHz reference counter over each wave's loop:
+    median of 5 timed batches of 10 launches after 200 ms of warm-up launches."""
+    import ctypes
+    import statistics
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_71_amd", "libexact_calib.so"))
+    lib.calib_mfma.restype = ctypes.c_int
+    lib.calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        rc = lib.calib_mfma(blocks, iters, sink.data_ptr(), ticks.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"calib_mfma failed ({rc})")
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 10)
+    ms = sorted(times)[2]
+    flops = blocks * 4 * iters * 4 * 32768
+    t = ticks.view(blocks, 2).cpu().numpy()
+    ghz = statistics.median((t[:, 0] / t[:, 1] * 0.1).tolist())
+    print(json.dumps({"mfma_bf16_TFLOPs": flops / (ms * 1e-3) / 1e12, "ms": ms, "shader_clock_GHz": ghz,
+                      "TFLOPs_at_clock": PEAK_BF16_TFLOPS * ghz / 2.4, "workgroups": blocks, "iters": iters}))
+
+
+def prefill_d64(reps=200):
+    """Only the batched prefill (B=4, H=16, N=1024, d=64, causal, with LSE; seed 1002): 300 ms of
+    warm-up calls, then `reps` timed calls; prints the mean ms.  For a profile of its kernel."""
+    import numpy as np
+    import torch
+    from exact_io_aware_71_amd import binding as attn
+    from synth import default_scale, make_prefill
+    attn.load()
+    dev = torch.device("cuda:0")
+    bp = make_prefill(4, 16, 16, 1024, 64, "bf16", seed=1002)
+    bq, bk, bv = (torch.from_numpy(np.ascontiguousarray(bp[x]).view(np.int16)).view(torch.bfloat16).to(dev)
+                  for x in ("q", "k", "v"))
+    bo = torch.empty_like(bq)
+    blse = torch.empty((4, 16, 1024), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        attn.attn_fwd(bq, bk, bv, True, default_scale(64), o=bo, lse=blse)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"workload": "attn_fwd B=4 H=16 N=1024 d=64 causal with LSE", "ms": ms,
+                      "TFLOPs": flops_fwd(4, 16, 1024, 64, True) / (ms * 1e-3) / 1e12, "calls": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +268,10 @@ def main():
                     help="only run plain 1 GiB device copies (reference for HBM byte counters)")
     ap.add_argument("--stream-read", action="store_true",
                     help="only time a streaming read of a 4 GiB buffer (HBM read ceiling of a plain kernel)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time a plain loop of dense bf16 MFMAs and read the shader clock it runs at")
+    ap.add_argument("--prefill-d64", action="store_true",
+                    help="only time the batched d=64 prefill (B=4 H=16 N=1024 causal), for a profile of its kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
@@ -199,6 +281,12 @@ def main():
         return
     if args.stream_read:
         stream_read()
+        return
+    if args.prefill_d64:
+        prefill_d64()
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
 
     import numpy as np
@@ -249,7 +337,14 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    log(f"warmup {args.warmup} steps")
+    # The shader clock needs some 25 ms of load to settle after an idle gap (inputs are built on
+    # the host with the GPU idle): run the step for 0.3 s before the W warm-up steps, so that a
+    # small W does not leave the ramp inside the timed steps.
+    log(f"settling 0.3 s, then warmup {args.warmup} steps")
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.3:
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -420,7 +515,9 @@ def main():
                                 "roofline": {"bound": "hbm", "achieved": b_pre64 / (ms_pre64 * 1e-3) / 1e9,
                                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                              "frac": floor_pre64 / ms_pre64, "floor_ms": floor_pre64,
-                                             "bytes": b_pre64}},
+                                             "bytes": b_pre64,
+                                             "traffic": load_traffic("fwd_ilv_kernel<64,4,64,true,false>",
+                                                                     source_digest("fwd.hip", "common.h"))}},
             "fwd_tiny_f32": {"ms": ms_tiny, "TFLOPs": f_tiny / (ms_tiny * 1e-3) / 1e12,
                              "workload": "attn_fwd B=1 H=1 N=256 d=64 fp32 non-causal (latency-bound)"},
             "fwd_long_prefill": {"workload": "attn_fwd B=1 H=32 d=128, Q and K x2, with LSE", "lines": sweep},
@@ -449,10 +546,12 @@ def main():
         "bound": "mfma", "achieved": f_fwd / (ms_fwd * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
     }
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
-    roofline["traffic"] = load_traffic("fwd_ilv_kernel", fwd_digest)
-    bwd_traffic = [load_traffic(kn, bwd_digest) for kn in ("bwd_dq_kernel", "bwd_dkdv_lag_kernel")]
+    roofline["traffic"] = load_traffic("fwd_ilv_kernel<128,8,64,true,false>", fwd_digest)
+    bwd_traffic = [load_traffic(kn, bwd_digest) for kn in ("bwd_dq_kernel<128,true,false,false>",
+                                                           "bwd_dq_kernel<128,true,false,true>",
+                                                           "bwd_dkdv_lag_kernel<128,true,false>")]
     roofline_bwd = {
-        "kernel": "bwd_dq_kernel + bwd_dkdv_lag_kernel (attn_bwd, causal, B*H=32, N=4096, d=128)",
+        "kernel": "bwd_dq_kernel (two launches) + bwd_dkdv_lag_kernel (attn_bwd, causal, B*H=32, N=4096, d=128)",
         "bound": "mfma", "achieved": f_bwd / (ms_bwd * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": f_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "traffic": None if None in bwd_traffic else sum(bwd_traffic),
@@ -460,7 +559,7 @@ def main():
     roofline_decode = {
         "kernel": "decode_split_kernel + decode_merge_kernel (attn_decode, B=64, Hq=32, Hkv=8, L=8192, d=128)",
         "bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS,
-        "traffic": load_traffic("decode_split_kernel", dec_digest), "splits": splits,
+        "traffic": load_traffic("decode_split_kernel<128,4>", dec_digest), "splits": splits,
     }
 
     result = {

@@ -12,15 +12,18 @@
 //   P = exp(scale S - LSE), dV = P^T dO, dP = dO V^T, D_i = sum_c dO_ic O_ic,
 //   dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
-// Two launches (three for a causal grouped-query shape with few key blocks), deterministic
+// Three launches (four for a causal grouped-query shape with few key blocks), deterministic
 // (no atomics):
 //   1. bwd_dq_kernel: one workgroup per 128 queries; S^T = K Q^T and dP^T = V dO^T with
 //      Q and dO resident in registers, K/V tiles streamed through LDS; dS^T in the C layout
 //      is the A operand of dQ = dS K, K entering through the transposing read.  It also
 //      writes D = rowsum(dO * O) (sum_j P_ij dP_ij where the rows' keys fit one tile) and
 //      LSE * log2(e) of its rows into row-padded arrays of the caller's workspace (padding
-//      rows get LSE = +inf, so their probabilities vanish).
-//   2. bwd_dkdv_lag_kernel: one workgroup per 128 keys of a KV head; each wave keeps its 32
+//      rows get LSE = +inf, so their probabilities vanish), and flags each wave that met a
+//      probability above 1/2.
+//   2. bwd_dq_kernel again (REDO): workgroups with a flagged wave form D = sum_j P_ij dP_ij
+//      from its definition, write it, and compute their dQ again with it; the others exit.
+//   3. bwd_dkdv_lag_kernel: one workgroup per 128 keys of a KV head; each wave keeps its 32
 //      keys' K (or V) rows in registers as the B operand of S = Q K^T (or dP = dO V^T) and
 //      its dV (or dK) accumulator in registers, while [Q | dO | LSE | D] tiles of 64 queries
 //      stream through a three-stage LDS ring.  In the C layout of S each lane owns one key,
@@ -28,7 +31,7 @@
 //      those products through the transposing ds_read_b64_tr_b16.  Causal: query tiles
 //      before the diagonal are never visited.  With few key blocks and an even group size the
 //      group's query heads split over two workgroups whose fp32 partial sums
-//      bwd_dkdv_sum_kernel adds (the third launch).
+//      bwd_dkdv_sum_kernel adds (the fourth launch).
 // Every kernel takes the per-sequence row map of the forward (dense [B,H,N,d], or packed
 // variable-length [H,total,d] with offsets), and causal masks aligned at the bottom right:
 // query i of Nq sees keys j <= i + Nk - Nq.

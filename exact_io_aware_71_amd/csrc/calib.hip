@@ -1,9 +1,12 @@
-// Calibration kernel for the benchmark (not part of libexact_attn.so): a streaming read of a
-// device buffer, so that the HBM read rate the attention kernels reach can be set beside what
-// a plain read of the same size reaches on the same GPU.
-//
-// Every thread reads 16-byte chunks at a grid stride, four loads in flight, and folds them into
-// one word so that the loads cannot be removed; one word per workgroup is written.
+// Calibration kernels for the benchmark (not part of libexact_attn.so), so that the rates the
+// attention kernels reach can be set beside what plain kernels reach on the same GPU:
+//   * stream_read_kernel, a streaming read of a device buffer (HBM read rate).  Every thread
+//     reads 16-byte chunks at a grid stride, four loads in flight, and folds them into one
+//     word so that the loads cannot be removed; one word per workgroup is written.
+//   * mfma_loop_kernel, back-to-back v_mfma_f32_32x32x16_bf16 on four independent
+//     accumulators per wave (dense bf16 matrix-core rate), which also reads the shader-clock
+//     counter (s_memtime) and the 100 MHz reference counter (s_memrealtime) around its loop,
+//     so that the clock the matrix cores run at under full load follows from their ratio.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,6 +37,41 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (threadIdx.x == 0) out[blockIdx.x] = red[0];
 }
 
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ sink,
+                                                        unsigned long long* __restrict__ ticks) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (short)(0x3c00 + lane);  // about 2^-7: the sums stay far from overflow
+    b[i] = (short)(0x3c00 - i);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  __builtin_amdgcn_sched_barrier(0);
+  for (int it = 0; it < iters; it += 2) {  // two rounds per pass: loop overhead under 2%
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (threadIdx.x == 0) {
+    ticks[2 * (size_t)blockIdx.x] = t1 - t0;
+    ticks[2 * (size_t)blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -44,6 +82,18 @@ int calib_stream_read(const void* p, size_t bytes, unsigned* out, int blocks, vo
   if (p == nullptr || out == nullptr || blocks <= 0 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4*)p, bytes / 16, (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+
+// Runs `blocks` workgroups of 256 threads (four waves), each wave issuing 4 * `iters` (`iters`
+// even) dense bf16 32x32x16 matrix products (32768 flops each) from registers.  `sink` (device,
+// 256 floats per workgroup) receives the folded products; `ticks` (device, 2 words per
+// workgroup) the shader-clock cycles and the 100 MHz reference ticks of wave 0's loop.  Returns
+// the hipError_t of the launch.
+int calib_mfma(int blocks, int iters, float* sink, unsigned long long* ticks, void* stream) {
+  if (sink == nullptr || ticks == nullptr || blocks <= 0 || iters <= 0 || iters % 2 != 0)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink, ticks);
   return (int)hipGetLastError();
 }
 
