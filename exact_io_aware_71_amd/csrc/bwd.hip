@@ -17,7 +17,8 @@
 //   1. bwd_dq_kernel: one workgroup per 128 queries; S^T = K Q^T and dP^T = V dO^T with
 //      Q and dO resident in registers, K/V tiles streamed through LDS; dS^T in the C layout
 //      is the A operand of dQ = dS K, K entering through the transposing read.  It also
-//      writes D = rowsum(dO * O) (sum_j P_ij dP_ij where the rows' keys fit one tile) and
+//      writes D = rowsum(dO * O) (sum_j P_ij dP_ij where the rows' keys fit one tile, or two
+//      at d = 64) and
 //      LSE * log2(e) of its rows into row-padded arrays of the caller's workspace (padding
 //      rows get LSE = +inf, so their probabilities vanish), and flags each wave that met a
 //      probability above 1/2.
@@ -594,7 +595,8 @@ constexpr int dq_vslot(int L, int g) { return 1 + g * (L - 2) / 3; }
 // sum_j P_ij dP_ij (fp32), in a walk that computes only S and dP, writes it for the dK/dV kernel
 // (launched after both), and walks the key tiles once more, last first (the last two are still
 // in LDS), for dQ with that D.  On N(0,1) inputs only the first rows of a causal sequence (few
-// keys) trigger it; rows whose keys all fit one tile get the exact D in the first launch.
+// keys) trigger it; rows whose keys all fit one tile (two at d = 64) get the exact D in the
+// first launch.  The redo launch takes light (early) query tiles first, where that work sits.
 template <int D, bool CAUSAL, bool SPARSE, bool REDO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -612,7 +614,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
   const int bh = blockIdx.x % BH;
   const int t_ = blockIdx.x / BH;
-  const int qt = CAUSAL ? (n_qtiles - 1 - t_) : t_;
+  // Causal: the first launch takes heavy (late) query tiles first; the redo launch, whose work
+  // sits in the first query tiles of a sequence, takes them first.
+  const int qt = (CAUSAL && !REDO) ? (n_qtiles - 1 - t_) : t_;
+  const size_t fl = 4 * ((size_t)qt * BH + bh);  // this workgroup's flag words (one per wave)
   const int q0 = qt * BM, qw0 = q0 + wave * 32, qi = qw0 + l32;
   // K/V of the query head's KV head (grouped-query: kv = h / (Hq/Hkv)).
   const int b = bh / Hq, hq = bh - b * Hq, hk = hq / (Hq / Hkv);
@@ -620,7 +625,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int Nq = sr.lq, Nk = sr.lk;
   if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
   if constexpr (REDO) {  // one flag word per wave of the first launch
-    const u32x4 f = *reinterpret_cast<const u32x4*>(flags + 4 * (size_t)blockIdx.x);
+    const u32x4 f = *reinterpret_cast<const u32x4*>(flags + fl);
     if (__builtin_amdgcn_readfirstlane(f[0] | f[1] | f[2] | f[3]) == 0) return;
   }
   const int qd0 = qw0 + (Nk - Nq), kmax = qi + (Nk - Nq);  // causal: query i sees keys <= i + Nk - Nq
@@ -721,7 +726,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   uint16_t* dqp = dq + sr.q * D;
-  if (!REDO && lane == 0 && (ntiles == 0 || (!SPARSE && ntiles == 1))) flags[4 * blockIdx.x + wave] = 0u;
+  // d = 64: workgroups whose rows' keys fit two tiles form the exact D in this launch (one more
+  // walk over those two tiles), so the redo launch skips them.  (At d = 128 the extra path
+  // costs the first launch's tile loop two register reloads per tile.)
+  const bool two_walk = REDO || (D == 64 && !SPARSE && ntiles == 2);
+  if (!REDO && lane == 0 && (ntiles == 0 || (!SPARSE && (ntiles == 1 || (D == 64 && ntiles == 2)))))
+    flags[fl + wave] = 0u;
   if (ntiles == 0) {  // no key for any row of the tile: dQ = 0
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -766,7 +776,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return join_tr(ds_read_tr16(smem + ofs.v[db][0] + roff), ds_read_tr16(smem + ofs.v[db][1] + roff));
     }
   };
-  if constexpr (REDO) {
+  if (two_walk) {
     // D_i = sum_j P_ij dP_ij over the rows' keys, from S and dP alone (tile t+1 copied during
     // tile t), then dQ with it, walking the tiles last first: the last two are still in the two
     // stages, and tile t-2 is copied into the stage of tile t during tile t-1.
@@ -964,7 +974,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // The wave's flag for the redo launch (rows past the sequence have P = 0, so a flagged
     // lane holds a real row).
     const bool dom = __builtin_amdgcn_ballot_w64(pmx > 0.5f) != 0;
-    if (lane == 0) flags[4 * blockIdx.x + wave] = dom ? 1u : 0u;
+    if (lane == 0) flags[fl + wave] = dom ? 1u : 0u;
   }
   }
   // C layout: lane holds feature db*32 + l32 of queries qw0 + 8(r/4) + 4*h32 + r%4.
