@@ -404,15 +404,15 @@ def test_bwd_training_step_other_seed(gpu_lib):
             check_bwd([g[b:b + 1, h:h + 1] for g in grads], sub, scale, True, tag=f"b{b}h{h}")
 
 
-def dominated_inputs(N, trend, qk_mult, seed):
+def dominated_inputs(N, trend, qk_mult, seed, d=128):
     """Q, K, V, dO whose rows are dominated by one key over stretches longer than a key tile:
     "spike" puts a few keys along the mean query with large norms, so every later row's softmax
     is carried by the latest spike; "rising" grows the key norms along the sequence, so each
     row's largest weights sit on its most recent keys."""
     from synth import bf16_bits_to_f32, f32_to_bf16_bits
-    inp = make_prefill(1, 2, 2, N, 128, "bf16", seed=seed, with_dout=True, qk_mult=qk_mult)
-    q = bf16_bits_to_f32(inp["q"]).reshape(1, 2, N, 128)
-    k = bf16_bits_to_f32(inp["k"]).reshape(1, 2, N, 128)
+    inp = make_prefill(1, 2, 2, N, d, "bf16", seed=seed, with_dout=True, qk_mult=qk_mult)
+    q = bf16_bits_to_f32(inp["q"]).reshape(1, 2, N, d)
+    k = bf16_bits_to_f32(inp["k"]).reshape(1, 2, N, d)
     if trend == "rising":
         k = k * np.linspace(0.2, 3.0, N, dtype=np.float32)[None, None, :, None]
     else:
@@ -435,6 +435,20 @@ def test_bwd_dominated_rows_long(gpu_lib, N, trend, qk_mult, causal):
     scale = default_scale(128)
     grads = run_fwd_bwd(gpu_lib, inp, causal, scale)
     check_bwd(grads, inp, scale, causal, tag=f"dominated N={N} {trend} x{qk_mult} causal={causal}")
+
+
+@pytest.mark.parametrize("N", [100, 1000])
+@pytest.mark.parametrize("trend", ["spike", "rising"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_dominated_rows_d64(gpu_lib, N, trend, causal):
+    """d = 64 on dominated rows: query tiles whose keys fit two 64-key tiles (N = 100, and the
+    first query tile of a causal sequence) form the exact D in the first dQ launch, longer ones
+    in the second."""
+    print(f"bwd dominated d=64 N={N} {trend} causal={causal}", flush=True)
+    inp = dominated_inputs(N, trend, 2.0, seed=5300 + N, d=64)
+    scale = default_scale(64)
+    grads = run_fwd_bwd(gpu_lib, inp, causal, scale)
+    check_bwd(grads, inp, scale, causal, tag=f"dominated d=64 N={N} {trend} causal={causal}")
 
 
 @pytest.mark.parametrize("N", [1, 17, 64, 200, 333])
