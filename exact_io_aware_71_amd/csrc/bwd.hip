@@ -17,8 +17,7 @@
 //   1. bwd_dq_kernel: one workgroup per 128 queries; S^T = K Q^T and dP^T = V dO^T with
 //      Q and dO resident in registers, K/V tiles streamed through LDS; dS^T in the C layout
 //      is the A operand of dQ = dS K, K entering through the transposing read.  It also
-//      writes D = rowsum(dO * O) (sum_j P_ij dP_ij where the rows' keys fit one tile, or two
-//      at d = 64) and
+//      writes D = rowsum(dO * O) (sum_j P_ij dP_ij where the rows' keys fit two tiles) and
 //      LSE * log2(e) of its rows into row-padded arrays of the caller's workspace (padding
 //      rows get LSE = +inf, so their probabilities vanish), and flags each wave that met a
 //      probability above 1/2.
@@ -595,8 +594,8 @@ constexpr int dq_vslot(int L, int g) { return 1 + g * (L - 2) / 3; }
 // sum_j P_ij dP_ij (fp32), in a walk that computes only S and dP, writes it for the dK/dV kernel
 // (launched after both), and walks the key tiles once more, last first (the last two are still
 // in LDS), for dQ with that D.  On N(0,1) inputs only the first rows of a causal sequence (few
-// keys) trigger it; rows whose keys all fit one tile (two at d = 64) get the exact D in the
-// first launch.  The redo launch takes light (early) query tiles first, where that work sits.
+// keys) trigger it; rows whose keys all fit one or two tiles get the exact D in the first
+// launch.  The redo launch takes light (early) query tiles first, where that work sits.
 template <int D, bool CAUSAL, bool SPARSE, bool REDO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -726,12 +725,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   uint16_t* dqp = dq + sr.q * D;
-  // d = 64: workgroups whose rows' keys fit two tiles form the exact D in this launch (one more
-  // walk over those two tiles), so the redo launch skips them.  (At d = 128 the extra path
-  // costs the first launch's tile loop two register reloads per tile.)
-  const bool two_walk = REDO || (D == 64 && !SPARSE && ntiles == 2);
-  if (!REDO && lane == 0 && (ntiles == 0 || (!SPARSE && (ntiles == 1 || (D == 64 && ntiles == 2)))))
-    flags[fl + wave] = 0u;
+  // Workgroups whose rows' keys fit two tiles form the exact D in this launch, so the redo
+  // launch skips them: at d = 64 through the two-walk path below, at d = 128 through a walk for D
+  // ahead of the main walk (the two-walk path in this launch cost the d = 128 main walk two
+  // register reloads per tile).
+  const bool two_walk = REDO || (D == 64 && ntiles == 2);
+  if (!REDO && lane == 0 && ntiles <= 2) flags[fl + wave] = 0u;
   if (ntiles == 0) {  // no key for any row of the tile: dQ = 0
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -776,32 +775,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       return join_tr(ds_read_tr16(smem + ofs.v[db][0] + roff), ds_read_tr16(smem + ofs.v[db][1] + roff));
     }
   };
+  // S (as P, masked) and dP of key block kb of the tile at key t0, from the current stage.
+  auto tile_sdp = [&](auto kc, int t0, f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
+    constexpr int kb = decltype(kc)::value;
+    static_for<DC>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      const bf16x8 ak = opnd(std::integral_constant<int, (2 * kb) * DC + c>{});
+      const bf16x8 av = opnd(std::integral_constant<int, (2 * kb + 1) * DC + c>{});
+      if constexpr (c == 0) {
+        sv = mfma32(ak, qreg[0], f32x16{});
+        dpv = mfma32(av, doreg[0], f32x16{});
+      } else {
+        sv = mfma32(ak, qreg[c], sv);
+        dpv = mfma32(av, doreg[c], dpv);
+      }
+    });
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      const float pr = fast_exp2(fmaf(sv[r], scale_log2, -lse2));
+      sv[r] = (kj >= Nk || (CAUSAL && kj > kmax)) ? 0.f : pr;
+    }
+  };
+  // d = 128, rows whose keys fit two tiles: D from its definition in a walk over the two tiles
+  // (S and dP only) before the main walk, which then takes that D; both tiles stay in the two
+  // stages, so the main walk starts on tile 0 as usual.
+  bool exact_d = false;
+  if constexpr (!REDO && D == 128) {
+    if (ntiles == 2) {
+      float dpart = 0.f;
+      for (int t = 0; t < 2; ++t) {
+        const int t0 = kt(t) * BN;
+        if (t == 0) copy_tile(kt(1), 1);
+        if (!(CAUSAL && t0 > qd0 + 31)) {
+          static_for<2>([&](auto kc) {
+            f32x16 sv, dpv;
+            tile_sdp(kc, t0, sv, dpv);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dpart = fmaf(sv[r], dpv[r], dpart);
+          });
+        }
+        wait_vmem();
+        lds_barrier();
+        ofs.toggle(STAGE);
+      }
+      dl = qi < Nq ? sum_xor32(dpart) : 0.f;
+      if (h32 == 0 && qi < Nq) st[stat_half + qi] = dl;
+      exact_d = true;
+    }
+  }
   if (two_walk) {
     // D_i = sum_j P_ij dP_ij over the rows' keys, from S and dP alone (tile t+1 copied during
     // tile t), then dQ with it, walking the tiles last first: the last two are still in the two
     // stages, and tile t-2 is copied into the stage of tile t during tile t-1.
     float dpart = 0.f;
-    auto tile_sdp = [&](auto kc, int t0, f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
-      constexpr int kb = decltype(kc)::value;
-      static_for<DC>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        const bf16x8 ak = opnd(std::integral_constant<int, (2 * kb) * DC + c>{});
-        const bf16x8 av = opnd(std::integral_constant<int, (2 * kb + 1) * DC + c>{});
-        if constexpr (c == 0) {
-          sv = mfma32(ak, qreg[0], f32x16{});
-          dpv = mfma32(av, doreg[0], f32x16{});
-        } else {
-          sv = mfma32(ak, qreg[c], sv);
-          dpv = mfma32(av, doreg[c], dpv);
-        }
-      });
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kj = t0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        const float pr = fast_exp2(fmaf(sv[r], scale_log2, -lse2));
-        sv[r] = (kj >= Nk || (CAUSAL && kj > kmax)) ? 0.f : pr;
-      }
-    };
     for (int t = 0; t < ntiles; ++t) {
       const int t0 = kt(t) * BN;
       if (t + 1 < ntiles) copy_tile(kt(t + 1), (t + 1) & 1);
@@ -845,7 +872,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ofs.toggle(STAGE);
     }
   } else
-  if (!SPARSE && ntiles == 1) {
+  if (ntiles == 1) {
     // The tile's keys are all the keys of these rows: D = sum_j P_ij dP_ij, its definition,
     // replaces rowsum(dO * O) here and in the statistics the dK/dV kernel reads.  O is stored in
     // bf16 and D inherits its rounding; on rows dominated by one key dP - D nearly cancels, and
@@ -974,7 +1001,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // The wave's flag for the redo launch (rows past the sequence have P = 0, so a flagged
     // lane holds a real row).
     const bool dom = __builtin_amdgcn_ballot_w64(pmx > 0.5f) != 0;
-    if (lane == 0) flags[fl + wave] = dom ? 1u : 0u;
+    if (lane == 0 && !exact_d) flags[fl + wave] = dom ? 1u : 0u;
   }
   }
   // C layout: lane holds feature db*32 + l32 of queries qw0 + 8(r/4) + 4*h32 + r%4.
