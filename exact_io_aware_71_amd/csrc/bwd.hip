@@ -153,7 +153,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* kp = k + sr.k * D;
   const uint16_t* vp = v + sr.k * D;
   const uint16_t* dop = dout + sr.q * D;
-  // stats = [LSE2 | D]; LSE2 is the log-sum-exp times log2(e).  Head i of the group: + i*stride.
+  // stats = [LSE2 | -D]; LSE2 is the log-sum-exp times log2(e).  Head i of the group: + i*stride.
   const float* lse_b = stats + stat_row(geo, stat_stride, b, h0, Hq);
   const float* dl_b = lse_b + stat_half;
   const int npad = (Nq + BQ - 1) / BQ * BQ;  // statistics rows of one head of this sequence
@@ -334,6 +334,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int db = 0; db < DB; ++db)
           acc[db] = mfma32(pa[qb][sh], trop(T::BYTES, qb * 32 + 16 * sh, db), acc[db]);
   };
+  // -D of the 32 queries of block qb in the C layout of dP (register r: query 32 qb + 8(r/4) +
+  // 4 h32 + r%4): the dP products accumulate onto it, so dP - D comes out of the matrix core.
+  auto neg_d = [&](const float* dls, int qb) __attribute__((always_inline)) -> f32x16 {
+    f32x16 x;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * r4 + 4 * h32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * r4 + e] = d4[e];
+    }
+    return x;
+  };
   auto dk_tile_plain = [&](int tt) __attribute__((always_inline)) {
     // dK wave, tile t-1: dP = dO V^T, dS = P (dP - D) with P from LDS, dK += dS^T Q.
     const char* qs = smem + (tt % NS) * STAGE;
@@ -343,8 +355,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 dp[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+      dp[qb] = neg_d(dls, qb);
 #pragma unroll
       for (int c = 0; c < DC; ++c)
         dp[qb] = mfma32(rowop(T::BYTES, qb * 32, c), kreg[c], dp[qb]);
@@ -356,12 +367,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const u32x4 pw = *reinterpret_cast<const u32x4*>(pr + (qb * 2 + sh) * 1024 + 16 * lane);
 #pragma unroll
         for (int r4 = 0; r4 < 2; ++r4) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * (2 * sh + r4) + 4 * h32);
           const int r = 8 * sh + 4 * r4;
-          dp[qb][r + 0] = bf16_lo(pw[2 * r4]) * (dp[qb][r + 0] - d4[0]);
-          dp[qb][r + 1] = bf16_hi(pw[2 * r4]) * (dp[qb][r + 1] - d4[1]);
-          dp[qb][r + 2] = bf16_lo(pw[2 * r4 + 1]) * (dp[qb][r + 2] - d4[2]);
-          dp[qb][r + 3] = bf16_hi(pw[2 * r4 + 1]) * (dp[qb][r + 3] - d4[3]);
+          dp[qb][r + 0] = bf16_lo(pw[2 * r4]) * dp[qb][r + 0];
+          dp[qb][r + 1] = bf16_hi(pw[2 * r4]) * dp[qb][r + 1];
+          dp[qb][r + 2] = bf16_lo(pw[2 * r4 + 1]) * dp[qb][r + 2];
+          dp[qb][r + 3] = bf16_hi(pw[2 * r4 + 1]) * dp[qb][r + 3];
         }
       }
 #pragma unroll
@@ -459,20 +469,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 dp[NQB];
     bf16x8 dsa[NQB][2];
     bf16x8 buf[LA];
+    dp[0] = neg_d(dls, 0);
     static_for<LA>([&](auto jc) { buf[decltype(jc)::value] = opnd(jc); });
     sched_fence();
     static_for<32>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      if constexpr (i == 3) dp[1] = neg_d(dls, 1);  // read ahead of its first product (slot 8)
       if constexpr (i < 16) {
         constexpr int qb = i / 8, c = i % 8;
-        if constexpr (c == 0) {
-          f32x16 z;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) z[r] = 0.f;
-          dp[qb] = mfma32(buf[i % LA], kreg[0], z);
-        } else {
-          dp[qb] = mfma32(buf[i % LA], kreg[c], dp[qb]);
-        }
+        dp[qb] = mfma32(buf[i % LA], kreg[c], dp[qb]);
       } else {
         constexpr int jj = i - 16, qb = jj / 8, sh = (jj / 4) % 2, db = jj % 4;
         acc[db] = mfma32(dsa[qb][sh], buf[i % LA], acc[db]);
@@ -485,12 +490,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         u32x4 u;
 #pragma unroll
         for (int r4 = 0; r4 < 2; ++r4) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * (2 * sh + r4) + 4 * h32);
           const int r = 8 * sh + 4 * r4;
-          const float e0 = bf16_lo(pw[2 * r4]) * (dp[qb][r + 0] - d4[0]);
-          const float e1 = bf16_hi(pw[2 * r4]) * (dp[qb][r + 1] - d4[1]);
-          const float e2 = bf16_lo(pw[2 * r4 + 1]) * (dp[qb][r + 2] - d4[2]);
-          const float e3 = bf16_hi(pw[2 * r4 + 1]) * (dp[qb][r + 3] - d4[3]);
+          const float e0 = bf16_lo(pw[2 * r4]) * dp[qb][r + 0];
+          const float e1 = bf16_hi(pw[2 * r4]) * dp[qb][r + 1];
+          const float e2 = bf16_lo(pw[2 * r4 + 1]) * dp[qb][r + 2];
+          const float e3 = bf16_hi(pw[2 * r4 + 1]) * dp[qb][r + 3];
           u[2 * r4] = pack_bf16x2(e0, e1);
           u[2 * r4 + 1] = pack_bf16x2(e2, e3);
         }
@@ -582,7 +586,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(const float* __restri
 constexpr int dq_vslot(int L, int g) { return 1 + g * (L - 2) / 3; }
 
 // Also forms the per-row statistics the dK/dV kernel reads (it runs first): LSE2 = LSE*log2(e)
-// and D for its 128 rows, padding rows up to the sequence's multiple of 64 getting +inf and 0.
+// and -D for its 128 rows (negated: the dK/dV kernel starts its dP accumulators from it, so that
+// the products give dP - D directly), padding rows up to the sequence's multiple of 64 getting
+// +inf and 0.
 //
 // D.  dS = P (dP - D) takes D = rowsum(dO * O), known before the key walk, but O is stored in
 // bf16 and that D carries O's rounding, up to 2^-9 relative.  On the key that dominates a row
@@ -658,7 +664,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float lse2 = qi < Nq ? lse[sr.q + qi] * kLog2e : INFINITY;
   if (!REDO && h32 == 0 && qi < (Nq + 63) / 64 * 64) {
     st[qi] = lse2;
-    st[stat_half + qi] = dl;
+    st[stat_half + qi] = -dl;
   }
 
   f32x16 dq_acc[DB];
@@ -820,7 +826,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         ofs.toggle(STAGE);
       }
       dl = qi < Nq ? sum_xor32(dpart) : 0.f;
-      if (h32 == 0 && qi < Nq) st[stat_half + qi] = dl;
+      if (h32 == 0 && qi < Nq) st[stat_half + qi] = -dl;
       exact_d = true;
     }
   }
@@ -845,7 +851,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (t + 1 < ntiles) ofs.toggle(STAGE);
     }
     dl = qi < Nq ? sum_xor32(dpart) : 0.f;
-    if (h32 == 0 && qi < Nq) st[stat_half + qi] = dl;
+    if (h32 == 0 && qi < Nq) st[stat_half + qi] = -dl;
     // ofs is on the stage of tile ntiles-1 and tile ntiles-2 is still in the other stage.  At
     // tile t <= ntiles-2 the stage of tile t+1 is free again and takes tile t-1.
     for (int t = ntiles - 1; t >= 0; --t) {
@@ -906,7 +912,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dpart += pr * dpv[kb][r];
       }
     const float dex = sum_xor32(dpart);
-    if (h32 == 0 && qi < Nq) st[stat_half + qi] = dex;
+    if (h32 == 0 && qi < Nq) st[stat_half + qi] = -dex;
     bf16x8 dsv[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {

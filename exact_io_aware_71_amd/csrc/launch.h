@@ -23,8 +23,8 @@ struct FwdArgs {
 
 // Backward: dense [B,H,N,d] tensors (cu_q == nullptr, Nq == Nk == N) or packed
 // variable-length [H,total,d] tensors with offsets cu_q/cu_k [B+1] (Nq, Nk the totals, max_q,
-// max_k the longest sequences).  The workspace holds two fp32 halves (LSE*log2(e), then
-// D = rowsum(dO*O)) of `stat_half` floats; the rows of (b, h) start at (b*Hq + h)*stat_stride
+// max_k the longest sequences).  The workspace holds two fp32 halves (LSE*log2(e), then -D,
+// D = sum_j P_ij dP_ij = rowsum(dO*O)) of `stat_half` floats; the rows of (b, h) start at (b*Hq + h)*stat_stride
 // (dense, stat_stride = roundup(N, 64)) or at h*stat_stride + cu_q[b] + 64b (packed,
 // stat_stride = total_q + 64B), so every sequence owns roundup(len, 64) rows.
 struct BwdArgs {

@@ -135,7 +135,7 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void*
                               attn_dtype_t dtype, int causal, float scale, void* stream);
 
 /* Bytes of device workspace attn_bwd needs:
- *   - fp32 per-row statistics (LSE * log2(e) and D, see attn_bwd) for every query row padded
+ *   - fp32 per-row statistics (LSE * log2(e) and -D, see attn_bwd) for every query row padded
  *     to a multiple of 64: 2 * B * Hq * roundup(N, 64) * 4 bytes, rounded up to 256;
  *   - one 4-byte flag per wave of 32 query rows, B * Hq * ceil(N/128) * 4 * 4 bytes rounded up
  *     to 256 (a wave that meets a probability above 1/2 asks for D from its definition);
