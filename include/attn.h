@@ -157,10 +157,11 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  * Supported: BF16, d in {64, 128}.  Grouped-query heads ([OPT] §5.3, kv = h / (Hq/Hkv)): dk and
  * dv of a KV head are the sums of the gradients of the Hq/Hkv query heads sharing it.
  * D_i = sum_j P_ij dP_ij enters dS = P (dP - D).  It is taken as rowsum(dO * O) from the stored
- * O, except for the 128-query blocks that hold a row whose largest probability exceeds 1/2:
- * there the bf16 rounding of O would dominate the nearly cancelling dP - D of the dominant key,
- * so a second dQ launch forms D from its definition and computes dQ of the block again with it
- * (dK and dV use that D too).
+ * O, except where the bf16 rounding of O could dominate the nearly cancelling dP - D of a key
+ * that carries most of a row: 128-query blocks whose keys fit two 64-key tiles form D from its
+ * definition in the first dQ launch, and blocks that hold a row whose largest probability
+ * exceeds 1/2 get it from a second dQ launch, which also computes their dQ again (dK and dV use
+ * that D too).
  * Deterministic (no atomics).
  */
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
