@@ -30,10 +30,11 @@ for rocprofv3's FETCH_SIZE / WRITE_SIZE byte counters); --stream-read times a st
 a 4 GiB buffer (libexact_calib.so) at several grid sizes, the HBM read rate a kernel that only
 reads reaches on this GPU; --mfma-ceiling times a plain loop of dense bf16 MFMAs on every SIMD
 and reads the shader clock it runs at (the matrix-core rate such a loop reaches on this GPU).
---prefill-d64 times only the batched d=64 prefill, for a profile of its kernel.
+--prefill-d64 and --tiny-f32 time only the batched d=64 prefill or the tiny fp32 forward, for a
+profile of its kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-                       [--copy-calibration | --stream-read | --mfma-ceiling | --prefill-d64]
+                       [--copy-calibration | --stream-read | --mfma-ceiling | --prefill-d64 | --tiny-f32]
 """
 from __future__ import annotations
 
@@ -221,6 +222,38 @@ def mfma_ceiling(blocks=1024, iters=4096):
                       "TFLOPs_at_clock": PEAK_BF16_TFLOPS * ghz / 2.4, "workgroups": blocks, "iters": iters}))
 
 
+def tiny_f32(reps=200):
+    """Only the tiny fp32 forward (B=1 H=1 N=256 d=64, non-causal; seed 1001): 0.3 s of warm-up
+    calls, then `reps` timed calls; prints the mean ms per call.  For a profile of its kernel."""
+    import numpy as np
+    import torch
+    from exact_io_aware_71_amd import binding as attn
+    from synth import default_scale, make_prefill
+    attn.load()
+    tp = make_prefill(1, 1, 1, 256, 64, "f32", seed=1001)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(tp[x])).to("cuda:0") for x in ("q", "k", "v"))
+    to = torch.empty_like(tq)
+    tl = torch.empty((1, 1, 256), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        attn.attn_fwd(tq, tk, tv, False, default_scale(64), o=to, lse=tl)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"workload": "attn_fwd B=1 H=1 N=256 d=64 fp32 non-causal", "ms_per_call": ms,
+                      "TFLOPs": flops_fwd(1, 1, 256, 64, False) / (ms * 1e-3) / 1e12, "calls": reps}))
+
+
 def prefill_d64(reps=200):
     """Only the batched prefill (B=4, H=16, N=1024, d=64, causal, with LSE; seed 1002): 300 ms of
     warm-up calls, then `reps` timed calls; prints the mean ms.  For a profile of its kernel."""
@@ -270,6 +303,8 @@ def main():
                     help="only time a streaming read of a 4 GiB buffer (HBM read ceiling of a plain kernel)")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only time a plain loop of dense bf16 MFMAs and read the shader clock it runs at")
+    ap.add_argument("--tiny-f32", action="store_true",
+                    help="only time the tiny fp32 forward (B=1 H=1 N=256 d=64), for a profile of its kernel")
     ap.add_argument("--prefill-d64", action="store_true",
                     help="only time the batched d=64 prefill (B=4 H=16 N=1024 causal), for a profile of its kernel")
     args = ap.parse_args()
@@ -287,6 +322,9 @@ def main():
         return
     if args.mfma_ceiling:
         mfma_ceiling()
+        return
+    if args.tiny_f32:
+        tiny_f32()
         return
 
     import numpy as np

@@ -81,6 +81,8 @@ constexpr double kFwd128NarrowKeys = 2048.0;
 // Largest lane-partial row sum of one 32-key step accepted without moving the reference max
 // (so every probability stays below it).
 constexpr float kSumMax = 256.f;
+// fp32: below this many 128-row workgroups (one per CU), the split-key kernel runs instead.
+constexpr long long kFwdF32SplitGrid = 256;
 
 template <int D, int NW_, int BN_>
 struct IlvShape {
@@ -573,6 +575,151 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   }
 }
 
+// fp32 inputs with few query rows (a grid of 128-row tiles that would leave CUs idle, such as
+// one head of 256 queries): a workgroup takes 32 query rows and its four waves split the keys,
+// wave w walking the 32-key tiles w, w+4, w+8, ... with its own running max, sum and output.
+// The four partial results are merged through LDS at the end: with m = max_w m_w and
+// e_w = 2^(m_w - m), O = sum_w e_w O_w / sum_w e_w l_w, the same combination as for blocks of one
+// row ([OPT] §3.2.2), exact in real arithmetic.  Each wave keeps its own K/V tile in LDS (no
+// workgroup barrier in the walk) and loads its next tile into registers while it computes the
+// current one.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_split_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, SeqGeo geo, BlockMask /*dense only*/,
+    float scale_log2, int n_qtiles, int BH) {
+  constexpr int D = 64, BM = 32, BN = 32, P = D + 1, NW = 4;  // P: padded pitch in floats
+  constexpr int MP = 33;                                      // merge: [d][query] pitch
+  static_assert(NW * (D * MP + 2 * BM) <= NW * 2 * BN * P, "merge area fits the tiles");
+  __shared__ float smem[NW * 2 * BN * P];  // per wave: K tile, V tile; then the merge area
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  int bh, qt;
+  fwd_tile_of(blockIdx.x, BH, n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / Hq, hq = bh - b * Hq, hk = hq / (Hq / Hkv);
+  const SeqRows sr = seq_rows(geo, b, hq, Hq, hk, Hkv);
+  const int Nq = sr.lq, Nk = sr.lk;
+  const int q0 = qt * BM, qi = q0 + l32;
+  if (q0 >= Nq) return;  // query tile past the end of a shorter sequence
+  const float* qp = q + sr.q * D;
+  const float* kp = k + sr.k * D;
+  const float* vp = v + sr.k * D;
+  const int qd0 = q0 + (Nk - Nq), kmax = qi + (Nk - Nq);  // causal: query i sees keys <= i + Nk - Nq
+
+  float qr[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) qr[c] = (qi < Nq) ? qp[(size_t)qi * D + 2 * c + h32] : 0.f;
+  f32x16 acc[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { acc[0][r] = 0.f; acc[1][r] = 0.f; }
+  float m_run = -INFINITY, l_run = 0.f;
+  const int kv_end = CAUSAL ? min(Nk, q0 + BM + (Nk - Nq)) : Nk;
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  float* ks = smem + wave * (2 * BN * P);
+  float* vs = ks + BN * P;
+  // Tile rows 4j + lane/16 (j = 0..7), 16-byte chunk lane%16; rows past the last key read the
+  // last key (their scores are masked, so they get probability 0).
+  f32x4 pk[8], pv[8];
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = min(t * BN + 4 * j + (lane >> 4), Nk - 1);
+      pk[j] = *reinterpret_cast<const f32x4*>(kp + (size_t)row * D + 4 * (lane & 15));
+      pv[j] = *reinterpret_cast<const f32x4*>(vp + (size_t)row * D + 4 * (lane & 15));
+    }
+  };
+  if (wave < ntiles) fetch(wave);
+  for (int t = wave; t < ntiles; t += NW) {
+    const int t0 = t * BN;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ks[(4 * j + (lane >> 4)) * P + 4 * (lane & 15) + e] = pk[j][e];
+        vs[(4 * j + (lane >> 4)) * P + 4 * (lane & 15) + e] = pv[j][e];
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done before its reads
+    __builtin_amdgcn_wave_barrier();
+    if (t + NW < ntiles) fetch(t + NW);  // in flight during this tile
+    if (!CAUSAL || t0 <= qd0 + 31) {
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 2; ++c) s = mfma32_f32(ks[l32 * P + 2 * c + h32], qr[c], s);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kj = t0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        if (kj >= Nk || (CAUSAL && kj > kmax)) s[r] = -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[r] = fast_exp2(fmaf(s[r], scale_log2, -m_use)); rs += s[r]; }
+      l_run = fmaf(l_run, alpha, rs);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { acc[0][r] *= alpha; acc[1][r] *= alpha; }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * h32 + (r & 3);
+        acc[0] = mfma32_f32(vs[key * P + l32], s[r], acc[0]);
+        acc[1] = mfma32_f32(vs[key * P + 32 + l32], s[r], acc[1]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this tile's LDS reads are done before the next writes
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Merge.  Wave w's partial: mo[w][d * MP + query] (unnormalised O), then m_w and l_w per query.
+  const float lt = sum_xor32(l_run);
+  __syncthreads();  // every wave is done with its tiles
+  float* mo = smem + wave * (D * MP + 2 * BM);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mo[(db * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3)) * MP + l32] = acc[db][r];
+  if (h32 == 0) {
+    mo[D * MP + l32] = m_run;
+    mo[D * MP + BM + l32] = lt;
+  }
+  __syncthreads();
+  // Wave w finishes features 16w + 8 h32 .. +7 of query q0 + l32.
+  float mw[NW], ew[NW];
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mw[w] = smem[w * (D * MP + 2 * BM) + D * MP + l32];
+    m = fmaxf(m, mw[w]);
+  }
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    ew[w] = (m == -INFINITY) ? 0.f : fast_exp2(mw[w] - m);  // a row without keys: every e_w = 0
+    L = fmaf(ew[w], smem[w * (D * MP + 2 * BM) + D * MP + BM + l32], L);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (qi < Nq) {
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 16 * wave + 8 * h32 + e;
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) x = fmaf(ew[w], smem[w * (D * MP + 2 * BM) + d * MP + l32], x);
+      out[e] = x * inv;
+    }
+    float* op = o + (sr.q + qi) * D + 16 * wave + 8 * h32;
+    *reinterpret_cast<f32x4*>(op) = f32x4{out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<f32x4*>(op + 4) = f32x4{out[4], out[5], out[6], out[7]};
+    if (lse != nullptr && wave == 0 && h32 == 0) lse[sr.q + qi] = L > 0.f ? (m + fast_log2(L)) * kLn2 : -INFINITY;
+  }
+}
+
 // ------------------------------------------------------------------------- host launchers
 // Grid: one workgroup per (query tile, batch, head); query tiles cover the longest query
 // sequence and those past a shorter sequence's end exit at once.
@@ -598,8 +745,12 @@ static hipError_t launch_fwd_grid(FwdKernel<T> kern, int BM, int threads, const 
                 : (a.causal ? K<__VA_ARGS__, true, false> : K<__VA_ARGS__, false, false>))
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.dtype == 0)  // fp32, d = 64 (dense only)
+  if (a.dtype == 0) {  // fp32, d = 64 (dense only)
+    // A grid of 128-row tiles that leaves CUs idle takes 32-row tiles whose waves split the keys.
+    if ((long long)((a.max_q + 127) / 128) * a.B * a.Hq < kFwdF32SplitGrid)
+      return launch_fwd_grid<float>(a.causal ? fwd_f32_split_kernel<true> : fwd_f32_split_kernel<false>, 32, 256, a);
     return launch_fwd_grid<float>(a.causal ? fwd_f32_kernel<true> : fwd_f32_kernel<false>, 128, 256, a);
+  }
   if (a.d == 64) {  // four waves, 128-row tiles, 64-key tiles: two workgroups per CU
     using S = IlvShape<64, 4, 64>;
     return launch_fwd_grid<uint16_t>(XATTN_PICK(fwd_ilv_kernel, 64, S::NW, S::BN), S::BM, S::NW * 64, a);

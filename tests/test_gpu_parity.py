@@ -190,6 +190,25 @@ def test_fwd_ragged_fp32(gpu_lib, N, causal):
     assert err["max"] <= 5e-5 and err["lse"] <= 5e-5, err
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 2, 1000), (1, 3, 97), (2, 16, 1024)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp32_grids(gpu_lib, B, H, N, causal):
+    """fp32 on both of its kernels: small grids (fewer 128-row tiles than CUs) split each
+    workgroup's keys over its four waves and merge them, large ones (B=2 H=16 N=1024: 256 tiles)
+    take 128-row tiles; every element of the small shapes, sampled rows of the large one."""
+    print(f"fwd fp32 B={B} H={H} N={N} causal={causal}", flush=True)
+    inp = make_prefill(B, H, H, N, 64, "f32", seed=7000 + N + H)
+    o, lse = run_fwd(gpu_lib, inp, causal, 0.125)
+    if B * H * N <= 4096:
+        o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], 0.125, causal)
+    else:
+        rows = sample_rows(N, seed=7001, extra=56)
+        o, lse = o[:, :, rows], lse[:, :, rows]
+        o_ref, lse_ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], 0.125, causal, rows)
+    err = fwd_errors(o, o_ref, lse, lse_ref)
+    assert err["max"] <= 5e-5 and err["lse"] <= 5e-5, err  # the fp32 kernels keep fp32 precision
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_grouped_query(gpu_lib, d, causal):
