@@ -25,7 +25,9 @@
 //   * K/V tiles arrive ahead of use, so HBM/L2 latency hides behind compute ([OPT] §5.2):
 //     fwd_ilv_kernel (bf16, d = 64 and 128) copies them straight into LDS rings of four
 //     stages (buffer_load ... lds, no registers), K three tiles and V two tiles ahead, one
-//     barrier per tile; fwd_f32_kernel (fp32 inputs) is single-buffered.
+//     barrier per tile; fwd_f32_kernel (fp32 inputs) is single-buffered, and
+//     fwd_f32_split_kernel (fp32, grids too small to fill the CUs) splits each workgroup's keys
+//     over its waves, which load their next tile into registers during the current one.
 //   * fwd_ilv_kernel software-pipelines each wave: the MFMAs of P_{u-1} V_{u-1} and of S_{u+1}
 //     interleave with the vector work of the softmax of S_u in fixed slots.
 //   * Causal: tiles past the diagonal are never loaded, waves whose rows all precede a tile
