@@ -237,11 +237,12 @@ def test_fwd_closed_forms(gpu_lib):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("trend", ["rising", "falling", "spike"])
-def test_fwd_moving_running_max(gpu_lib, causal, trend):
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_moving_running_max(gpu_lib, causal, trend, d):
     """Inputs whose row maxima keep moving, so the kernels' lazily updated reference max has to
-    move many times (and by large amounts, for the spike) mid-row."""
+    move many times (and by large amounts, for the spike) mid-row; at d = 64 and 128."""
     from synth import bf16_bits_to_f32, f32_to_bf16_bits
-    B, H, N, d = 1, 2, 700, 128
+    B, H, N = 1, 2, 700
     inp = make_prefill(B, H, H, N, d, "bf16", seed=41)
     k = bf16_bits_to_f32(inp["k"]).reshape(B, H, N, d)
     ramp = np.linspace(0.2, 4.0, N, dtype=np.float32)
