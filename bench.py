@@ -288,6 +288,46 @@ def prefill_d64(reps=200):
                       "TFLOPs": flops_fwd(4, 16, 1024, 64, True) / (ms * 1e-3) / 1e12, "calls": reps}))
 
 
+def prefill_d64_sweep(reps=200):
+    """The causal d=64 forward on one batch of 16 heads at N = 128 .. 1024 (2 to 16 key tiles on
+    the longest walk, 16 to 128 workgroups, so at most one per CU) and on the batched prefill
+    (B=4): 300 ms of warm-up calls per shape, then `reps` timed calls; prints the mean ms per
+    shape (host-bound below about 10 us).  Under a kernel trace the grid sizes tell the shapes
+    apart: the kernel durations give the per-launch fixed cost and the per-tile time of a
+    workgroup alone on its CU."""
+    import numpy as np
+    import torch
+    from exact_io_aware_71_amd import binding as attn
+    from synth import default_scale, make_prefill
+    attn.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = []
+    for B, N in ((1, 128), (1, 256), (1, 512), (1, 1024), (4, 1024)):
+        bp = make_prefill(B, 16, 16, N, 64, "bf16", seed=1100 + N + B)
+        bq, bk, bv = (torch.from_numpy(np.ascontiguousarray(bp[x]).view(np.int16)).view(torch.bfloat16).to(dev)
+                      for x in ("q", "k", "v"))
+        bo = torch.empty_like(bq)
+        blse = torch.empty((B, 16, N), dtype=torch.float32, device=dev)
+
+        def run():
+            attn.attn_fwd(bq, bk, bv, True, default_scale(64), o=bo, lse=blse)
+
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append({"B": B, "H": 16, "N": N, "workgroups": B * 16 * ((N + 127) // 128),
+                    "ms": e0.elapsed_time(e1) / reps})
+    print(json.dumps({"workload": "attn_fwd d=64 causal with LSE, N sweep", "shapes": out, "calls": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +347,8 @@ def main():
                     help="only time the tiny fp32 forward (B=1 H=1 N=256 d=64), for a profile of its kernel")
     ap.add_argument("--prefill-d64", action="store_true",
                     help="only time the batched d=64 prefill (B=4 H=16 N=1024 causal), for a profile of its kernel")
+    ap.add_argument("--prefill-d64-sweep", action="store_true",
+                    help="only the causal d=64 forward at N = 128 .. 1024 (one batch of 16 heads) and the batched prefill")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
@@ -316,6 +358,9 @@ def main():
         return
     if args.stream_read:
         stream_read()
+        return
+    if args.prefill_d64_sweep:
+        prefill_d64_sweep()
         return
     if args.prefill_d64:
         prefill_d64()
