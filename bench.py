@@ -156,7 +156,7 @@ def stream_read(nbytes=4 << 30):
     out = torch.empty(1 << 16, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream()
     res = {}
-    for blocks in (1024, 2048, 4096, 8192, 16384):
+    for blocks in (2048, 4096, 8192, 16384, 32768):
         def run():
             rc = lib.calib_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, ctypes.c_void_p(stream.cuda_stream))
             if rc != 0:

@@ -70,12 +70,19 @@ attn_status_t from_hip(hipError_t e, const char* what) {
   return ok();
 }
 
-// Split choice for decode: enough workgroups to fill 256 CUs several times over, chunks
-// of whole 32-key blocks, at least 256 keys per chunk.
+// Split choice for decode (chunks of whole 32-key blocks): about 1024 workgroups, but chunks of
+// at least 2048 keys where that still leaves 256 workgroups (one per CU), and never chunks
+// under 256 keys.  Measured on the 2 GiB cache and on longer caches of fewer sequences (B=4,
+// L=32768; B=1, L=65536): 512-1024 workgroups of long chunks stream fastest, and chunks of
+// 1024 keys or fewer cost 7-25% there in partial results and their merge.
 int auto_splits(int B, int Hkv, int L) {
   const long long groups = (long long)B * Hkv;
-  const int max_by_len = (L + 255) / 256;
-  long long s = (2048 + groups - 1) / groups;
+  long long s = (1024 + groups - 1) / groups;
+  const long long long_chunks = (L + 2047) / 2048;
+  if (s > long_chunks) s = long_chunks;
+  const long long fill = (256 + groups - 1) / groups;
+  if (s < fill) s = fill;
+  const long long max_by_len = (L + 255) / 256;
   if (s > max_by_len) s = max_by_len;
   if (s < 1) s = 1;
   if (s > 64) s = 64;

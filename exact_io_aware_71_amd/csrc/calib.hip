@@ -1,8 +1,10 @@
 // Calibration kernels for the benchmark (not part of libexact_attn.so), so that the rates the
 // attention kernels reach can be set beside what plain kernels reach on the same GPU:
-//   * stream_read_kernel, a streaming read of a device buffer (HBM read rate).  Every thread
-//     reads 16-byte chunks at a grid stride, four loads in flight, and folds them into one
-//     word so that the loads cannot be removed; one word per workgroup is written.
+//   * stream_read_kernel, a streaming read of a device buffer (HBM read rate).  Each workgroup
+//     reads one contiguous share of the buffer, every thread eight 16-byte nontemporal loads in
+//     flight (the fastest of the plain forms measured: grid-stride loads, four or eight in
+//     flight, with and without the hint), folded into one word so that the loads cannot be
+//     removed; one word per workgroup is written.
 //   * mfma_loop_kernel, back-to-back v_mfma_f32_32x32x16_bf16 on four independent
 //     accumulators per wave (dense bf16 matrix-core rate), which also reads the shader-clock
 //     counter (s_memtime) and the 100 MHz reference counter (s_memrealtime) around its loop,
@@ -15,16 +17,20 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16, uint32_t* out) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t chunk = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t base = (size_t)blockIdx.x * chunk;
+  const size_t end = base + chunk < n16 ? base + chunk : n16;
+  size_t i = base + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^
-           d[2] ^ d[3];
+  for (; i + 7 * 256 < end; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) v[f] = __builtin_nontemporal_load(p + i + 256 * f);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc ^= v[f][0] ^ v[f][1] ^ v[f][2] ^ v[f][3];
   }
-  for (; i < n16; i += stride) {
-    const u32x4 a = p[i];
+  for (; i < end; i += 256) {
+    const u32x4 a = __builtin_nontemporal_load(p + i);
     acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
   }
   __shared__ uint32_t red[256];

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         u32x4 u = {0u, 0u, 0u, 0u};
-        if (key < kend) u = ld_global16(kp + (size_t)key * D + 32 * c + 8 * grp);
+        if (key < kend) u = ld_global_nt<u32x4>(kp + (size_t)key * D + 32 * c + 8 * grp);
         kraw[blk][c] = u;
       }
     }
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
       for (int r = 0; r < 4; ++r) {
         const int key = k0 + blk * 16 + 4 * grp + r;
         VRaw u = {};
-        if (key < kend) u = *reinterpret_cast<const VRaw*>(vp + (size_t)key * D + EPL * col);
+        if (key < kend) u = ld_global_nt<VRaw>(vp + (size_t)key * D + EPL * col);
         vraw[blk][r] = u;
       }
     f32x4 sc[2];
