@@ -17,7 +17,8 @@
 //   * P V on the vector ALU: lane (16*j + c) owns features [c*D/16, (c+1)*D/16) of keys
 //     4j + r; the probability p[h][key] sits in lane 16*j + h of the same 16-lane row and
 //     is broadcast with a DPP row_newbcast move.  V rows are read with coalesced 16-byte
-//     loads (D = 128) and no LDS staging.
+//     loads (D = 128) and no LDS staging.  K and V loads carry the nontemporal hint: the cache
+//     is read once per token, and streaming it past the caches reads HBM faster.
 //   * Online softmax per 32-key chunk ([OPT] §3.2.1); the four row groups of a wave and the
 //     four waves of a workgroup share one running max per head, so only the final
 //     cross-wave combine needs LDS.
