@@ -520,6 +520,45 @@ def test_bwd_short_peaky_rows(gpu_lib, B, Hq, Hkv, N, d, causal, seed):
     check_bwd(grads, inp, scale, causal, tag=f"short peaky N={N} d={d}")
 
 
+def uncancelled_scales(inp, scale, causal):
+    """Norms of dQ and dK with |P * dP| in place of dS = P * (dP - D): the size the gradients
+    would have without the cancellation in dP - D (fp64, from the inputs)."""
+    Q, K, V, dO = (oracle.upcast(inp[x]) for x in ("q", "k", "v", "dout"))
+    g = Q.shape[1] // K.shape[1]
+    K, V = np.repeat(K, g, axis=1), np.repeat(V, g, axis=1)
+    S = scale * np.einsum("bhid,bhjd->bhij", Q, K)
+    if causal:
+        n, m = S.shape[-2:]
+        S = np.where(np.arange(m)[None, :] <= np.arange(n)[:, None] + (m - n), S, -np.inf)
+    P = np.exp(S - S.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    aP = np.abs(P * np.einsum("bhid,bhjd->bhij", dO, V))
+    dq = scale * np.einsum("bhij,bhjd->bhid", aP, np.abs(K))
+    dk = scale * np.einsum("bhij,bhid->bhjd", aP, np.abs(Q))
+    return float(np.linalg.norm(dq)), float(np.linalg.norm(dk))
+
+
+@pytest.mark.parametrize("N,d,causal", [(3, 128, True), (3, 64, False), (100, 128, True), (333, 64, True),
+                                        (700, 128, False)])
+def test_bwd_cancelling_gradients(gpu_lib, N, d, causal):
+    """Logits x16 (Q and K x4): rows are one-hot to within e^-30, so dS = P (dP - D) cancels and
+    the exact dQ and dK can shrink to 1e-13 of the size they would have without the cancellation
+    (3-key causal rows), and a relative bound on them then measures fp32 rounding against
+    nothing.  dV keeps the relative bound; dQ and dK are held to it against the larger of their
+    own norm and 1e-3 of their uncancelled size (fp32 rounding of the uncancelled terms leaves a
+    few 1e-7 of it)."""
+    print(f"bwd cancelling N={N} d={d} causal={causal}", flush=True)
+    inp = make_prefill(1, 2, 1, N, d, "bf16", seed=8800 + N + d, with_dout=True, qk_mult=4.0)
+    scale = default_scale(d)
+    grads = run_fwd_bwd(gpu_lib, inp, causal, scale)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["dout"], scale, causal)
+    unc = uncancelled_scales(inp, scale, causal)
+    for name, g, r, u in zip(("dq", "dk", "dv"), grads, ref, unc + (None,)):
+        den = np.linalg.norm(r) if u is None else max(np.linalg.norm(r), 1e-3 * u)
+        err = float(np.linalg.norm(g - r) / den)
+        assert err <= BWD_REL_L2, (name, err)
+
+
 def test_bwd_from_oracle_forward(gpu_lib):
     """Feed the oracle's O (as bf16) and LSE into attn_bwd: isolates the backward kernels."""
     import torch
