@@ -383,13 +383,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  // Interleaved versions (no mask needed): 32 MFMA slots per tile.  dV wave: S of block 0,
-  // then S of block 1 while the vector ALU forms P of block 0, then dV of block 0 while it
-  // forms P of block 1, then dV of block 1.  The dK wave does the same with dP, dS and dK.
+  // Interleaved versions: 32 MFMA slots per tile.  dV wave: S of block 0, then S of block 1
+  // while the vector ALU forms P of block 0, then dV of block 0 while it forms P of block 1,
+  // then dV of block 1.  The dK wave does the same with dP, dS and dK.  On a diagonal tile the
+  // dV wave zeroes the probabilities of queries that do not see its key (causal), so the dK
+  // wave, whose dS = P * (dP - D) then vanishes there, needs no mask.
   constexpr int LA = kDkdvLookahead;
   constexpr bool kIlv = D == 128;  // the interleaved slot plan assumes 8 chunks, 4 blocks
-  auto dv_tile_ilv = [&](int vt, int cvt, int ch, int ct) __attribute__((always_inline)) {
+  auto dv_tile_ilv = [&](int vt, int t, int cvt, int ch, int ct) __attribute__((always_inline)) {
    if constexpr (kIlv) {  // only instantiated where the slot plan applies
+    const int q0 = t * BQ;
     const char* qs = smem + (vt % NS) * STAGE;
     const char* dos = qs + T::BYTES;
     const float* ls = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
@@ -434,6 +437,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = fast_exp2(fmaf(sv[qb][4 * r4 + e], scale_log2, -l4[e]));
+        // Causal, on a diagonal tile: register 4 r4 + e holds query qb0 + 8 r4 + 4 h32 + e,
+        // which sees key kj only if kj <= that query + doff.
+        const int qb0 = q0 + qb * 32 + doff;
+        if (CAUSAL && qb0 < kw0 + 31) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kj > qb0 + 8 * r4 + 4 * h32 + e) pv[e] = 0.f;
+        }
         u32x2 w;
         w[0] = pack_bf16x2(pv[0], pv[1]);
         w[1] = pack_bf16x2(pv[2], pv[3]);
@@ -524,12 +535,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int vt = 0; vt <= nvt; ++vt) {
     const bool more = vt + 1 < nvt;
     const int ch = more ? h_nxt : h_end, ct = more ? t_nxt : t_end;
-    const bool ilv_dv = kIlv && role == 0 && vt < nvt && !(CAUSAL && t_cur * BQ + doff < kw0 + 31);
+    const bool ilv_dv = kIlv && role == 0 && vt < nvt;
     const bool ilv_dk = kIlv && role == 1 && vt > 0;
     if (!(ilv_dv || ilv_dk) && more) copy_tile(vt + 1, h_nxt, t_nxt);
     if (role == 0) {
       if (vt < nvt) {
-        if (ilv_dv) dv_tile_ilv(vt, vt + 1, ch, ct);
+        if (ilv_dv) dv_tile_ilv(vt, t_cur, vt + 1, ch, ct);
         else dv_tile_plain(vt, t_cur);
       }
     } else if (vt > 0) {
