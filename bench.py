@@ -29,12 +29,15 @@ Calibration modes (no step): --copy-calibration runs plain 1 GiB device copies (
 for rocprofv3's FETCH_SIZE / WRITE_SIZE byte counters); --stream-read times a streaming read of
 a 4 GiB buffer (libexact_calib.so) at several grid sizes, the HBM read rate a kernel that only
 reads reaches on this GPU; --mfma-ceiling times a plain loop of dense bf16 MFMAs on every SIMD
-and reads the shader clock it runs at (the matrix-core rate such a loop reaches on this GPU).
---prefill-d64 and --tiny-f32 time only the batched d=64 prefill or the tiny fp32 forward, for a
-profile of its kernel.
+and reads the shader clock it runs at (the matrix-core rate such a loop reaches on this GPU);
+--atomic-add times fp32 atomic adds in 64 x 128 tiles into a dQ-sized accumulator (the rate a
+backward that summed dQ with atomics would depend on).  --prefill-d64, --prefill-d64-sweep and
+--tiny-f32 time only the batched d=64 prefill (or the causal d=64 forward over N = 128 .. 1024)
+or the tiny fp32 forward, for a profile of its kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-                       [--copy-calibration | --stream-read | --mfma-ceiling | --prefill-d64 | --tiny-f32]
+                       [--copy-calibration | --stream-read | --mfma-ceiling | --atomic-add |
+                        --prefill-d64 | --prefill-d64-sweep | --tiny-f32]
 """
 from __future__ import annotations
 
@@ -140,6 +143,42 @@ def copy_calibration(nbytes=1 << 30, reps=5):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def atomic_add(heads=32, N=4096, reps=16):
+    """fp32 atomic adds of 64 x 128 tiles into a [heads, N, 128] fp32 accumulator (the dQ of the
+    training workload's shape) with the calibration kernel at two grid sizes: GB/s of added
+    floats (4 bytes each) per grid, median of 5 timed launches after 100 ms of warm-up."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_71_amd", "libexact_calib.so"))
+    lib.calib_atomic_add.restype = ctypes.c_int
+    lib.calib_atomic_add.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    acc = torch.zeros(heads * N * 128, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for blocks in (1024, 4096):
+        def run():
+            rc = lib.calib_atomic_add(acc.data_ptr(), heads, N, reps, blocks, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"calib_atomic_add failed ({rc})")
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:
+            run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[2]
+        res[blocks] = blocks * reps * 64 * 128 * 4 / (ms * 1e-3) / 1e9
+    print(json.dumps({"atomic_add_fp32_GBps_by_workgroups": res, "tile": "64 x 128 fp32", "tiles_per_workgroup": reps,
+                      "accumulator": f"[{heads}, {N}, 128] fp32"}))
 
 
 def stream_read(nbytes=4 << 30):
@@ -339,6 +378,8 @@ def main():
                          "variable-length decode) so that a profile holds the timed step only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (reference for HBM byte counters)")
+    ap.add_argument("--atomic-add", action="store_true",
+                    help="only time fp32 atomic adds in 64 x 128 tiles (calibration)")
     ap.add_argument("--stream-read", action="store_true",
                     help="only time a streaming read of a 4 GiB buffer (HBM read ceiling of a plain kernel)")
     ap.add_argument("--mfma-ceiling", action="store_true",
@@ -355,6 +396,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.atomic_add:
+        atomic_add()
         return
     if args.stream_read:
         stream_read()

@@ -5,6 +5,8 @@
 //     flight (the fastest of the plain forms measured: grid-stride loads, four or eight in
 //     flight, with and without the hint), folded into one word so that the loads cannot be
 //     removed; one word per workgroup is written.
+//   * atomic_add_kernel, fp32 atomic adds in 64 x 128 tiles (the atomic rate that a backward
+//     summing dQ shares with atomics would depend on).
 //   * mfma_loop_kernel, back-to-back v_mfma_f32_32x32x16_bf16 on four independent
 //     accumulators per wave (dense bf16 matrix-core rate), which also reads the shader-clock
 //     counter (s_memtime) and the 100 MHz reference counter (s_memrealtime) around its loop,
@@ -78,6 +80,20 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
   }
 }
 
+// fp32 atomic adds (no return value) into an accumulator of `heads` x N rows of 128 floats, in
+// tiles of 64 rows: the traffic a backward would make that summed each key block's dQ share into
+// one fp32 dQ with atomics.  Workgroup w adds `reps` tiles of head w % heads; 256 threads add
+// 32 floats each per tile.
+__global__ __launch_bounds__(256) void atomic_add_kernel(float* __restrict__ acc, int heads, int N, int reps) {
+  const int h = blockIdx.x % heads, ntile = N / 64;
+  float* base = acc + (size_t)h * N * 128;
+  for (int r = 0; r < reps; ++r) {
+    float* tp = base + (size_t)((blockIdx.x / heads + 7 * r) % ntile) * (64 * 128);
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) atomicAdd(tp + 256 * i + threadIdx.x, 1.0f);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,6 +116,16 @@ int calib_mfma(int blocks, int iters, float* sink, unsigned long long* ticks, vo
   if (sink == nullptr || ticks == nullptr || blocks <= 0 || iters <= 0 || iters % 2 != 0)
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, sink, ticks);
+  return (int)hipGetLastError();
+}
+
+// Runs `blocks` workgroups of atomic_add_kernel on `acc` (device, heads * N * 128 floats; N a
+// positive multiple of 64), each adding `reps` tiles of 64 x 128 floats.  Returns the
+// hipError_t of the launch.
+int calib_atomic_add(float* acc, int heads, int N, int reps, int blocks, void* stream) {
+  if (acc == nullptr || heads <= 0 || N < 64 || N % 64 != 0 || reps <= 0 || blocks <= 0)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(atomic_add_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, acc, heads, N, reps);
   return (int)hipGetLastError();
 }
 

@@ -225,8 +225,8 @@ def test_binding_raises_typed_error():
 
 
 def test_calibration_library_loads_and_validates():
-    """The benchmark's calibration library (streaming read, MFMA loop) loads, exports both
-    entry points and rejects bad arguments before launching anything."""
+    """The benchmark's calibration library (streaming read, MFMA loop, atomic adds) loads,
+    exports its entry points and rejects bad arguments before launching anything."""
     from exact_io_aware_71_amd import build
     calib = ctypes.CDLL(build.CALIB_LIB)
     calib.calib_stream_read.restype = ctypes.c_int
@@ -241,3 +241,10 @@ def test_calibration_library_loads_and_validates():
     assert calib.calib_mfma(4, 8, None, P, None) == invalid
     assert calib.calib_mfma(4, 7, P, P, None) == invalid
     assert calib.calib_mfma(0, 8, P, P, None) == invalid
+    calib.calib_atomic_add.restype = ctypes.c_int
+    calib.calib_atomic_add.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    assert calib.calib_atomic_add(None, 32, 4096, 16, 1024, None) == invalid
+    assert calib.calib_atomic_add(P, 32, 100, 16, 1024, None) == invalid  # N not a multiple of 64
+    assert calib.calib_atomic_add(P, 0, 4096, 16, 1024, None) == invalid
+    assert calib.calib_atomic_add(P, 32, 4096, 16, 0, None) == invalid
