@@ -393,9 +393,16 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int w = 0; w < 4; ++w) p[w] = fast_exp2(fmaf(sc[4 * jq + w], scale_log2, -m_run));
             uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
-            // fp32 row sums (summing the bf16-rounded values would cost the LSE up to 2^-9).
-            rs0 += p[0] + p[2];
-            rs1 += p[1] + p[3];
+            // fp32 row sums (summing the bf16-rounded values would cost the LSE up to 2^-9).  The
+            // first group assigns: adding it to 0.f is not an identity for the compiler (signed
+            // zeros), so it would cost two adds per step.
+            if constexpr (jq == 0) {
+              rs0 = p[0] + p[2];
+              rs1 = p[1] + p[3];
+            } else {
+              rs0 += p[0] + p[2];
+              rs1 += p[1] + p[3];
+            }
             // Keeps this step's vector work in its slot (the compiler would otherwise sink it).
             asm volatile("" : "+v"(w0), "+v"(w1), "+v"(rs0), "+v"(rs1));
             pc[jq / 2][2 * (jq % 2)] = w0;
@@ -423,16 +430,15 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
-        rs0 = 0.f;
-        rs1 = 0.f;
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           float pv[4];
 #pragma unroll
           for (int w = 0; w < 4; ++w) pv[w] = fast_exp2(fmaf(sc[4 * jq + w], scale_log2, -m_new));
           const uint32_t w0 = pack_bf16x2(pv[0], pv[1]), w1 = pack_bf16x2(pv[2], pv[3]);
-          rs0 += pv[0] + pv[2];
-          rs1 += pv[1] + pv[3];
+          const float a0 = pv[0] + pv[2], a1 = pv[1] + pv[3];
+          rs0 = jq == 0 ? a0 : rs0 + a0;
+          rs1 = jq == 0 ? a1 : rs1 + a1;
           pc[jq / 2][2 * (jq % 2)] = w0;
           pc[jq / 2][2 * (jq % 2) + 1] = w1;
         }
