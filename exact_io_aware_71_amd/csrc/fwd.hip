@@ -333,6 +333,15 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
+  // Operands in flight (read L products ahead of their use, across step boundaries).  Step 0's
+  // first ones are V block -1 (stage NS-1, zeroed; its second half with 64-key tiles).
+  static_assert(L <= NPV, "the operands read across a step boundary are V^T operands");
+  bf16x8 buf[L];
+  {
+    const char* vs0 = smem + ((NS - 1) * TILE + (SPT - 1) * 32 * (2 * D));
+    static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(vs0, vs0, jc); });
+  }
+
   // Step u (phase ph of tile t = u / SPT): sc = S_u (complete), sn <- S_{u+1}, pp = P_{u-1},
   // pc <- P_u; the step's share of the tile's copy list (step_copy).  Tiles past the end are
   // copied too, clamped to the last key, into stages nobody reads any more, so every step
@@ -358,9 +367,10 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2, 2))
       constexpr int vst = SPT == 2 ? (st + NS - 1 + ph) % NS : (st + NS - 1) % NS, vhalf = SPT == 2 ? 1 - ph : 0;
       const char* ks = smem + (kst * TILE + khalf * 32 * (2 * D));
       const char* vs = smem + (vst * TILE + vhalf * 32 * (2 * D));  // V ring base is in ofs.v
+      // The next step's V block is V_u: stage st, half ph.  It has landed (it is read in this
+      // tile or the next one) and no copy overwrites its stage before the next tile's barrier.
+      const char* nvs = smem + (st * TILE + ph * 32 * (2 * D));
       float rs0 = 0.f, rs1 = 0.f;
-      bf16x8 buf[L];
-      static_for<L>([&](auto jc) { buf[decltype(jc)::value] = operand(ks, vs, jc); });
       sched_fence();
       static_for<NMF>([&](auto ic) {
         constexpr int j = decltype(ic)::value;
@@ -379,7 +389,9 @@ __global__ __launch_bounds__(64 * NW_) __attribute__((amdgpu_waves_per_eu(2, 2))
             sn = mfma32(buf[j % L], qreg[c], sn);
           }
         }
+        // Operand reads L slots ahead; the last L slots read the next step's first operands.
         if constexpr (j + L < NMF) buf[j % L] = operand(ks, vs, std::integral_constant<int, j + L>{});
+        else buf[j % L] = operand(ks, nvs, std::integral_constant<int, j + L - NMF>{});
         // Vector work: the exponentials of S_u, four per group.  d = 128 (16 slots): spread
         // evenly over slots 1 .. 14 (1, 4, 7, 10).  d = 64 (8 slots): every other slot from 0
         // on, so that the chain of S_{u+1} products in the second half of the step also runs
