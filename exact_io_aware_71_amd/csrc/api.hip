@@ -314,7 +314,7 @@ size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int L, i
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || L <= 0 || d <= 0 || num_splits < 0) return 0;
   int splits, kps;
   decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
-  const size_t rows = (size_t)splits * xattn::decode_partials_per_split(T, Hq / Hkv) * B * Hq * T;
+  const size_t rows = xattn::decode_partial_rows(splits, T, Hq / Hkv, (size_t)B * Hq * T);
   return align_up(rows * d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
 }
 
@@ -387,7 +387,7 @@ static attn_status_t decode_impl(const void* q, const void* k_cache, const void*
   decode_plan(L, num_splits == 0 ? auto_splits(B, Hkv, L) : num_splits, &splits, &kps);
   if ((long long)B * Hkv * ((T * (Hq / Hkv) + 31) / 32) * splits > 0x7fffffffLL)
     return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large");
-  const size_t rows = (size_t)splits * xattn::decode_partials_per_split(T, Hq / Hkv) * B * Hq * T;
+  const size_t rows = xattn::decode_partial_rows(splits, T, Hq / Hkv, (size_t)B * Hq * T);
   float* part_o = (float*)workspace;
   float* part_lse = (float*)((char*)workspace + align_up(rows * d * sizeof(float), 256));
   xattn::DecodeArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, L, d, scale, splits, kps, part_o, part_lse,

@@ -24,6 +24,9 @@
 //     cross-wave combine needs LDS.
 //   * Each chunk writes (O_s normalised, lse_s); the merge kernel combines the chunks with
 //     weights 2^(lse_s - max) — exact by the order independence of [OPT] §3.2.2.
+//   * Sequences of their own lengths: the workgroups share the 32-key blocks of all groups
+//     equally (stream-K), so long and short sequences load the chip evenly; a workgroup may
+//     write partials of several groups, and decode_merge_sk_kernel gathers them.
 //   * Multi-token decode: T new tokens per sequence; the MFMA rows are the T x g (token,
 //     head) pairs of the group, so the cache is still read once per group.  With the causal
 //     mask aligned at the bottom right, token t sees keys j <= len - T + t.  Up to 8 rows the
@@ -39,8 +42,10 @@ namespace xattn {
 
 constexpr int kDecWaves = 4;
 constexpr float kDecLazy = 8.f;
+// 32-key blocks of a sequence of len keys (clamped to [0, L]).
+__device__ __forceinline__ int dec_blocks(int len, int L) { return (min(max(len, 0), L) + 31) >> 5; }
 
-template <int D, int GP>
+template <int D, int GP, bool SK>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq, int Hkv, int L,
@@ -50,169 +55,260 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(
   __shared__ float s_m[kDecWaves][GP];
   __shared__ float s_l[kDecWaves][GP];
   __shared__ float s_acc[kDecWaves][GP][D];
+  __shared__ int s_pre[SK ? kDecSkMaxB + 1 : 1];  // stream-K: 32-key blocks of sequences < b
+  __shared__ int s_scan[SK ? kDecWaves * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int g = Hq / Hkv, R = T * g;  // MFMA row r < R: token r / g of head kvh*g + r % g
-  const int split = blockIdx.x % splits;
-  const int bk = blockIdx.x / splits;  // b * Hkv + kv head
-  const int b = bk / Hkv, kvh = bk - b * Hkv;
-  // Sequence b attends to the first len keys of its cache (all L without seqlens).
-  const int len = seqlens != nullptr ? min(max(seqlens[b], 0), L) : L;
-  const int kbeg = split * keys_per_split;
-  const int kend = max(kbeg, min(len, kbeg + keys_per_split));
-  const uint16_t* kp = kc + (size_t)bk * L * D;
-  const uint16_t* vp = vc + (size_t)bk * L * D;
+  // One key range [kbeg, kend) of group (b, kv head kvh): the rows' partial (O normalised,
+  // base-2 LSE) goes to partial row prow(h, tok) of MFMA row h.
+  auto chunk = [&](int b, int kvh, int len, int kbeg, int kend, auto prow) __attribute__((always_inline)) {
+    const size_t bk = (size_t)b * Hkv + kvh;
+    const uint16_t* kp = kc + bk * L * D;
+    const uint16_t* vp = vc + bk * L * D;
 
-  // Causal: the last key row col's token sees (rows past R see every key; they are never
-  // written).
-  const int ctok = col / g;
-  const int klast = (causal && col < R) ? len - T + ctok : L;
-  bf16x8 qB[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c) {
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (col < R)
-      u = ld_global16(q + ((size_t)(b * Hq + kvh * g + col - ctok * g) * T + ctok) * D + 32 * c + 8 * grp);
-    qB[c] = as_bf16x8(u);
-  }
+    // Causal: the last key row col's token sees (rows past R see every key; they are never
+    // written).
+    const int ctok = col / g;
+    const int klast = (causal && col < R) ? len - T + ctok : L;
+    bf16x8 qB[DC];
+  #pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (col < R)
+        u = ld_global16(q + ((size_t)(b * Hq + kvh * g + col - ctok * g) * T + ctok) * D + 32 * c + 8 * grp);
+      qB[c] = as_bf16x8(u);
+    }
 
-  // The running max starts finite (kMaxInit), so rows whose keys a chunk masks entirely get
-  // probability 0 there, and a row without any key ends with l = 0.
-  float m_run = kMaxInit, l_run = 0.f;
-  float acc[GP][EPL];
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    // The running max starts finite (kMaxInit), so rows whose keys a chunk masks entirely get
+    // probability 0 there, and a row without any key ends with l = 0.
+    float m_run = kMaxInit, l_run = 0.f;
+    float acc[GP][EPL];
+  #pragma unroll
+    for (int h = 0; h < GP; ++h)
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
 
-  const int nchunks = (kend - kbeg + 31) / 32;
-  for (int ci = wave; ci < nchunks; ci += kDecWaves) {
-    const int k0 = kbeg + ci * 32;
-    // Issue this chunk's K and V loads together (V is consumed after the softmax), so each
-    // wave keeps 2 x 8 KB in flight.
-    u32x4 kraw[2][DC];
-    using VRaw = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
-    VRaw vraw[2][4];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int key = k0 + blk * 16 + col;
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (key < kend) u = ld_global_nt<u32x4>(kp + (size_t)key * D + 32 * c + 8 * grp);
-        kraw[blk][c] = u;
+    const int nchunks = (kend - kbeg + 31) / 32;
+    for (int ci = wave; ci < nchunks; ci += kDecWaves) {
+      const int k0 = kbeg + ci * 32;
+      // Issue this chunk's K and V loads together (V is consumed after the softmax), so each
+      // wave keeps 2 x 8 KB in flight.
+      u32x4 kraw[2][DC];
+      using VRaw = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
+      VRaw vraw[2][4];
+  #pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int key = k0 + blk * 16 + col;
+  #pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          u32x4 u = {0u, 0u, 0u, 0u};
+          if (key < kend) u = ld_global_nt<u32x4>(kp + (size_t)key * D + 32 * c + 8 * grp);
+          kraw[blk][c] = u;
+        }
       }
-    }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + blk * 16 + 4 * grp + r;
-        VRaw u = {};
-        if (key < kend) u = ld_global_nt<VRaw>(vp + (size_t)key * D + EPL * col);
-        vraw[blk][r] = u;
+  #pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + blk * 16 + 4 * grp + r;
+          VRaw u = {};
+          if (key < kend) u = ld_global_nt<VRaw>(vp + (size_t)key * D + EPL * col);
+          vraw[blk][r] = u;
+        }
+      f32x4 sc[2];
+  #pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int c = 0; c < DC; ++c) sc[blk] = mfma16(as_bf16x8(kraw[blk][c]), qB[c], sc[blk]);
       }
-    f32x4 sc[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < DC; ++c) sc[blk] = mfma16(as_bf16x8(kraw[blk][c]), qB[c], sc[blk]);
-    }
-    // Lane (16*grp + col): head col, keys k0 + 16*blk + 4*grp + r.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + blk * 16 + 4 * grp + r;
-        if (key >= kend || key > klast) sc[blk][r] = -INFINITY;
-        mx = fmaxf(mx, sc[blk][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mx *= scale_log2;
-    // Lazy reference max (as in the forward kernel): move m_run and rescale only when some
-    // head's chunk max exceeds it by more than 2^kDecLazy; the result is unchanged.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kDecLazy) != 0) {
-      const float m_new = fmaxf(m_run, mx);  // finite: m_run starts at kMaxInit
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      static_for<GP>([&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        const float a_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= a_h;
-      });
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(sc[blk][r], scale_log2, -m_run));
-        sc[blk][r] = p;
-        rs += p;
-      }
-    l_run += rs;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float vf[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL / 2; ++e) { vf[2 * e] = bf16_lo(vraw[blk][r][e]); vf[2 * e + 1] = bf16_hi(vraw[blk][r][e]); }
-        const float pr = sc[blk][r];
+      // Lane (16*grp + col): head col, keys k0 + 16*blk + 4*grp + r.
+      float mx = -INFINITY;
+  #pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + blk * 16 + 4 * grp + r;
+          if (key >= kend || key > klast) sc[blk][r] = -INFINITY;
+          mx = fmaxf(mx, sc[blk][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= scale_log2;
+      // Lazy reference max (as in the forward kernel): move m_run and rescale only when some
+      // head's chunk max exceeds it by more than 2^kDecLazy; the result is unchanged.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kDecLazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);  // finite: m_run starts at kMaxInit
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
         static_for<GP>([&](auto hc) {
           constexpr int h = decltype(hc)::value;
-          const float p_h = row_bcast<h>(pr);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p_h, vf[e], acc[h][e]);
+          const float a_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= a_h;
         });
       }
-  }
+      float rs = 0.f;
+  #pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(sc[blk][r], scale_log2, -m_run));
+          sc[blk][r] = p;
+          rs += p;
+        }
+      l_run += rs;
+  #pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float vf[EPL];
+  #pragma unroll
+          for (int e = 0; e < EPL / 2; ++e) { vf[2 * e] = bf16_lo(vraw[blk][r][e]); vf[2 * e + 1] = bf16_hi(vraw[blk][r][e]); }
+          const float pr = sc[blk][r];
+          static_for<GP>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const float p_h = row_bcast<h>(pr);
+  #pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p_h, vf[e], acc[h][e]);
+          });
+        }
+    }
 
-  // Combine the four row groups of the wave (they share m_run), then the four waves.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float x = acc[h][e] + __shfl_xor(acc[h][e], 16);
-      acc[h][e] = x + __shfl_xor(x, 32);
-    }
-  if (grp == 0) {
-#pragma unroll
+    // Combine the four row groups of the wave (they share m_run), then the four waves.
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+  #pragma unroll
     for (int h = 0; h < GP; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][h][EPL * col + e] = acc[h][e];
-  }
-  if (lane < GP) {
-    s_m[wave][lane] = m_run;
-    s_l[wave][lane] = l_tot;
-  }
-  __syncthreads();
-  for (int i = tid; i < R * D; i += kDecWaves * 64) {
-    const int h = i / D, d = i - h * D;  // MFMA row h: token h / g, head kvh*g + h % g
-    float M = kMaxInit;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float wt = fast_exp2(s_m[w][h] - M);  // a wave that saw no key has l = 0
-      num = fmaf(wt, s_acc[w][h][d], num);
-      den = fmaf(wt, s_l[w][h], den);
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = acc[h][e] + __shfl_xor(acc[h][e], 16);
+        acc[h][e] = x + __shfl_xor(x, 32);
+      }
+    if (grp == 0) {
+  #pragma unroll
+      for (int h = 0; h < GP; ++h)
+  #pragma unroll
+        for (int e = 0; e < EPL; ++e) s_acc[wave][h][EPL * col + e] = acc[h][e];
     }
-    const int tok = h / g;
-    const size_t row = ((size_t)(split * B + b) * Hq + kvh * g + h - tok * g) * T + tok;
-    // A chunk holding no key of this row: partial O = 0, lse = -inf (weight 0 in the merge).
-    const bool empty = !(den > 0.f);
-    part_o[row * D + d] = empty ? 0.f : num / den;
-    if (d == 0) part_lse[row] = empty ? -INFINITY : M + fast_log2(den);
+    if (lane < GP) {
+      s_m[wave][lane] = m_run;
+      s_l[wave][lane] = l_tot;
+    }
+    __syncthreads();
+    for (int i = tid; i < R * D; i += kDecWaves * 64) {
+      const int h = i / D, d = i - h * D;  // MFMA row h: token h / g, head kvh*g + h % g
+      float M = kMaxInit;
+  #pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
+      float num = 0.f, den = 0.f;
+  #pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float wt = fast_exp2(s_m[w][h] - M);  // a wave that saw no key has l = 0
+        num = fmaf(wt, s_acc[w][h][d], num);
+        den = fmaf(wt, s_l[w][h], den);
+      }
+      const int tok = h / g;
+      const size_t row = prow(h, tok);
+      // A chunk holding no key of this row: partial O = 0, lse = -inf (weight 0 in the merge).
+      const bool empty = !(den > 0.f);
+      part_o[row * D + d] = empty ? 0.f : num / den;
+      if (d == 0) part_lse[row] = empty ? -INFINITY : M + fast_log2(den);
+    }
+  };
+
+  if constexpr (!SK) {
+    // Workgroup (b*Hkv + kv head, key chunk split), the group fastest: workgroups go to the
+    // XCDs in turn, so each XCD gets every split of its groups, short and long alike when the
+    // sequences have their own lengths (with the split fastest and two splits, four XCDs got
+    // every full first chunk and the other four only the partial second ones; 4-7% faster on
+    // lengths uniform in [L/2, L], no change with equal lengths).
+    const int BK = B * Hkv;
+    const int split = blockIdx.x / BK;
+    const int bk = blockIdx.x - split * BK;  // b * Hkv + kv head
+    const int b = bk / Hkv, kvh = bk - b * Hkv;
+    // Sequence b attends to the first len keys of its cache (all L without seqlens).
+    const int len = seqlens != nullptr ? min(max(seqlens[b], 0), L) : L;
+    const int kbeg = split * keys_per_split;
+    const int kend = max(kbeg, min(len, kbeg + keys_per_split));
+    chunk(b, kvh, len, kbeg, kend, [&](int h, int tok) {
+      return ((size_t)(split * B + b) * Hq + kvh * g + h - tok * g) * T + tok;
+    });
+  } else {
+    // Stream-K split for sequences of their own lengths: the 32-key blocks of all groups, in
+    // (b, kv head) order, are cut into gridDim.x equal ranges, so every workgroup reads the
+    // same number of blocks whatever the lengths.  Workgroup w takes blocks
+    // [w NB / G, (w+1) NB / G) and writes one partial per group it meets, to slot w + k
+    // (k = b*Hkv + kv head; unique, since along the blocks neither w nor k decreases), rows
+    // slot * R + h.  decode_merge_sk_kernel finds a group's workgroups from the same sums.
+    static_assert(kDecWaves * 64 == 256, "four values per lane in the scan of wave 0");
+    constexpr int NT = kDecWaves * 64;
+    const int per = (B + NT - 1) / NT;  // sequences per thread (B <= kDecSkMaxB)
+    int loc = 0;
+    for (int i = 0; i < per; ++i) {
+      const int bb = tid * per + i;
+      if (bb < B) loc += dec_blocks(seqlens[bb], L);
+    }
+    s_scan[tid] = loc;
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefix of the 256 per-thread counts
+      const int v0 = s_scan[4 * lane], v1 = s_scan[4 * lane + 1], v2 = s_scan[4 * lane + 2], v3 = s_scan[4 * lane + 3];
+      const int sum = v0 + v1 + v2 + v3;
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      const int ex = incl - sum;
+      s_scan[4 * lane] = ex;
+      s_scan[4 * lane + 1] = ex + v0;
+      s_scan[4 * lane + 2] = ex + v0 + v1;
+      s_scan[4 * lane + 3] = ex + v0 + v1 + v2;
+    }
+    __syncthreads();
+    int run = s_scan[tid];
+    for (int i = 0; i < per; ++i) {
+      const int bb = tid * per + i;
+      if (bb < B) {
+        s_pre[bb] = run;
+        run += dec_blocks(seqlens[bb], L);
+      }
+    }
+    if (tid == NT - 1) s_pre[B] = run;  // the total (the last thread's range ends at or past B)
+    __syncthreads();
+    const long long NB = (long long)Hkv * s_pre[B], G = gridDim.x, w = blockIdx.x;
+    const long long lo = w * NB / G, hi = (w + 1) * NB / G;
+    if (lo < hi) {
+      // The sequence holding block lo: the largest b with Hkv * s_pre[b] <= lo (it has blocks).
+      int b = 0;
+      for (int top = B - 1; b < top;) {
+        const int m = (b + top + 1) >> 1;
+        if ((long long)Hkv * s_pre[m] <= lo) b = m;
+        else top = m - 1;
+      }
+      int nb = s_pre[b + 1] - s_pre[b];
+      int kvh = (int)((lo - (long long)Hkv * s_pre[b]) / nb);
+      long long S = (long long)Hkv * s_pre[b] + (long long)kvh * nb;  // first block of the group
+      while (S < hi) {
+        const long long x0 = S > lo ? S : lo, x1 = S + nb < hi ? S + nb : hi;
+        const int len = min(max(seqlens[b], 0), L);
+        const int kbeg = (int)(x0 - S) * 32, kend = min(len, (int)(x1 - S) * 32);
+        const size_t slot = (size_t)w + (size_t)b * Hkv + kvh;
+        chunk(b, kvh, len, kbeg, kend, [&](int h, int) { return slot * R + h; });
+        __syncthreads();  // the next group's combine reuses s_m, s_l and s_acc
+        if (++kvh == Hkv) {
+          kvh = 0;
+          do { ++b; } while (b < B && s_pre[b + 1] == s_pre[b]);
+          if (b >= B) break;
+          nb = s_pre[b + 1] - s_pre[b];
+        }
+        S = (long long)Hkv * s_pre[b] + (long long)kvh * nb;
+      }
+    }
   }
 }
 
@@ -239,7 +335,9 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
   const int g = Hq / Hkv, R = T * g, nrc = (R + 31) / 32;
-  // Workgroup (b*Hkv + kv head, 32-row chunk rc of the group's R rows, key chunk split).
+  // Workgroup (b*Hkv + kv head, 32-row chunk rc of the group's R rows, key chunk split); the
+  // split fastest (the group-fastest order of decode_split_kernel measured 3% slower on the
+  // multi-token workload with equal lengths).
   const int split = blockIdx.x % splits;
   const int rc = (blockIdx.x / splits) % nrc;
   const int bk = blockIdx.x / (splits * nrc);  // b * Hkv + kv head
@@ -388,10 +486,83 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
   if (lse != nullptr && d == 0) lse[row] = empty ? -INFINITY : (M + fast_log2(den)) * kLn2;
 }
 
+// Merge of the stream-K partials (decode_split_kernel with SK): row (b, head, token) of group
+// k = b*Hkv + kv head gathers the partials of the workgroups whose block range meets the
+// group's blocks [S, E), from slot w + k, with the prefix sums the split kernel used.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_sk_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, uint16_t* __restrict__ o,
+    float* __restrict__ lse, const int* __restrict__ seqlens, int B, int Hq, int Hkv, int T, int L, int G) {
+  __shared__ int s_red[2][D / 64];
+  const int row = blockIdx.x, d = threadIdx.x, lane = d & 63, wv = d >> 6;
+  const int tok = row % T, bh = row / T, b = bh / Hq, head = bh - b * Hq;
+  const int g = Hq / Hkv, kvh = head / g, R = T * g, h = tok * g + head - kvh * g;
+  int before = 0, total = 0;
+  for (int i = d; i < B; i += D) {
+    const int n = dec_blocks(seqlens[i], L);
+    total += n;
+    if (i < b) before += n;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    before += __shfl_xor(before, off);
+    total += __shfl_xor(total, off);
+  }
+  if (lane == 0) {
+    s_red[0][wv] = before;
+    s_red[1][wv] = total;
+  }
+  __syncthreads();
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    before += s_red[0][i];
+    total += s_red[1][i];
+  }
+  const int nb = dec_blocks(seqlens[b], L);
+  const long long NB = (long long)Hkv * total, S = (long long)Hkv * before + (long long)kvh * nb, E = S + nb;
+  const long long k = (long long)b * Hkv + kvh;
+  // Workgroup holding block x: the largest w with w NB / G <= x, i.e. ((x + 1) G - 1) / NB.
+  const long long wf = nb > 0 ? ((S + 1) * G - 1) / NB : 0, wl = nb > 0 ? (E * G - 1) / NB : -1;
+  auto meets = [&](long long w) {  // workgroup w's range meets [S, E) (an empty range meets nothing)
+    const long long lo = w * NB / G, hi = (w + 1) * NB / G;
+    return (lo > S ? lo : S) < (hi < E ? hi : E);
+  };
+  float M = -INFINITY;
+  for (long long w = wf; w <= wl; ++w)
+    if (meets(w)) M = fmaxf(M, part_lse[(size_t)(w + k) * R + h]);
+  float num = 0.f, den = 0.f;
+  for (long long w = wf; w <= wl; ++w) {
+    if (!meets(w)) continue;
+    const size_t pr = (size_t)(w + k) * R + h;
+    const float ls = part_lse[pr];
+    const float wt = ls == -INFINITY ? 0.f : fast_exp2(ls - M);
+    num = fmaf(wt, part_o[pr * D + d], num);
+    den += wt;
+  }
+  const bool empty = M == -INFINITY;
+  const float val = empty ? 0.f : num / den;
+  const uint32_t packed = pack_bf16x2(val, 0.f);
+  o[(size_t)row * D + d] = (uint16_t)(packed & 0xffffu);
+  if (lse != nullptr && d == 0) lse[row] = empty ? -INFINITY : (M + fast_log2(den)) * kLn2;
+}
+
 template <int D, int GP>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((decode_split_kernel<D, GP>), dim3(a.B * a.Hkv * a.splits), dim3(kDecWaves * 64), 0,
+  const int G = a.B * a.Hkv * a.splits;
+  if (decode_stream_k(a.seqlens != nullptr, a.B, a.Hkv, a.L)) {
+    hipLaunchKernelGGL((decode_split_kernel<D, GP, true>), dim3(G), dim3(kDecWaves * 64), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.part_o, a.part_lse, a.B,
+                       a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2, a.seqlens, a.T, a.causal);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_sk_kernel<D>), dim3(a.B * a.Hq * a.T), dim3(D), 0, a.stream, a.part_o,
+                       a.part_lse, (uint16_t*)a.o, a.lse, a.seqlens, a.B, a.Hq, a.Hkv, a.T, a.L, G);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, false>), dim3(G), dim3(kDecWaves * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.part_o,
                      a.part_lse, a.B, a.Hq, a.Hkv, a.L, a.splits, a.keys_per_split, sl2, a.seqlens, a.T, a.causal);
   hipError_t e = hipGetLastError();

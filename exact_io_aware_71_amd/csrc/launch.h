@@ -80,6 +80,17 @@ constexpr int kDecValuRows = 8;
 constexpr int kDecMaxRows = 4096;
 inline bool decode_uses_mma(int T, int g) { return T * g > kDecValuRows; }
 inline int decode_partials_per_split(int T, int g) { return decode_uses_mma(T, g) ? 4 : 1; }
+// Per-sequence lengths on the vector-ALU kernel take the stream-K split (equal block ranges per
+// workgroup) up to kDecSkMaxB sequences and 2^31 blocks in all.
+constexpr int kDecSkMaxB = 2048;
+inline bool decode_stream_k(bool has_seqlens, int B, int Hkv, int L) {
+  return has_seqlens && B <= kDecSkMaxB && (long long)B * Hkv * ((L + 31) / 32) < (1LL << 31);
+}
+// Partial rows of a decode with `splits` key chunks: the stream-K split writes up to
+// splits*B*Hkv + B*Hkv group partials, so the vector-ALU path reserves one set more.
+inline size_t decode_partial_rows(int splits, int T, int g, size_t BHqT) {
+  return decode_uses_mma(T, g) ? (size_t)splits * 4 * BHqT : (size_t)(splits + 1) * BHqT;
+}
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);

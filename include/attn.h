@@ -248,7 +248,7 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
  *     every GPU the library runs on until the process ends.  A shape whose
  *     attn_decode_workspace_bytes(...) exceeds it returns ATTN_ERR_UNSUPPORTED (nothing is
  *     enqueued); the decode workload (B=64, Hq=32, Hkv=8, L=8192, d=128, automatic splits)
- *     needs about 4.3 MB.
+ *     needs about 3.2 MB.
  *   - The call allocates nothing: no hipMalloc, no hipFree, no library routine that
  *     allocates.  Its first call on a device looks up the scratch's device address there once.
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other
@@ -266,7 +266,11 @@ attn_status_t attn_decode_noalloc(const void* q, const void* k_cache, const void
  * attn_decode for a batch whose sequences hold different numbers of cached keys (caches of
  * one capacity L, each sequence b filled to its own length).  Sequence b attends to keys
  * [0, seqlens[b]) of its cache rows; everything else is as in attn_decode (same workspace
- * size for the same L and num_splits).
+ * size for the same L and num_splits).  Up to 2048 sequences (and 2^31 32-key blocks over all
+ * B*Hkv groups) the num_splits*B*Hkv workgroups each take an equal share of the 32-key blocks
+ * of all groups, so a long sequence is cut over many of them and short ones share one: the
+ * time follows the total length, not the longest.  Beyond that, fixed key chunks of L as in
+ * attn_decode.
  *   seqlens [B] int32          device array, 16-byte aligned, read by the kernels; values are
  *                              clamped to [0, L]; a sequence of length 0 gets o = 0 and
  *                              lse = -inf (the log of an empty sum)

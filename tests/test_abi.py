@@ -202,7 +202,7 @@ def test_decode_noalloc_validation():
     def decn(B=64, Hq=32, Hkv=8, L=8192, d=128, dt=1, splits=0, q=P, scale=0.1):
         return lib.attn_decode_noalloc(q, P, P, P, P, B, Hq, Hkv, L, d, dt, ctypes.c_float(scale), splits, None)
     assert binding.DECODE_NOALLOC_SCRATCH_BYTES == 16 << 20
-    # The decode workload fits (about 4.3 MB of partials).
+    # The decode workload fits (about 3.2 MB of partials).
     assert lib.attn_decode_workspace_bytes(64, 32, 8, 8192, 128, 0) <= binding.DECODE_NOALLOC_SCRATCH_BYTES
     big = lib.attn_decode_workspace_bytes(4096, 32, 8, 8192, 128, 0)
     assert big > binding.DECODE_NOALLOC_SCRATCH_BYTES

@@ -364,6 +364,58 @@ def test_decode_per_sequence_lengths(gpu_lib, d, splits):
     assert_fwd_ok(fwd_errors(o_h[1:], o_ref[1:], lse_h[1:], lse_ref[1:]), f"varlen d={d} splits={splits}")
 
 
+def run_decode_varlen(lib, inp, lens, d, splits):
+    import torch
+    sl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    q = to_dev(inp["q"])
+    B, Hq, _ = q.shape
+    Hkv, L = inp["k"].shape[1], inp["k"].shape[2]
+    g = Guarded()
+    o, lse = g.like(q), g.empty((B, Hq), torch.float32)
+    ws = g.empty((lib.attn_decode_workspace_bytes(B, Hq, Hkv, L, d, splits),), torch.uint8)
+    lib.attn_decode_varlen(q, to_dev(inp["k"]), to_dev(inp["v"]), sl, default_scale(d), num_splits=splits, o=o,
+                           lse=lse, workspace=ws)
+    g.check(f"decode varlen B={B} d={d} splits={splits}")
+    return to_host64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def check_varlen_rows(o, lse, o_ref, lse_ref, lens, tag):
+    """Empty sequences give O = 0 and LSE = -inf; every other row against the oracle."""
+    lens = np.asarray(lens)
+    empty, full = lens <= 0, lens > 0
+    assert np.all(o[empty] == 0.0) and np.all(lse[empty] == -np.inf), tag
+    assert_fwd_ok(fwd_errors(o[full], o_ref[full], lse[full], lse_ref[full]), tag)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [0, 1, 2, 7])
+def test_decode_skewed_lengths(gpu_lib, d, splits):
+    """attn_decode_varlen with two long sequences among many short or empty ones.  The split
+    gives every workgroup the same number of 32-key blocks, so the long sequences are cut over
+    many workgroups while one workgroup takes several short ones (its block range crossing
+    sequence and KV-head boundaries); every row against the oracle."""
+    L = 2048
+    lens = np.array([L] + [0, 1, 3, 40, 0, 65, 2] * 4 + [L - 1, 0, 31, 32, 33], dtype=np.int32)
+    print(f"decode skewed B={len(lens)} d={d} splits={splits}", flush=True)
+    inp = make_decode(len(lens), 4, 2, L, d, seed=6000 + d + splits)
+    o, lse = run_decode_varlen(gpu_lib, inp, lens, d, splits)
+    o_ref, lse_ref = oracle.decode(inp["q"], inp["k"], inp["v"], default_scale(d), seqlens=lens)
+    check_varlen_rows(o, lse, o_ref, lse_ref, lens, f"skewed d={d} splits={splits}")
+
+
+@pytest.mark.parametrize("B", [2048, 2049])
+def test_decode_lengths_many_sequences(gpu_lib, B):
+    """Up to 2048 sequences the split's per-sequence block counts sit in LDS; beyond that the
+    fixed key chunks take over.  Both against the oracle, lengths uniform in [0, L]."""
+    L, d = 96, 64
+    lens = np.random.default_rng(6100 + B).integers(0, L + 1, size=B).astype(np.int32)
+    print(f"decode many B={B}", flush=True)
+    inp = make_decode(B, 2, 1, L, d, seed=6200 + B)
+    o, lse = run_decode_varlen(gpu_lib, inp, lens, d, 0)
+    o_ref, lse_ref = oracle.decode(inp["q"], inp["k"], inp["v"], default_scale(d), seqlens=lens)
+    check_varlen_rows(o, lse, o_ref, lse_ref, lens, f"many B={B}")
+
+
 # ----------------------------------------------------------------------------- backward
 def run_fwd_bwd(lib, inp, causal, scale):
     """Gradients and the backward workspace in guarded buffers."""
