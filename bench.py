@@ -686,7 +686,7 @@ def main():
     roofline_decode = {
         "kernel": "decode_split_kernel + decode_merge_kernel (attn_decode, B=64, Hq=32, Hkv=8, L=8192, d=128)",
         "bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS,
-        "traffic": load_traffic("decode_split_kernel<128,4>", dec_digest), "splits": splits,
+        "traffic": load_traffic("decode_split_kernel<128,4,false>", dec_digest), "splits": splits,
     }
 
     result = {
