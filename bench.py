@@ -20,7 +20,7 @@ Secondary lines, each timed on its own after the step (skipped with --no-extras)
     sweep (B=1 H=32 d=128, Q and K x2, N = 4096 / 8192 / 16384, causal and not);
   * decode with per-sequence cache lengths, multi-token decode, chunked prefill (Nq != Nk),
     packed sequences of different lengths (forward and backward), a block-sparse mask (forward
-    and backward).
+    and backward), a grouped-query training step (B=1 Hq=32 Hkv=8 N=4096 d=128, causal).
 FLOP counts are 4 d per (query, key) pair the mask keeps.  Each line carries its fraction of
 the roofline: dense bf16 MFMA peak 2516.6 TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP per clock), HBM
 8000 GB/s (the published MI355X figures).
@@ -574,6 +574,22 @@ def main():
                                                                     dq=sg[0], dk=sg[1], dv=sg[2], workspace=sws))
         del sq_, sk_, sv_, sdo, so, slse, sg, sws
 
+        # Grouped-query training step: B=1, Hq=32, Hkv=8 (4 query heads per KV head), N=4096,
+        # d=128, causal (seed 1012); the backward sums dK and dV over each group's query heads.
+        GHq, GHkv, GN = 32, 8, 4096
+        gp = make_prefill(1, GHq, GHkv, GN, d, "bf16", seed=1012, with_dout=True)
+        gq, gk, gv, gdo = (to_dev(gp[x]) for x in ("q", "k", "v", "dout"))
+        del gp
+        go = torch.empty_like(gq)
+        glse = torch.empty((1, GHq, GN), dtype=torch.float32, device=dev)
+        ms_gqa_fwd = time_call(lambda: attn.attn_fwd(gq, gk, gv, True, scale, o=go, lse=glse))
+        gg = [torch.empty_like(gq), torch.empty_like(gk), torch.empty_like(gv)]
+        gws = torch.empty(attn.attn_bwd_workspace_bytes(1, GHq, GHkv, GN, d), dtype=torch.uint8, device=dev)
+        ms_gqa_bwd = time_call(lambda: attn.attn_bwd(gq, gk, gv, go, glse, gdo, True, scale, dq=gg[0], dk=gg[1],
+                                                     dv=gg[2], workspace=gws))
+        f_gqa = flops_fwd(1, GHq, GN, d, True)
+        del gq, gk, gv, gdo, go, glse, gg, gws
+
         # Multi-token decode: 4 tokens per sequence on the decode cache (16 (token, head) rows per
         # KV head), causal, seed 1011 for the queries.
         MT = 4
@@ -635,6 +651,9 @@ def main():
                            "bwd_TFLOPs": 2.5 * f_varlen / (ms_varlen_bwd * 1e-3) / 1e12, "bwd_ms": ms_varlen_bwd,
                            "workload": "attn_fwd_varlen 12 packed sequences, lengths uniform in [256, 4096] "
                                        "(seed 1008, total %d), H=16 d=128 causal" % int(vl.sum())},
+            "train_gqa": {"fwd_TFLOPs": f_gqa / (ms_gqa_fwd * 1e-3) / 1e12, "fwd_ms": ms_gqa_fwd,
+                          "bwd_TFLOPs": 2.5 * f_gqa / (ms_gqa_bwd * 1e-3) / 1e12, "bwd_ms": ms_gqa_bwd,
+                          "workload": "attn_fwd + attn_bwd B=1 Hq=32 Hkv=8 N=4096 d=128 causal"},
             "decode_multi": {"GBps": mdec_bytes / (ms_mdec * 1e-3) / 1e9, "ms": ms_mdec,
                          "workload": "attn_decode_multi B=64 Hq=32 Hkv=8 T=4 L=8192 d=128 causal"},
             "fwd_prefill_d64": {"TFLOPs": f_pre64 / (ms_pre64 * 1e-3) / 1e12, "ms": ms_pre64,
