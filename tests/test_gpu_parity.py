@@ -687,8 +687,8 @@ def test_decode_multi_full_size_sampled_batches(gpu_lib, decode_inputs):
 # ----------------------------------------------------------------------------- HIP graph capture
 def test_hip_graph_replay_matches_eager(gpu_lib):
     """Every entry point enqueues kernels only (no allocation, no memset), so a captured graph of
-    forward, backward, decode and the packed forward replays to the eager results bit for bit,
-    with eager work and synchronisation between replays."""
+    forward, backward, decode (equal and per-sequence lengths) and the packed forward replays to
+    the eager results bit for bit, with eager work and synchronisation between replays."""
     import torch
     d = 128
     scale = default_scale(d)
@@ -707,14 +707,18 @@ def test_hip_graph_replay_matches_eager(gpu_lib):
     od, ld = torch.empty_like(dq_), torch.empty((4, 8), dtype=torch.float32, device="cuda")
     wsd = torch.empty(gpu_lib.attn_decode_workspace_bytes(4, 8, 2, 1000, d, 3), dtype=torch.uint8, device="cuda")
     po, pl = torch.empty_like(pq), torch.empty((4, pq.shape[1]), dtype=torch.float32, device="cuda")
+    sl = torch.tensor([1000, 0, 37, 640], dtype=torch.int32, device="cuda")  # per-sequence lengths
+    ov, lv = torch.empty_like(dq_), torch.empty((4, 8), dtype=torch.float32, device="cuda")
+    wsv = torch.empty_like(wsd)
 
     def work():
         gpu_lib.attn_fwd(q, k, v, True, scale, o=o, lse=lse)
         gpu_lib.attn_bwd(q, k, v, o, lse, do, True, scale, dq=g[0], dk=g[1], dv=g[2], workspace=wsb)
         gpu_lib.attn_decode(dq_, dk_, dv_, scale, num_splits=3, o=od, lse=ld, workspace=wsd)
+        gpu_lib.attn_decode_varlen(dq_, dk_, dv_, sl, scale, num_splits=3, o=ov, lse=lv, workspace=wsv)
         gpu_lib.attn_fwd_varlen(pq, pk, pv, cq, ck, 300, True, scale, o=po, lse=pl)
 
-    outs = (o, lse, *g, od, ld, po, pl)
+    outs = (o, lse, *g, od, ld, ov, lv, po, pl)
     work()
     torch.cuda.synchronize()
     eager = [t.clone() for t in outs]

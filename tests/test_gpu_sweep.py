@@ -1,5 +1,6 @@
 """Randomised GPU parity sweep: forward, backward and the Nq != Nk forward on seeded random
-shapes against the fp64 oracle, every element compared.
+shapes against the fp64 oracle, every element compared; then decode with per-sequence lengths
+on seeded random batches (test_random_decode_lengths).
 
 Shapes: N near and off the tile sizes (1 to 700), d in {64, 128}, group sizes 1 to 8, one or
 two batches, causal or not, logits x1 or x2 (rows dominated by one key).  Bounds as everywhere:
@@ -55,3 +56,35 @@ def test_random_shape(gpu_lib, case):
             assert np.abs(h).max() <= 1e-3, (name, np.abs(h).max())
             continue
         assert rel_l2(h, r) <= BWD_REL_L2, (name, rel_l2(h, r))
+
+
+def _decode_cases(seed, n):
+    """Per-sequence-length decode: batch sizes 1 to 40, KV heads 1 to 3, groups 1 to 8 (with T
+    tokens, up to 8 rows per KV head: the stream-K path), cache capacities near and off the 32-key
+    blocks, lengths drawn from {0, 1, random, L} so that workgroup ranges cross sequences, KV heads
+    and empty sequences; split counts 0 (automatic) to 9."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        g = int(rng.choice([1, 2, 4, 8]))
+        T = int(rng.choice([t for t in (1, 2, 4, 8) if t * g <= 8]))
+        L = int(rng.choice([1, 31, 32, 33, 100, 257, 700]))
+        B = int(rng.integers(1, 41))
+        lens = [int(rng.choice([0, 1, int(rng.integers(0, L + 1)), L])) for _ in range(B)]
+        out.append(dict(B=B, Hkv=int(rng.integers(1, 4)), g=g, T=T, L=L, d=int(rng.choice([64, 128])),
+                        causal=bool(rng.integers(0, 2)), splits=int(rng.integers(0, 10)), lens=lens,
+                        seed=9500 + c))
+    return out
+
+
+@pytest.mark.parametrize("case", _decode_cases(12, 32), ids=lambda c: f"B{c['B']}-g{c['g']}x{c['Hkv']}-T{c['T']}-"
+                         f"L{c['L']}-d{c['d']}-s{c['splits']}-{'c' if c['causal'] else 'f'}")
+def test_random_decode_lengths(gpu_lib, case):
+    from tests.test_gpu_kv_varlen import check_rows
+    from tests.test_gpu_parity import run_decode_multi
+    B, Hkv, g, T, L, d = (case[x] for x in ("B", "Hkv", "g", "T", "L", "d"))
+    x = make_prefill(B, g * Hkv, Hkv, T, d, "bf16", seed=case["seed"], L=L)
+    scale = default_scale(d)
+    o, lse = run_decode_multi(gpu_lib, x["q"], x["k"], x["v"], case["lens"], case["causal"], case["splits"], scale)
+    o_ref, lse_ref = oracle.decode_multi(x["q"], x["k"], x["v"], scale, case["causal"], seqlens=case["lens"])
+    check_rows(o, lse, o_ref, lse_ref, f"decode {case}")
