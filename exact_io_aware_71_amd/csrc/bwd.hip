@@ -938,6 +938,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     });
   } else {
   float pmx = 0.f;  // largest probability this lane meets (first launch)
+  // The dP accumulators start from -D (every element of a lane belongs to its query row), so
+  // the matrix cores return dP - D and dS = P (dP - D) is one multiply per element: 32 vector
+  // subtractions fewer per tile for 16 registers held across the walk (1.3% off the kernel).
+  f32x16 ndl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = -dl;
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = kt(t) * BN, kn = kt(t + 1);
     if (CAUSAL && t0 > qd0 + 31) {
@@ -967,7 +973,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       auto ds_group = [&](const f32x16& p, f32x16& dp, bf16x8 (&ds)[2], int g) __attribute__((always_inline)) {
         if constexpr (!REDO) pmx = fmaxf(fmaxf(pmx, p[4 * g]), fmaxf(fmaxf(p[4 * g + 1], p[4 * g + 2]), p[4 * g + 3]));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dp[4 * g + e] = p[4 * g + e] * (dp[4 * g + e] - dl);
+        for (int e = 0; e < 4; ++e) dp[4 * g + e] = p[4 * g + e] * dp[4 * g + e];  // dp holds dP - D
         if (g % 2 == 1) {
           ds[g / 2] = pack8(dp, g / 2);
           asm volatile("" : "+v"(ds[g / 2]));
@@ -983,13 +989,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           if constexpr (i == PA) { s0 = mfma32(buf[i % LA], qreg[0], f32x16{}); }
           else s0 = mfma32(buf[i % LA], qreg[i - PA], s0);
         } else if constexpr (i < PC) {
-          if constexpr (i == PB) dp0 = mfma32(buf[i % LA], doreg[0], f32x16{});
+          if constexpr (i == PB) dp0 = mfma32(buf[i % LA], doreg[0], ndl);
           else dp0 = mfma32(buf[i % LA], doreg[i - PB], dp0);
         } else if constexpr (i < PD) {
           if constexpr (i == PC) s1 = mfma32(buf[i % LA], qreg[0], f32x16{});
           else s1 = mfma32(buf[i % LA], qreg[i - PC], s1);
         } else if constexpr (i < PE) {
-          if constexpr (i == PD) dp1 = mfma32(buf[i % LA], doreg[0], f32x16{});
+          if constexpr (i == PD) dp1 = mfma32(buf[i % LA], doreg[0], ndl);
           else dp1 = mfma32(buf[i % LA], doreg[i - PD], dp1);
         } else if constexpr (i < PF) {
           constexpr int jj = i - PE, sh = jj / DB, db = jj % DB;
