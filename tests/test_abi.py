@@ -196,6 +196,23 @@ def test_decode_plan_and_validation():
     assert decv(d=32) == 2
 
 
+def test_decode_workspace_layout():
+    """Decode partials are B*Hq*T rows of d fp32 values plus one fp32 LSE each, each array
+    256-byte aligned: (splits + 1) sets on the vector-ALU path (up to 8 (token, head) rows per KV
+    head; the stream-K split of per-sequence lengths writes up to one set more than the split
+    count) and 4 * splits sets on the matrix-core path (one partial per wave)."""
+    def size(rows, d):
+        up = lambda x: (x + 255) // 256 * 256
+        return up(rows * d * 4) + up(rows * 4)
+    B, Hq, Hkv, L = 3, 8, 2, 1000
+    for d in (64, 128):
+        for s in (1, 3, 16):  # 1000 keys in chunks of 1000, 352 and 64 keys: exactly s chunks
+            assert lib.attn_decode_workspace_bytes(B, Hq, Hkv, L, d, s) == size((s + 1) * B * Hq, d)
+            assert lib.attn_decode_multi_workspace_bytes(B, Hq, Hkv, 2, L, d, s) == size((s + 1) * B * Hq * 2, d)
+            # 4 tokens x 4 heads = 16 rows per KV head: the matrix-core path.
+            assert lib.attn_decode_multi_workspace_bytes(B, Hq, Hkv, 4, L, d, s) == size(4 * s * B * Hq * 4, d)
+
+
 def test_decode_noalloc_validation():
     """attn_decode_noalloc: argument errors as attn_decode, and shapes whose partials exceed the
     library's fixed 16 MiB scratch are refused before any HIP call."""
